@@ -1,0 +1,419 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+The pages print no worked numeric example, so every pin comes from the
+mathematics of softmax attention and from invariants the method must keep:
+
+1. brute force: an independent pure-Python implementation (its own bf16
+   decoding, token slots found by walking each request's page list, math.fsum
+   sums) on tiny batches;
+2. seq_len = 1 returns that token's V row exactly;
+3. relabelling the physical pages (and the page table with them) changes no bit;
+4. any split count merges to the unsplit result (empty splits included);
+5. q = 0 gives the uniform average of the V rows;
+6. constant V returns the constant; one dominant key returns its V row;
+7. with an identity page table the result is torch's scaled_dot_product_attention
+   in float64 with the KV heads repeated;
+8. integer parts: kv_indptr page counts bracket the lengths, the split plan
+   equals a search-based re-derivation of its rule, the append writes exactly
+   the slot of the newest token;
+9. NaN poison in free pages and past-the-end slots never reaches an output.
+
+``test_planted_mistakes`` plants plausible mistakes in the oracle (on the CPU)
+and checks that at least one pin fails for each.
+"""
+
+import math
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as OA
+import workloads as W
+
+
+# ----------------------------------------------------------------- fixtures
+
+def tiny_batch(seed=11, poison=True, lengths=(1, 23, 9, 0)):
+    return W.make_batch(
+        name="tiny4", seed=seed, B=len(lengths), Hq=4, Hkv=2, D=16, P=4,
+        lengths=np.array(lengths), num_pages=24, poison=poison,
+    )
+
+
+def gqa8_batch(seed=12):
+    # G = 4 with 8 query heads; ragged lengths with a partial last page.
+    return W.make_batch(
+        name="gqa8", seed=seed, B=2, Hq=8, Hkv=2, D=8, P=4,
+        lengths=np.array([13, 6]), num_pages=12,
+    )
+
+
+def run_decode(mod, batch):
+    ip = mod.kv_indptr(batch.seq_lens, batch.P)
+    return mod.decode(batch.q, batch.k_pool, batch.v_pool, ip, batch.kv_indices,
+                      batch.seq_lens, batch.sm_scale, batch.P)
+
+
+# --------------------------------------------------------- brute force (pin 1)
+
+def _bf16_py(bits) -> float:
+    return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+
+def _token_slots(batch, b):
+    """(page, offset) of request b's tokens, found by walking its pages in order."""
+    slots = []
+    for page in batch.page_lists[b]:
+        for off in range(batch.P):
+            slots.append((int(page), off))
+    return slots[: int(batch.seq_lens[b])]
+
+
+def brute_force(batch):
+    B, Hq, Hkv, D = batch.B, batch.Hq, batch.Hkv, batch.D
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        slots = _token_slots(batch, b)
+        if not slots:
+            continue
+        for hq in range(Hq):
+            h = (hq * Hkv) // Hq
+            qv = [_bf16_py(batch.q[b, hq, d]) for d in range(D)]
+            xs = []
+            for page, off in slots:
+                kv = [_bf16_py(batch.k_pool[page, h, off, d]) for d in range(D)]
+                xs.append(batch.sm_scale * math.fsum(a * c for a, c in zip(qv, kv)))
+            m = max(xs)
+            ws = [math.exp(x - m) for x in xs]
+            den = math.fsum(ws)
+            for d in range(D):
+                num = math.fsum(w * _bf16_py(batch.v_pool[p, h, o, d]) for w, (p, o) in zip(ws, slots))
+                out[b, hq, d] = num / den
+    return out
+
+
+def pin_brute_force(mod):
+    for batch in (W.config(1), tiny_batch(), gqa8_batch()):
+        got = run_decode(mod, batch)
+        ref = brute_force(batch)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------ invariants (pins 2-6)
+
+def pin_seq_len_one(mod):
+    batch = W.make_batch(name="len1", seed=21, B=3, Hq=8, Hkv=2, D=32, P=16,
+                         lengths=np.ones(3, np.int64), num_pages=8)
+    got = run_decode(mod, batch)
+    G = batch.Hq // batch.Hkv
+    for b in range(batch.B):
+        page = int(batch.page_lists[b][0])
+        for hq in range(batch.Hq):
+            row = W.bf16_bits_to_f32(batch.v_pool[page, hq // G, 0]).astype(np.float64)
+            assert np.array_equal(got[b, hq], row)
+
+
+def pin_permutation(mod):
+    for batch in (W.config(1), tiny_batch()):
+        a = run_decode(mod, batch)
+        b = run_decode(mod, W.permute_pool(batch, seed=99))
+        assert np.array_equal(a, b, equal_nan=False)
+
+
+def pin_split_invariance(mod):
+    for batch in (W.config(1), tiny_batch(), gqa8_batch()):
+        ip = mod.kv_indptr(batch.seq_lens, batch.P)
+        ref = run_decode(mod, batch)
+        npages = [len(pl) for pl in batch.page_lists]
+        for k in range(1, max(npages) + 3):
+            # k splits where possible; requests with fewer pages also get empty splits
+            ns = np.full(batch.B, k)
+            got = mod.decode_split(batch.q, batch.k_pool, batch.v_pool, ip, batch.kv_indices,
+                                   batch.seq_lens, batch.sm_scale, batch.P, ns)
+            np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def _valid_rows(pool, batch, b, h):
+    return np.array([W.bf16_bits_to_f32(pool[p, h, o]) for p, o in _token_slots(batch, b)],
+                    dtype=np.float64)
+
+
+def pin_q_zero(mod):
+    for batch in (tiny_batch(), gqa8_batch()):
+        batch.q[:] = 0
+        got = run_decode(mod, batch)
+        G = batch.Hq // batch.Hkv
+        for b in range(batch.B):
+            if batch.seq_lens[b] == 0:
+                continue
+            for hq in range(batch.Hq):
+                mean = _valid_rows(batch.v_pool, batch, b, hq // G).mean(axis=0)
+                np.testing.assert_allclose(got[b, hq], mean, rtol=0, atol=1e-12)
+
+
+def pin_constant_v(mod):
+    batch = tiny_batch(poison=False, lengths=(5, 17, 3))
+    c = W.f32_to_bf16_bits(np.float32(0.7109375))
+    batch.v_pool[:] = c
+    got = run_decode(mod, batch)
+    np.testing.assert_allclose(got, np.full(got.shape, 0.7109375), rtol=0, atol=1e-12)
+
+
+def pin_dominant_key(mod):
+    batch = tiny_batch(poison=True, lengths=(9, 14, 6))
+    rng = np.random.default_rng(5)
+    G = batch.Hq // batch.Hkv
+    for b in range(batch.B):
+        slots = _token_slots(batch, b)
+        j = int(rng.integers(len(slots)))
+        p, o = slots[j]
+        for h in range(batch.Hkv):
+            big = W.bf16_bits_to_f32(batch.k_pool[p, h, o]) * np.float32(4.0)
+            batch.k_pool[p, h, o] = W.f32_to_bf16_bits(big)
+            for g in range(G):
+                batch.q[b, h * G + g] = W.f32_to_bf16_bits(big * np.float32(16.0))
+        batch.notes[b] = (p, o)
+    got = run_decode(mod, batch)
+    for b in range(batch.B):
+        p, o = batch.notes[b]
+        for hq in range(batch.Hq):
+            row = W.bf16_bits_to_f32(batch.v_pool[p, hq // G, o]).astype(np.float64)
+            np.testing.assert_allclose(got[b, hq], row, rtol=0, atol=1e-9)
+
+
+# ------------------------------------------------- library special case (pin 7)
+
+def pin_sdpa(mod):
+    for batch in (W.identity_layout(W.config(1)), W.identity_layout(tiny_batch()),
+                  W.identity_layout(gqa8_batch())):
+        got = run_decode(mod, batch)
+        G = batch.Hq // batch.Hkv
+        for b in range(batch.B):
+            L = int(batch.seq_lens[b])
+            if L == 0:
+                continue
+            pages = batch.page_lists[b]
+            p0, n = int(pages[0]), len(pages)
+
+            def dense(pool):
+                blk = W.bf16_bits_to_f32(pool[p0 : p0 + n]).astype(np.float64)  # [n, Hkv, P, D]
+                blk = np.transpose(blk, (1, 0, 2, 3)).reshape(batch.Hkv, n * batch.P, batch.D)
+                t = torch.from_numpy(np.ascontiguousarray(blk[:, :L]))
+                return t.repeat_interleave(G, dim=0)[None]  # [1, Hq, L, D]
+
+            q = torch.from_numpy(W.bf16_bits_to_f32(batch.q[b]).astype(np.float64))[None, :, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q, dense(batch.k_pool), dense(batch.v_pool), scale=batch.sm_scale)
+            np.testing.assert_allclose(got[b], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------- integer parts (pin 8)
+
+def pin_kv_indptr(mod):
+    ragged = W.make_batch(name="ragged_small_d", seed=3, B=16, Hq=4, Hkv=1, D=8, P=16,
+                          lengths=lambda r: r.integers(1, 4097, size=16), poison=False)
+    for batch in (W.config(1), ragged, tiny_batch()):
+        ip = np.asarray(mod.kv_indptr(batch.seq_lens, batch.P))
+        assert ip.shape == (batch.B + 1,) and ip[0] == 0
+        for b in range(batch.B):
+            n = int(ip[b + 1] - ip[b])
+            L = int(batch.seq_lens[b])
+            assert n == len(batch.page_lists[b])
+            assert (n == 0 and L == 0) or ((n - 1) * batch.P < L <= n * batch.P)
+
+
+def _search_plan(seq_lens, P, Hkv, max_splits, target, min_chunk, forced):
+    pages = []
+    for L in seq_lens:
+        n = 0
+        while n * P < L:
+            n += 1
+        pages.append(n)
+    N = sum(pages)
+    chunk = min_chunk
+    while chunk * target < Hkv * N:
+        chunk += 1
+    ns = []
+    for n in pages:
+        if n == 0:
+            ns.append(0)
+        elif forced:
+            ns.append(min(forced, n, max_splits))
+        else:
+            k = 1
+            while k * chunk < n:
+                k += 1
+            ns.append(min(k, max_splits))
+    return chunk, ns
+
+
+def pin_plan(mod):
+    rng = np.random.default_rng(7)
+    cases = [(np.array([37]), 16, 2, 4, 64, 1, 3)]
+    for _ in range(60):
+        B = int(rng.integers(1, 20))
+        seq = rng.integers(0, 3000, size=B)
+        cases.append((seq, int(rng.choice([1, 4, 16])), int(rng.choice([1, 2, 8])),
+                      int(rng.integers(1, 300)), int(rng.choice([64, 512, 2048])),
+                      int(rng.integers(1, 9)), int(rng.choice([0, 0, 1, 3, 7]))))
+    for seq, P, Hkv, smax, target, cmin, forced in cases:
+        plan = mod.plan_splits(seq, P, Hkv, smax, target, cmin, forced)
+        chunk, ns = _search_plan(list(seq), P, Hkv, smax, target, cmin, forced)
+        assert plan["chunk"] == chunk
+        assert list(plan["nsplit"]) == ns
+        assert list(np.diff(plan["split_indptr"])) == ns and plan["split_indptr"][0] == 0
+        if not forced:
+            assert plan["num_items"] <= -(-target // Hkv) + len(seq)
+        for n, k in zip([len(range(0, L, P)) for L in seq], ns):
+            if k == 0:
+                continue
+            ranges = mod.even_page_ranges(n, k)
+            assert ranges[0][0] == 0 and ranges[-1][1] == n
+            assert all(ranges[i][1] == ranges[i + 1][0] for i in range(k - 1))
+            sizes = [r1 - r0 for r0, r1 in ranges]
+            assert max(sizes) - min(sizes) <= 1 and min(sizes) >= 1
+
+
+def pin_append(mod):
+    batch = W.make_batch(name="append_small", seed=31, B=6, Hq=4, Hkv=2, D=8, P=4,
+                         lengths=np.array([1, 4, 5, 8, 13, 2]), num_pages=40, append=True)
+    ip = mod.kv_indptr(batch.seq_lens, batch.P)
+    k2, v2 = mod.append_kv(batch.k_pool, batch.v_pool, batch.k_new, batch.v_new, ip,
+                           batch.kv_indices, batch.seq_lens, batch.P)
+    changed = np.zeros(batch.k_pool.shape[:1] + batch.k_pool.shape[2:3], bool)
+    for b in range(batch.B):
+        p, o = _token_slots(batch, b)[-1]
+        assert np.array_equal(k2[p, :, o], batch.k_new[b])
+        assert np.array_equal(v2[p, :, o], batch.v_new[b])
+        changed[p, o] = True
+    keep = np.broadcast_to(~changed[:, None, :, None], k2.shape)
+    assert np.array_equal(k2[keep], batch.k_pool[keep])
+    assert np.array_equal(v2[keep], batch.v_pool[keep])
+    # the appended batch is now fully written: poison must not reach any output
+    out = mod.decode(batch.q, k2, v2, ip, batch.kv_indices, batch.seq_lens,
+                     batch.sm_scale, batch.P)
+    assert np.isfinite(out).all()
+
+
+# ------------------------------------------------------------ poison (pin 9)
+
+def pin_poison(mod):
+    for batch in (W.config(1), W.config(2), tiny_batch(), gqa8_batch()):
+        assert batch.poisoned
+        out = run_decode(mod, batch)
+        assert np.isfinite(out).all()
+
+
+PINS = [pin_brute_force, pin_seq_len_one, pin_permutation, pin_split_invariance, pin_q_zero,
+        pin_constant_v, pin_dominant_key, pin_sdpa, pin_kv_indptr, pin_plan, pin_append,
+        pin_poison]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(OA)
+
+
+def test_poison_large_configs():
+    # full-size ragged batch: the oracle never touches a NaN slot
+    batch = W.config(3)
+    out = run_decode(OA, batch)
+    assert np.isfinite(out).all()
+
+
+# ----------------------------------------------------------- planted mistakes
+
+def _mutants():
+    m = {}
+
+    m["gqa_head_interleaved"] = {"kv_head_of": lambda hq, G: hq % 2}
+
+    def gather_off_by_one(pool_bits, indptr, indices, b, L, P):
+        pool = np.asarray(pool_bits)
+        out = np.empty((L, pool.shape[1], pool.shape[3]))
+        for t in range(L):
+            page = int(indices[int(indptr[b]) + (t + 1) // P])
+            out[t] = OA.bf16_to_f64(pool[page, :, (t + 1) % P, :])
+        return out
+    m["gather_shifted_token"] = {"gather_request": gather_off_by_one}
+
+    def gather_swapped_page_offset(pool_bits, indptr, indices, b, L, P):
+        pool = np.asarray(pool_bits)
+        out = np.empty((L, pool.shape[1], pool.shape[3]))
+        for t in range(L):
+            page = int(indices[int(indptr[b]) + t % P])
+            out[t] = OA.bf16_to_f64(pool[page, :, t // P, :])
+        return out
+    m["gather_swapped_page_offset"] = {"gather_request": gather_swapped_page_offset}
+
+    def attend_no_scale(qv, Kd, Vd, sm_scale):
+        return OA.__dict__["_orig_softmax_attend"](qv, Kd, Vd, 1.0)
+    m["missing_sm_scale"] = {"softmax_attend": attend_no_scale}
+
+    def attend_scores_from_v(qv, Kd, Vd, sm_scale):
+        return OA.__dict__["_orig_softmax_attend"](qv, Vd, Vd, sm_scale)
+    m["scores_use_v"] = {"softmax_attend": attend_scores_from_v}
+
+    def attend_neg(qv, Kd, Vd, sm_scale):
+        return OA.__dict__["_orig_softmax_attend"](qv, Kd, Vd, -sm_scale)
+    m["score_sign_flipped"] = {"softmax_attend": attend_neg}
+
+    def attend_drop_last(qv, Kd, Vd, sm_scale):
+        n = max(1, Kd.shape[0] - 1) if Kd.shape[0] else 0
+        return OA.__dict__["_orig_softmax_attend"](qv, Kd[:n], Vd[:n], sm_scale)
+    m["drops_newest_token"] = {"softmax_attend": attend_drop_last}
+
+    def merge_plain_mean(parts):
+        live = [o for o, lse in parts if lse != -math.inf]
+        return np.mean(live, axis=0) if live else np.zeros(parts[0][0].shape[0])
+    m["merge_without_weights"] = {"merge_partials": merge_plain_mean}
+
+    def partial_lse_missing_max(qv, Kd, Vd, sm_scale):
+        o, lse = OA.__dict__["_orig_chunk_partial"](qv, Kd, Vd, sm_scale)
+        if lse == -math.inf:
+            return o, lse
+        x = sm_scale * (Kd @ qv)
+        return o, lse - float(np.max(x))
+    m["lse_missing_max"] = {"chunk_partial": partial_lse_missing_max}
+
+    def ranges_drop_last_page(n, k):
+        r = [((s * n) // k, ((s + 1) * n) // k) for s in range(k)]
+        r[-1] = (r[-1][0], max(r[-1][0], n - 1))
+        return r
+    m["ranges_drop_last_page"] = {"even_page_ranges": ranges_drop_last_page}
+
+    m["page_count_floor"] = {"page_counts": lambda L, P: np.asarray(L, np.int64) // P}
+
+    def plan_floor_chunk(seq_lens, P, Hkv, max_splits, target_items, min_chunk, forced=0):
+        p = OA.__dict__["_orig_plan_splits"](seq_lens, P, Hkv, max_splits, target_items, min_chunk, forced)
+        N = p["total_pages"]
+        p["chunk"] = max(min_chunk, Hkv * N // target_items)
+        return p
+    m["plan_chunk_floor"] = {"plan_splits": plan_floor_chunk}
+
+    def append_at_len(k_pool, v_pool, k_new, v_new, indptr, indices, seq_lens, P):
+        return OA.__dict__["_orig_append_kv"](k_pool, v_pool, k_new, v_new, indptr, indices,
+                                              np.asarray(seq_lens) + 1, P)
+    m["append_one_slot_late"] = {"append_kv": append_at_len}
+    return m
+
+
+MUTANTS = _mutants()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistakes(name, monkeypatch):
+    for fn in ("softmax_attend", "chunk_partial", "plan_splits", "append_kv"):
+        monkeypatch.setitem(OA.__dict__, "_orig_" + fn, getattr(OA, fn))
+    for attr, repl in MUTANTS[name].items():
+        monkeypatch.setattr(OA, attr, repl)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(OA)
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name!r} passed every pin"
