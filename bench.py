@@ -1,0 +1,237 @@
+"""Benchmark of paged-KV split-KV decode attention on one MI355X.
+
+One step = the whole hot path for one layer of one decode step: build the step
+metadata (page prefix sums + split plan), append this step's K/V token of every
+request, split-KV decode kernel, merge kernel.  Inputs are seeded synthetic
+batches already resident in HBM.  Between steps the pool rotates over several
+identical copies whose total size exceeds the 256 MB Infinity Cache, so every
+step streams its K/V from HBM.
+
+Timing: after W warm-up steps, a bounded spin kernel holds the GPU while the
+host enqueues all K timed steps; HIP events then bracket the K steps (step
+time) and every split-kernel launch (kernel time), on the stream the kernels
+run on.
+
+Prints one JSON line.  `value` is algorithmic GB/s of the whole step:
+bytes the method must move (K/V attended, q, output, page ids, appended rows)
+divided by the step time.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "paged decode attention µs/call + achieved HBM GB/s (% of peak), B=16 ragged"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "split_kernel_counters.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_split_attn_amd", "csrc", "pkv_decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload preset 1..5 (3 = B=16 ragged)")
+    ap.add_argument("--target-items", type=int, default=0, help="planner target (0 = library default)")
+    ap.add_argument("--min-chunk", type=int, default=0)
+    ap.add_argument("--max-splits", type=int, default=256)
+    ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0 = enough for 768 MB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time only whole steps (no events around the split kernel)")
+    ap.add_argument("--warm", action="store_true", help="no pool rotation (cache-warm numbers)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(batch):
+    """Bytes the method must move for one decode call and for one whole step."""
+    kv = int(batch.seq_lens.astype(np.int64).sum()) * batch.Hkv * batch.D * 2 * 2
+    qo = 2 * batch.B * batch.Hq * batch.D * 2
+    pages = sum(len(p) for p in batch.page_lists)
+    meta = 4 * pages + 4 * (batch.B + 1) + 4 * batch.B
+    append = batch.B * batch.Hkv * batch.D * 2 * 2 * 2  # read k_new/v_new, write the slots
+    call = kv + qo + meta
+    return call, call + append + 4 * (batch.B + 1)
+
+
+def cpu_baseline(batch, budget_s):
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    ip = oracle.kv_indptr(batch.seq_lens, batch.P)
+    idx = batch.kv_indices
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.decode(batch.q, batch.k_pool, batch.v_pool, ip, idx, batch.seq_lens,
+                          batch.sm_scale, batch.P)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 1000:
+                break
+    per_call = el / reps
+    call_bytes, _ = algorithmic_bytes(batch)
+    return {"value": round(call_bytes / per_call / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "us_per_call": round(per_call * 1e6, 1),
+            "sample": f"{reps} full decode calls of the {batch.name} batch (fp64 numpy oracle, "
+                      f"one thread), {el:.1f} s"}
+
+
+def counters_for_current_kernel():
+    """rocprofv3 FETCH/WRITE per split launch, if taken on the current kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return rec
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "this library has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_split_attn_amd as pkv
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    batch = W.config(args.config, poison=False)
+    if not batch.append:
+        # every step appends one token per request; draw it from its own stream
+        rng = np.random.default_rng(np.random.PCG64(1000 + args.config))
+        batch.k_new = W.normal_bf16(rng, (batch.B, batch.Hkv, batch.D))
+        batch.v_new = W.normal_bf16(rng, (batch.B, batch.Hkv, batch.D))
+        batch.append = True
+    print(f"[bench] workload {batch.name}: B={batch.B} Hq={batch.Hq} Hkv={batch.Hkv} D={batch.D} "
+          f"P={batch.P} tokens={batch.kv_tokens} pages={batch.num_pages}", file=sys.stderr,
+          flush=True)
+
+    desc = pkv.Desc(max_batch=batch.B, num_q_heads=batch.Hq, num_kv_heads=batch.Hkv,
+                    head_dim=batch.D, page_size=batch.P, max_splits=args.max_splits,
+                    target_items=args.target_items, min_chunk_pages=args.min_chunk)
+    base = W.to_device(batch, dev)
+    pool_bytes = 2 * base["k_pool"].numel() * 2
+    ncopies = args.copies or max(3, math.ceil(768e6 / pool_bytes))
+    if args.warm:
+        ncopies = 1
+    copies = [(pkv.Pool(base["k_pool"], base["v_pool"]), base["q"])]
+    for _ in range(ncopies - 1):
+        copies.append((pkv.Pool(base["k_pool"].clone(), base["v_pool"].clone()), base["q"].clone()))
+    ws = torch.zeros(pkv.pkv_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    kv_indptr = torch.zeros(batch.B + 1, dtype=torch.int32, device=dev)
+    out = torch.zeros((batch.B, batch.Hq, batch.D), dtype=torch.int16, device=dev)
+    seq, idx = base["seq_lens"], base["kv_indices"]
+    k_new, v_new = base["k_new"], base["v_new"]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        pool, q = copies[i % ncopies]
+        pkv.pkv_build_metadata(desc, seq, 0, kv_indptr, ws, stream)
+        pkv.pkv_append_kv(pool, k_new, v_new, kv_indptr, idx, seq, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.pkv_decode_partials(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.pkv_decode_merge(desc, batch.B, ws, out, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    plan = pkv.pkv_debug_validate(desc, seq, kv_indptr, idx, batch.num_pages, ws)
+    if plan["status"] != pkv.PKV_OK:
+        raise RuntimeError("device metadata failed validation")
+
+    K = args.steps
+    evs = None
+    if not args.no_kernel_events:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    # hold the GPU (bounded spin) while the host enqueues the K steps
+    torch.cuda._sleep(int(40e6))
+    start.record(stream)
+    for i in range(K):
+        step(i, evs[i] if evs else None)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+
+    call_bytes, step_bytes = algorithmic_bytes(batch)
+    res = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": batch.name, "seed": batch.seed, "B": batch.B, "Hq": batch.Hq,
+                   "Hkv": batch.Hkv, "head_dim": batch.D, "page_size": batch.P,
+                   "kv_tokens": batch.kv_tokens, "pool_pages": batch.num_pages,
+                   "pool_copies": ncopies, "target_items": desc.target_items or "default",
+                   "plan_items": plan["items"], "plan_chunk_pages": plan["chunk"],
+                   "parallelism": "single-gpu"},
+        "step_bytes": step_bytes,
+        "call_bytes": call_bytes,
+    }
+    if evs:
+        split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+        achieved = call_bytes / (split_ms * 1e-3) / 1e9
+        ctr = counters_for_current_kernel()
+        traffic = None
+        if ctr is not None:
+            traffic = ctr.get("traffic_bytes_per_launch", {}).get(batch.name)
+        res.update({
+            "us_per_call": round(call_ms * 1e3, 2),
+            "split_us": round(split_ms * 1e3, 2),
+            "merge_us": round(merge_ms * 1e3, 2),
+            "call_GBps": round(call_bytes / (call_ms * 1e-3) / 1e9, 1),
+            "call_frac_of_peak": round(call_bytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "roofline": {"bound": "hbm", "kernel": "split_kernel", "achieved": round(achieved, 1),
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
+        })
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * pkv.h - C ABI of the paged-KV split-KV decode attention library (libpkv.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  At every decode step each request contributes one query
+ * token with Hq query heads that share Hkv key/value heads (grouped-query
+ * attention, G = Hq / Hkv query heads per KV head).  Query head hq attends over
+ * the request's cached tokens through KV head hq / G:
+ *
+ *     out[b, hq, :] = softmax_t( sm_scale * q[b, hq, :] . K_t[hq / G, :] ) V_t[hq / G, :]
+ *
+ * for t = 0 .. seq_lens[b] - 1.  (Sources, the AstrAI project pages: the
+ * paged decode wrapper's docstring, AstrAI compare v1.3.12..6f09b1d,
+ * astrai/extension/attention_ops.py, attn_paged_decode; the reference
+ * semantics of TorchNativeBackend.fwd_decode in
+ * astrai/extension/attention_backend.py on the same page.)  The decode query is
+ * the newest position, so a causal mask removes nothing.
+ *
+ * Paged KV pool.  K and V of one layer live in fixed-size pages of a pool shared
+ * by all requests.  This library lays a pool out page-major, then head-major:
+ *
+ *     K, V : bf16 [num_pages][Hkv][page_size][head_dim]   (contiguous)
+ *
+ * so the page_size x head_dim tile of one (page, KV head) is one contiguous
+ * run of bytes.  Token t of request b lives in page
+ * kv_indices[kv_indptr[b] + t / page_size] at offset t % page_size (the pages'
+ * PagePool addressing: page index pos // page_size, offset pos % page_size,
+ * astrai/inference/core/cache.py on the compare page).  kv_indptr counts
+ * pages: kv_indptr[0] = 0, kv_indptr[b + 1] = kv_indptr[b] + ceil(seq_lens[b] /
+ * page_size); it is built once per step and reused by every layer (AstrAI
+ * commit 05739629, astrai/inference: the bind_tasks bullet on the prefix sum).
+ *
+ * Split KV.  Each request's pages are cut into contiguous chunks.  A first
+ * kernel writes each chunk's normalised partial output and log-sum-exp into a
+ * caller-owned workspace; a merge kernel combines them with log-sum-exp weights
+ * (commits by ViperEkura on the author-search page: split partials o_part /
+ * ml_part, one combine kernel, compute_num_splits retuned so the grid fills
+ * the chip).  Requests planned with one chunk are written directly.
+ *
+ * Conventions for every entry point.
+ *  - Pointers documented "device" are device memory owned by the caller; the
+ *    library keeps no pointer after a call returns, holds no global state and
+ *    allocates nothing (no hipMalloc / hipFree in any entry point).
+ *  - "stream" is a hipStream_t passed as void* (NULL = the default stream).
+ *    Launch entry points enqueue work on it and return without synchronising;
+ *    nothing on the launch path reads device memory from the host, so a
+ *    sequence of launches can be captured into a hipGraph.
+ *  - Every entry point returns a pkv_status.  Only host-checkable conditions
+ *    are reported (null pointers, shapes, capacities, workspace size, launch
+ *    failure).  The contents of device arrays are not validated on the launch
+ *    path: out-of-range page ids are skipped by the kernels (never read or
+ *    written) and latched in a device error word that pkv_debug_validate
+ *    reports.
+ *  - bf16 values are IEEE binary32 upper halves; fp32 -> bf16 rounds to
+ *    nearest, ties to even.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,          /* null pointer, negative size, inconsistent shapes */
+  PKV_ERR_UNSUPPORTED = 2,          /* head_dim / page_size / group size not compiled in */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below pkv_workspace_bytes(desc) */
+  PKV_ERR_CAPACITY = 4,             /* batch or forced split count above the descriptor's capacity */
+  PKV_ERR_LAUNCH = 5,               /* the HIP runtime rejected a kernel launch */
+  PKV_ERR_DEVICE_DATA = 6           /* pkv_debug_validate found bad device metadata */
+} pkv_status;
+
+/* Static description of one message of pkv_status (never NULL). */
+const char* pkv_status_str(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int32_t pkv_version(void);
+
+/* One layer's paged K/V pool (device memory owned by the caller).
+ * k, v: bf16 [num_pages][num_kv_heads][page_size][head_dim], contiguous. */
+typedef struct pkv_pool {
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  void* k;
+  void* v;
+} pkv_pool;
+
+/* Fixed capacities and shapes.  They fix the launch grids, so one captured
+ * hipGraph per batch size replays for any seq_lens within capacity (a grid
+ * that followed the step's longest sequence made graph replay unstable on the
+ * pages, which fixed it by sizing the split grid from the context capacity;
+ * commits by ViperEkura, PagedKV::host_kv_len bullet).
+ *
+ *  max_batch          requests per call (>= 1)
+ *  num_q_heads        Hq; num_kv_heads must divide it
+ *  num_kv_heads       Hkv
+ *  head_dim           D, 64 or 128
+ *  page_size          P, a multiple of 1024 / D (16 for both head dims)
+ *  max_splits         most chunks one request is cut into (1 .. 4096)
+ *  target_items       wanted number of (chunk, KV head) work items per call; the
+ *                     planner picks the chunk length so the batch yields about
+ *                     this many.  0 selects the default (2048).
+ *  min_chunk_pages    shortest chunk the planner makes, in pages (0 = default 4)
+ */
+typedef struct pkv_desc {
+  int32_t max_batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_splits;
+  int32_t target_items;
+  int32_t min_chunk_pages;
+} pkv_desc;
+
+/* Bytes of workspace a descriptor needs (split plan, partial outputs and
+ * log-sum-exp values, error word), or 0 if the descriptor is invalid.  The
+ * caller allocates it once (any device allocation, 256-byte aligned) and passes
+ * it to every pkv_build_metadata / pkv_decode call of that descriptor.  Its
+ * contents need no initialisation: pkv_build_metadata writes everything the
+ * decode reads. */
+size_t pkv_workspace_bytes(const pkv_desc* desc);
+
+/* Step metadata, once per decode step (before the per-layer calls).
+ *
+ * From seq_lens (device int32 [batch]: tokens each request attends to this
+ * step, the token appended this step included) it writes
+ *   kv_indptr   device int32 [batch + 1], page prefix sums as defined above,
+ * and the split plan into the workspace.  Plan rule, N = total pages:
+ *   chunk     = max(min_chunk_pages, ceil(num_kv_heads * N / target_items))
+ *   nsplit[b] = min(max_splits, ceil(pages_b / chunk))      (0 if pages_b = 0)
+ *   forced_splits > 0 overrides: nsplit[b] = min(forced_splits, pages_b, max_splits)
+ * and split s of request b covers pages [s*pages_b/nsplit_b, (s+1)*pages_b/nsplit_b).
+ * Negative seq_lens count as 0 and latch the device error word.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_CAPACITY (batch > max_batch, or
+ * batch * min(forced_splits, max_splits) above the workspace's chunk capacity),
+ * PKV_ERR_WORKSPACE_TOO_SMALL, PKV_ERR_LAUNCH. */
+int pkv_build_metadata(const pkv_desc* desc, const int32_t* seq_lens, int32_t batch,
+                       int32_t forced_splits, int32_t* kv_indptr, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* KV append (once per layer, after pkv_build_metadata): writes this step's
+ * token of every request into the pool; on the pages this is an indexed store
+ * into the layer's K and V buffers at out_cache_loc before the attention call
+ * (attention_backend.py, CudaBackend.fwd_decode).  The token goes to position seq_lens[b] - 1:
+ *   K[kv_indices[kv_indptr[b] + pos / P]][h][pos % P][:] = k_new[b][h][:], same for V.
+ *  k_new, v_new   device bf16 [batch][num_kv_heads][head_dim]
+ *  kv_indptr      device int32 [batch + 1] (from pkv_build_metadata)
+ *  kv_indices     device int32 [num_indices], physical page ids
+ *  seq_lens       device int32 [batch], post-append lengths; <= 0 writes nothing
+ * Two requests must not target the same slot (the writes would race).
+ * Page ids outside [0, num_pages) or index positions outside [0, num_indices)
+ * are skipped. */
+int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
+                  const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
+                  const int32_t* seq_lens, int32_t batch, void* stream);
+
+/* Decode attention for one layer: split kernel, then merge kernel.
+ *  q            device bf16 [batch][num_q_heads][head_dim], contiguous
+ *  kv_indptr    device int32 [batch + 1] written by pkv_build_metadata this step
+ *  kv_indices   device int32 [num_indices]
+ *  seq_lens     device int32 [batch], the same array pkv_build_metadata read
+ *  sm_scale     softmax scale (usually 1 / sqrt(head_dim))
+ *  workspace    the workspace pkv_build_metadata wrote this step
+ *  out          device bf16 [batch][num_q_heads][head_dim]; a request with
+ *               seq_len 0 gets a zero row
+ * Accumulation is fp32 (scores, online softmax, partials, merge).  For a fixed
+ * plan the result is deterministic (no atomics in the arithmetic). */
+int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+               const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
+               const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
+               size_t workspace_bytes, void* out, void* stream);
+
+/* The two halves of pkv_decode, for callers that time or schedule them
+ * separately.  pkv_decode == pkv_decode_partials followed by pkv_decode_merge
+ * on the same stream with the same arguments. */
+int pkv_decode_partials(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                        const int32_t* kv_indptr, const int32_t* kv_indices,
+                        int32_t num_indices, const int32_t* seq_lens, int32_t batch,
+                        float sm_scale, void* workspace, size_t workspace_bytes, void* out,
+                        void* stream);
+int pkv_decode_merge(const pkv_desc* desc, int32_t batch, void* workspace,
+                     size_t workspace_bytes, void* out, void* stream);
+
+/* Debug only (synchronises the stream; not capturable).  Copies the plan to
+ * host arrays and checks device metadata.
+ *  nsplit_out   host int32 [batch] or NULL: chunks per request
+ *  chunk_out    host int32 or NULL: planned chunk length in pages
+ *  items_out    host int32 or NULL: total (request, chunk) items
+ * Returns PKV_ERR_DEVICE_DATA if kv_indptr is not the page prefix sum of
+ * seq_lens, any listed page id is outside [0, num_pages), kv_indptr[batch]
+ * exceeds num_indices, or a kernel latched the device error word (which it
+ * then clears). */
+int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, int32_t num_indices, int32_t num_pages,
+                       int32_t batch, void* workspace, size_t workspace_bytes,
+                       int32_t* nsplit_out, int32_t* chunk_out, int32_t* items_out,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

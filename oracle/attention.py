@@ -17,25 +17,25 @@ the hunk or bullet, as the pages have no section numbers):
   of the paged kernel's wrapper (same page, astrai/extension/attention_ops.py,
   attn_paged_decode docstring: q [batch, n_heads, head_dim], per-request
   lengths from kv_indptr).  The decode query is the newest position, so the
-  causal mask removes nothing (commits by ViperEkura: "Force is_causal=True in
-  CUDA decode backend").
+  causal mask removes nothing (commits by ViperEkura: the bullet that makes the
+  CUDA decode backend always causal).
 * Paged addressing: token t of request b lives in page
   kv_indices[kv_indptr[b] + t // P] at offset t % P (same page,
   astrai/inference/core/cache.py, PagePool._extend_slot: page index is
   pos // page_size, slot offset is pos % page_size).  kv_indptr is a prefix
   sum over requests, built once per step (AstrAI commit 05739629,
-  astrai/inference: "bind_tasks builds kv_indptr (prefix sum of seq_lens) a
-  single time").  Here it counts pages, not tokens.
+  astrai/inference: the bind_tasks bullet on the kv_indptr prefix sum).  Here
+  it counts pages, not tokens.
 * Split KV and merge: a request's KV range is cut into chunks whose partial
-  outputs and (max, sum) statistics are merged by a single combine kernel
-  (commits by ViperEkura: split-partial tensors o_part / ml_part; "single
-  combine kernel"; compute_num_splits retune).  Each partial is stored as the
+  outputs and (max, sum) statistics are merged by one combine kernel
+  (commits by ViperEkura: split-partial tensors o_part / ml_part, the shared
+  combine kernel, the compute_num_splits retune).  Each partial is stored as the
   chunk's normalised output and its log-sum-exp; the merge weights each chunk
   by exp(lse_s - max lse).
 * KV append: the token written this step goes to position seq_len - 1
   (cache.py, bind_tasks: write_pos = seq_lens - 1).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 kv_indptr in pages; KV head of query head hq is hq // G; seq_len includes
 the token appended this step; empty chunks have lse = -inf and weight 0; a
 request with seq_len 0 gets a zero output row; chunks are contiguous runs of

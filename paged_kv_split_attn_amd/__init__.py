@@ -1,0 +1,287 @@
+"""paged_kv_split_attn_amd: paged-KV split-KV decode attention for MI355X (gfx950).
+
+Thin ctypes binding over libpkv.so, whose C ABI is declared in include/pkv.h.
+Each function here has the name of the C entry point it calls and only
+marshals arguments: torch tensors supply device pointers, torch's current
+stream supplies the hipStream_t.  Every step of the computation runs in the
+library's HIP kernels; there is no Python or CPU fallback.  If the library is
+missing or fails to load, the calls raise.
+
+torch is imported before the library is loaded so that libpkv binds to the
+HIP runtime torch already holds (both carry the soname libamdhip64.so.7).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PkvError",
+    "Desc",
+    "Pool",
+    "library_path",
+    "load_library",
+    "declared_functions",
+    "pkv_status_str",
+    "pkv_version",
+    "pkv_workspace_bytes",
+    "pkv_build_metadata",
+    "pkv_append_kv",
+    "pkv_decode",
+    "pkv_decode_partials",
+    "pkv_decode_merge",
+    "pkv_debug_validate",
+    "PKV_OK",
+    "PKV_ERR_INVALID_ARG",
+    "PKV_ERR_UNSUPPORTED",
+    "PKV_ERR_WORKSPACE_TOO_SMALL",
+    "PKV_ERR_CAPACITY",
+    "PKV_ERR_LAUNCH",
+    "PKV_ERR_DEVICE_DATA",
+]
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = 1
+PKV_ERR_UNSUPPORTED = 2
+PKV_ERR_WORKSPACE_TOO_SMALL = 3
+PKV_ERR_CAPACITY = 4
+PKV_ERR_LAUNCH = 5
+PKV_ERR_DEVICE_DATA = 6
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "pkv.h")
+
+
+def library_path() -> str:
+    return os.environ.get("PKV_LIBRARY", os.path.join(_PKG, "lib", "libpkv.so"))
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+class _CPool(ctypes.Structure):
+    _fields_ = [("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+class _CDesc(ctypes.Structure):
+    _fields_ = [("max_batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("target_items", ctypes.c_int32), ("min_chunk_pages", ctypes.c_int32)]
+
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_SIGNATURES = {
+    "pkv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_version": (_i32, []),
+    "pkv_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_CDesc)]),
+    "pkv_build_metadata": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _i32, _i32, _vp, _vp,
+                                          ctypes.c_size_t, _vp]),
+    "pkv_append_kv": (ctypes.c_int, [ctypes.POINTER(_CPool), _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                     _vp]),
+    "pkv_decode": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp, _vp,
+                                  _i32, _vp, _i32, ctypes.c_float, _vp, ctypes.c_size_t, _vp,
+                                  _vp]),
+    "pkv_decode_partials": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp,
+                                           _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
+                                           ctypes.c_size_t, _vp, _vp]),
+    "pkv_decode_merge": (ctypes.c_int, [ctypes.POINTER(_CDesc), _i32, _vp, ctypes.c_size_t, _vp,
+                                        _vp]),
+    "pkv_debug_validate": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _vp, _vp, _i32, _i32, _i32,
+                                          _vp, ctypes.c_size_t, _i32p, _i32p, _i32p, _vp]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libpkv.so once and declare its signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"libpkv.so not found at {p}; build it with `python -m paged_kv_split_attn_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def declared_functions(header: str = _HEADER):
+    """Names of the functions include/pkv.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PKV_OK:
+        raise PkvError(fn, status, pkv_status_str(status))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor, name: str, dtypes=None, numel: Optional[int] = None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32 = (torch.int32,)
+
+
+@dataclass
+class Desc:
+    """Fixed capacities and shapes (mirror of pkv_desc)."""
+
+    max_batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    max_splits: int = 256
+    target_items: int = 0
+    min_chunk_pages: int = 0
+
+    def c(self) -> _CDesc:
+        return _CDesc(self.max_batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
+                      self.page_size, self.max_splits, self.target_items, self.min_chunk_pages)
+
+
+@dataclass
+class Pool:
+    """One layer's pool: k, v are bf16 [num_pages, Hkv, page_size, head_dim] device tensors."""
+
+    k: torch.Tensor
+    v: torch.Tensor
+
+    def c(self) -> _CPool:
+        if self.k.shape != self.v.shape or self.k.dim() != 4:
+            raise ValueError("k and v must both be [num_pages, Hkv, page_size, head_dim]")
+        n, h, p, d = self.k.shape
+        return _CPool(n, p, h, d, _ptr(self.k, "pool.k", _BF16), _ptr(self.v, "pool.v", _BF16))
+
+
+def pkv_status_str(status: int) -> str:
+    return load_library().pkv_status_str(int(status)).decode()
+
+
+def pkv_version() -> int:
+    return int(load_library().pkv_version())
+
+
+def pkv_workspace_bytes(desc: Desc) -> int:
+    n = load_library().pkv_workspace_bytes(ctypes.byref(desc.c()))
+    if n == 0:
+        raise PkvError("pkv_workspace_bytes", PKV_ERR_INVALID_ARG, "invalid descriptor")
+    return int(n)
+
+
+def pkv_build_metadata(desc: Desc, seq_lens: torch.Tensor, forced_splits: int,
+                       kv_indptr: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    B = seq_lens.numel()
+    st = load_library().pkv_build_metadata(
+        ctypes.byref(desc.c()), _ptr(seq_lens, "seq_lens", _I32), B, int(forced_splits),
+        _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("pkv_build_metadata", st)
+
+
+def pkv_append_kv(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor, kv_indptr: torch.Tensor,
+                  kv_indices: torch.Tensor, seq_lens: torch.Tensor, stream=None) -> None:
+    B = seq_lens.numel()
+    cp = pool.c()
+    per = cp.num_kv_heads * cp.head_dim
+    st = load_library().pkv_append_kv(
+        ctypes.byref(cp), _ptr(k_new, "k_new", _BF16, B * per), _ptr(v_new, "v_new", _BF16, B * per),
+        _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
+        kv_indices.numel(), _ptr(seq_lens, "seq_lens", _I32), B, _stream(stream))
+    _check("pkv_append_kv", st)
+
+
+def _decode_args(pool, desc, q, kv_indptr, kv_indices, seq_lens, sm_scale, workspace, out, stream):
+    B = seq_lens.numel()
+    n = B * desc.num_q_heads * desc.head_dim
+    return (ctypes.byref(pool.c()), ctypes.byref(desc.c()), _ptr(q, "q", _BF16, n),
+            _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
+            kv_indices.numel(), _ptr(seq_lens, "seq_lens", _I32), B, float(sm_scale),
+            _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _ptr(out, "out", _BF16, n), _stream(stream))
+
+
+def pkv_decode(pool: Pool, desc: Desc, q: torch.Tensor, kv_indptr: torch.Tensor,
+               kv_indices: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float,
+               workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    st = load_library().pkv_decode(*_decode_args(pool, desc, q, kv_indptr, kv_indices, seq_lens,
+                                                 sm_scale, workspace, out, stream))
+    _check("pkv_decode", st)
+
+
+def pkv_decode_partials(pool: Pool, desc: Desc, q: torch.Tensor, kv_indptr: torch.Tensor,
+                        kv_indices: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float,
+                        workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    st = load_library().pkv_decode_partials(*_decode_args(pool, desc, q, kv_indptr, kv_indices,
+                                                          seq_lens, sm_scale, workspace, out,
+                                                          stream))
+    _check("pkv_decode_partials", st)
+
+
+def pkv_decode_merge(desc: Desc, batch: int, workspace: torch.Tensor, out: torch.Tensor,
+                     stream=None) -> None:
+    st = load_library().pkv_decode_merge(
+        ctypes.byref(desc.c()), int(batch), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(out, "out", _BF16), _stream(stream))
+    _check("pkv_decode_merge", st)
+
+
+def pkv_debug_validate(desc: Desc, seq_lens: torch.Tensor, kv_indptr: torch.Tensor,
+                       kv_indices: torch.Tensor, num_pages: int, workspace: torch.Tensor,
+                       stream=None) -> dict:
+    """Synchronising check of device metadata; returns the status and the plan."""
+    B = seq_lens.numel()
+    nsplit = (ctypes.c_int32 * max(B, 1))()
+    chunk = ctypes.c_int32(0)
+    items = ctypes.c_int32(0)
+    st = load_library().pkv_debug_validate(
+        ctypes.byref(desc.c()), _ptr(seq_lens, "seq_lens", _I32),
+        _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
+        kv_indices.numel(), int(num_pages), B, _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), nsplit, ctypes.byref(chunk),
+        ctypes.byref(items), _stream(stream))
+    if st not in (PKV_OK, PKV_ERR_DEVICE_DATA):
+        _check("pkv_debug_validate", st)
+    return {"status": st, "nsplit": list(nsplit)[:B], "chunk": chunk.value, "items": items.value}

@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, answers host-only queries, rejects bad arguments before any
+launch, and links no device allocator."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import paged_kv_split_attn_amd as pkv
+
+LIB = pkv.library_path()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libpkv.so is not built (python -m paged_kv_split_attn_amd.build)")
+    return pkv.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    names = pkv.declared_functions()
+    assert set(names) == {
+        "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
+        "pkv_append_kv", "pkv_decode", "pkv_decode_partials", "pkv_decode_merge",
+        "pkv_debug_validate"}
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in pkv.declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_no_device_allocation_linked():
+    out = subprocess.run(["nm", "-D", "--undefined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    undefined = {ln.split()[-1].split("@")[0] for ln in out.splitlines() if ln.strip()}
+    for bad in ("hipMalloc", "hipFree", "hipMallocAsync", "hipFreeAsync", "hipMallocManaged",
+                "hipHostMalloc", "hipExtMallocWithFlags", "hipMallocPitch"):
+        assert bad not in undefined, bad
+
+
+def test_status_strings_and_version(lib):
+    assert pkv.pkv_status_str(pkv.PKV_OK) == "ok"
+    for st in range(1, 7):
+        assert pkv.pkv_status_str(st) not in ("ok", "unknown status")
+    assert pkv.pkv_status_str(99) == "unknown status"
+    assert pkv.pkv_version() >> 16 == 1
+
+
+def _desc(**kw):
+    base = dict(max_batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                max_splits=256, target_items=0, min_chunk_pages=0)
+    base.update(kw)
+    return pkv.Desc(**base)
+
+
+def test_workspace_bytes(lib):
+    d = _desc()
+    n = pkv.pkv_workspace_bytes(d)
+    # max items = min(16 * 256, ceil(2048 / 8) + 16) = 272 (request, chunk) items
+    items = 272
+    expect = 256  # header
+    for sz in (4 * 17, 8 * items, 4 * items * 32, 4 * items * 32 * 128):
+        expect += (sz + 255) // 256 * 256
+    assert n == expect
+    assert pkv.pkv_workspace_bytes(_desc(max_batch=1, max_splits=3)) < n
+    for bad in (dict(num_q_heads=30), dict(max_batch=0), dict(max_splits=0),
+                dict(max_splits=5000), dict(target_items=-1)):
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_workspace_bytes(_desc(**bad))
+
+
+def _raw(lib, name, *args):
+    return getattr(lib, name)(*args)
+
+
+def test_host_checks_reject_before_launch(lib):
+    d = _desc().c()
+    pool = pkv._CPool(100, 16, 8, 128, 0x1000, 0x2000)
+    ws_bytes = pkv.pkv_workspace_bytes(_desc())
+    fake = 0x10000  # never dereferenced: every call below fails a host check first
+    B = ctypes.byref
+    # null pointers
+    assert _raw(lib, "pkv_build_metadata", B(d), None, 4, 0, fake, fake, ws_bytes, None) == 1
+    assert _raw(lib, "pkv_decode", B(pool), B(d), None, fake, fake, 10, fake, 4, 0.1, fake,
+                ws_bytes, fake, None) == 1
+    # batch above capacity
+    assert _raw(lib, "pkv_build_metadata", B(d), fake, 17, 0, fake, fake, ws_bytes, None) == 4
+    # workspace too small
+    assert _raw(lib, "pkv_build_metadata", B(d), fake, 4, 0, fake, fake, ws_bytes - 1, None) == 3
+    assert _raw(lib, "pkv_decode", B(pool), B(d), fake, fake, fake, 10, fake, 4, 0.1, fake,
+                ws_bytes - 1, fake, None) == 3
+    # forced splits beyond the item capacity: 16 requests x 256 splits > 272 items
+    assert _raw(lib, "pkv_build_metadata", B(d), fake, 16, 256, fake, fake, ws_bytes, None) == 4
+    # unsupported head_dim / page_size / group size
+    for bad in (dict(head_dim=96), dict(page_size=12), dict(page_size=24),
+                dict(num_q_heads=48, num_kv_heads=8)):
+        db = _desc(**bad)
+        assert _raw(lib, "pkv_build_metadata", B(db.c()), fake, 4, 0, fake, fake, 1 << 30,
+                    None) == 2
+    # pool that disagrees with the descriptor
+    pool_bad = pkv._CPool(100, 16, 4, 128, 0x1000, 0x2000)
+    assert _raw(lib, "pkv_decode", B(pool_bad), B(d), fake, fake, fake, 10, fake, 4, 0.1, fake,
+                ws_bytes, fake, None) == 1
+    # NaN scale
+    assert _raw(lib, "pkv_decode", B(pool), B(d), fake, fake, fake, 10, fake, 4, float("nan"),
+                fake, ws_bytes, fake, None) == 1
+    # append with a head_dim that is not a multiple of 8 channels
+    pool_odd = pkv._CPool(100, 16, 8, 60, 0x1000, 0x2000)
+    assert _raw(lib, "pkv_append_kv", B(pool_odd), fake, fake, fake, fake, 10, fake, 4, None) == 2
+
+
+def test_binding_requires_gpu_tensors(lib):
+    import torch
+    d = _desc()
+    with pytest.raises(ValueError):
+        pkv.pkv_build_metadata(d, torch.zeros(4, dtype=torch.int32), 0,
+                               torch.zeros(5, dtype=torch.int32), torch.zeros(10, dtype=torch.uint8))

@@ -1,0 +1,228 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on the GPU.
+
+Integer work (kv_indptr, split plan, KV append) must be bit-exact; decode
+outputs must be within max |err| 1e-2 and mean |err| 1e-3 of the oracle with
+bf16 inputs/outputs and fp32 accumulation.  Pools carry NaN in every unwritten
+slot and the workspace starts as all-ones bytes (NaN as fp32), so any stray
+read or unwritten partial shows up as NaN.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_split_attn_amd as pkv
+import workloads as W
+from gpu_util import GpuRun, compare, forced_desc, make_desc, oracle_out, say
+
+pytestmark = pytest.mark.gpu
+
+_BATCHES = {}
+_REFS = {}
+
+
+def cfg(i):
+    if i not in _BATCHES:
+        _BATCHES[i] = W.config(i)
+    return _BATCHES[i]
+
+
+def ref(i):
+    if i not in _REFS:
+        _REFS[i] = oracle_out(cfg(i))
+    return _REFS[i]
+
+
+def plan_of(batch, desc, forced):
+    T = desc.target_items or 2048
+    cmin = desc.min_chunk_pages or 4
+    return oracle.plan_splits(batch.seq_lens, batch.P, batch.Hkv, desc.max_splits, T, cmin, forced)
+
+
+# ------------------------------------------------------------------ metadata
+
+def _random_lengths_batch(seed, B, with_zeros):
+    rng = np.random.default_rng(seed)
+    L = rng.integers(0 if with_zeros else 1, 5000, size=B)
+    return W.make_batch(name=f"lens{seed}", seed=seed, B=B, Hq=8, Hkv=2, D=64, P=16,
+                        lengths=L, poison=False)
+
+
+@pytest.mark.parametrize("case", ["c1", "c2", "c3", "c4", "c5", "rand0", "rand1", "rand_big"])
+@pytest.mark.parametrize("forced", [0, 3])
+def test_metadata_bit_exact(case, forced):
+    say(f"metadata case={case} forced={forced}")
+    if case.startswith("c"):
+        batch = cfg(int(case[1]))
+    elif case == "rand_big":
+        batch = _random_lengths_batch(77, 1500, True)  # more requests than one block scans at once
+    else:
+        batch = _random_lengths_batch(int(case[-1]) + 10, 37, case == "rand0")
+    desc = forced_desc(batch, forced) if forced else make_desc(batch)
+    run = GpuRun(batch, desc)
+    run.metadata(forced)
+    torch.cuda.synchronize()
+    ip = run.kv_indptr.cpu().numpy()
+    assert np.array_equal(ip, oracle.kv_indptr(batch.seq_lens, batch.P))
+    info = run.validate()
+    assert info["status"] == pkv.PKV_OK
+    plan = plan_of(batch, desc, forced)
+    assert info["nsplit"] == list(plan["nsplit"])
+    assert info["items"] == plan["num_items"]
+    assert info["chunk"] == (0 if forced else plan["chunk"])
+
+
+# -------------------------------------------------------------------- append
+
+@pytest.mark.parametrize("which", ["small", "c5"])
+def test_append_bit_exact(which):
+    say(f"append {which}")
+    if which == "c5":
+        batch = cfg(5)
+    else:
+        batch = W.make_batch(name="app", seed=41, B=9, Hq=8, Hkv=2, D=128, P=16,
+                             lengths=np.array([1, 15, 16, 17, 33, 64, 100, 2, 48]), append=True)
+    run = GpuRun(batch, make_desc(batch))
+    run.metadata()
+    run.append()
+    torch.cuda.synchronize()
+    ip = oracle.kv_indptr(batch.seq_lens, batch.P)
+    k_ref, v_ref = oracle.append_kv(batch.k_pool, batch.v_pool, batch.k_new, batch.v_new, ip,
+                                    batch.kv_indices, batch.seq_lens, batch.P)
+    k = run.t["k_pool"].cpu().numpy().view(np.uint16)
+    v = run.t["v_pool"].cpu().numpy().view(np.uint16)
+    assert np.array_equal(k, k_ref)
+    assert np.array_equal(v, v_ref)
+
+
+# -------------------------------------------------------------------- decode
+
+DECODE_CASES = [
+    (1, 1), (1, 3), (1, 0),
+    (2, 0), (2, 1), (2, 32),
+    (3, 0), (3, 1), (3, 7),
+    (4, 0), (4, 1), (4, 256),
+    (5, 0),
+]
+
+
+@pytest.mark.parametrize("i,forced", DECODE_CASES, ids=[f"cfg{i}-splits{f or 'plan'}" for i, f in DECODE_CASES])
+def test_decode_parity(i, forced):
+    batch = cfg(i)
+    say(f"decode cfg{i} ({batch.name}) forced={forced}")
+    desc = forced_desc(batch, forced) if forced else make_desc(batch)
+    run = GpuRun(batch, desc)
+    got = run.step(forced)
+    info = run.validate()
+    assert info["status"] == pkv.PKV_OK
+    if forced:
+        assert all(n == min(forced, len(pl)) for n, pl in zip(info["nsplit"], batch.page_lists))
+    compare(got, ref(i), f"cfg{i} splits={forced or 'plan'} items={info['items']}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,P", [
+    (8, 8, 128, 16),   # G = 1
+    (16, 8, 128, 16),  # G = 2
+    (24, 8, 64, 16),   # G = 3
+    (64, 8, 128, 16),  # G = 8: two waves per KV head
+    (32, 4, 64, 32),   # two rounds per page at D = 64
+    (8, 2, 128, 32),   # four rounds per page at D = 128
+    (8, 2, 128, 64),   # eight rounds per page
+])
+def test_decode_shapes(Hq, Hkv, D, P):
+    say(f"shapes Hq={Hq} Hkv={Hkv} D={D} P={P}")
+    batch = W.make_batch(name="shape", seed=Hq * 131 + D + P, B=5, Hq=Hq, Hkv=Hkv, D=D, P=P,
+                         lengths=np.array([1, P - 1, P + 1, 5 * P + 3, 700]))
+    expect = oracle_out(batch)
+    for forced in (0, 2):
+        desc = forced_desc(batch, forced) if forced else make_desc(batch, min_chunk_pages=1,
+                                                                   target_items=16)
+        got = GpuRun(batch, desc).step(forced)
+        compare(got, expect, f"Hq={Hq} Hkv={Hkv} D={D} P={P} forced={forced}")
+
+
+def test_seq_len_one_is_exact():
+    say("seq_len one")
+    batch = W.make_batch(name="len1", seed=5, B=6, Hq=32, Hkv=8, D=128, P=16,
+                         lengths=np.ones(6, np.int64), num_pages=40)
+    got = GpuRun(batch, make_desc(batch)).step()
+    G = batch.Hq // batch.Hkv
+    for b in range(batch.B):
+        page = batch.page_lists[b][0]
+        for hq in range(batch.Hq):
+            assert np.array_equal(got[b, hq], batch.v_pool[page, hq // G, 0])
+
+
+def test_zero_length_requests_give_zero_rows():
+    say("zero lengths")
+    batch = W.make_batch(name="zeros", seed=6, B=5, Hq=32, Hkv=8, D=128, P=16,
+                         lengths=np.array([0, 100, 0, 1, 17]))
+    got = GpuRun(batch, make_desc(batch, min_chunk_pages=1, target_items=64)).step()
+    assert not got[0].any() and not got[2].any()
+    compare(got, oracle_out(batch), "zero-length mix")
+
+
+def test_deterministic_and_page_permutation_invariant():
+    say("determinism / permutation cfg3")
+    batch = cfg(3)
+    desc = make_desc(batch)
+    a = GpuRun(batch, desc).step()
+    b = GpuRun(batch, desc).step()
+    assert np.array_equal(a, b)
+    c = GpuRun(W.permute_pool(batch, seed=1234), desc).step()
+    assert np.array_equal(a, c)
+
+
+def test_bad_page_id_is_skipped_and_reported():
+    say("bad page id")
+    batch = W.make_batch(name="bad", seed=8, B=3, Hq=8, Hkv=2, D=64, P=16,
+                         lengths=np.array([40, 50, 60]), poison=False)
+    run = GpuRun(batch, make_desc(batch))
+    # request 1's second page id points one past the pool: the kernels must skip it
+    pos = len(batch.page_lists[0]) + 1
+    run.t["kv_indices"][pos] = batch.num_pages
+    got = run.step()
+    info = run.validate()
+    assert info["status"] == pkv.PKV_ERR_DEVICE_DATA
+    assert run.validate()["status"] == pkv.PKV_ERR_DEVICE_DATA  # page id still bad
+    expect = oracle_out(batch)
+    compare(got[[0, 2]], expect[[0, 2]], "untouched requests")
+
+
+def test_graph_capture_replay_matches_eager():
+    say("graph replay")
+    batch = W.make_batch(name="graph", seed=9, B=8, Hq=32, Hkv=8, D=128, P=16,
+                         lengths=np.array([3000, 1, 700, 2048, 16, 4096, 999, 64]), append=True)
+    desc = make_desc(batch)
+    run = GpuRun(batch, desc)
+    full = batch.seq_lens.copy()
+    rng = np.random.default_rng(10)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run.step()  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.metadata()
+        run.append()
+        run.decode()
+    hk, hv = batch.k_pool.copy(), batch.v_pool.copy()
+    for rep in range(4):
+        lens = np.maximum(1, (full * rng.uniform(0.2, 1.0, size=batch.B)).astype(np.int32))
+        lists = [pl[: -(-int(L) // batch.P)] for pl, L in zip(batch.page_lists, lens)]
+        idx = np.concatenate(lists).astype(np.int32)
+        # the caller re-lays out kv_indices for the new lengths, in place
+        run.t["kv_indices"][: idx.size].copy_(torch.from_numpy(idx))
+        run.t["seq_lens"].copy_(torch.from_numpy(lens))
+        g.replay()
+        torch.cuda.synchronize()
+        replay_bits = run.out_bits().copy()
+        eager = run.step()
+        assert np.array_equal(replay_bits, eager), f"replay {rep} differs from eager"
+        # both the replay and the eager step wrote k_new/v_new at position lens-1
+        ip = oracle.kv_indptr(lens, batch.P)
+        hk, hv = oracle.append_kv(hk, hv, batch.k_new, batch.v_new, ip, idx, lens, batch.P)
+        expect = oracle.decode(batch.q, hk, hv, ip, idx, lens, batch.sm_scale, batch.P)
+        compare(eager, expect, f"replay {rep}")

@@ -43,6 +43,7 @@ __all__ = [
     "CONFIG_NAMES",
     "permute_pool",
     "identity_layout",
+    "to_device",
 ]
 
 
@@ -346,3 +347,27 @@ def identity_layout(batch: DecodeBatch) -> DecodeBatch:
     out = DecodeBatch(**{**batch.__dict__})
     out.k_pool, out.v_pool, out.page_lists, out.num_pages = k, v, lists, total
     return out
+
+
+def to_device(batch: DecodeBatch, device="cuda:0") -> dict:
+    """Copy a batch's arrays to device tensors (bf16 bits as int16, indices as int32).
+
+    Returns a dict with q, k_pool, v_pool, seq_lens, kv_indices and, for an
+    append batch, k_new and v_new.  Data movement only.
+    """
+    import torch
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+    d = {
+        "q": bits(batch.q),
+        "k_pool": bits(batch.k_pool),
+        "v_pool": bits(batch.v_pool),
+        "seq_lens": torch.from_numpy(batch.seq_lens.astype(np.int32)).to(device),
+        "kv_indices": torch.from_numpy(batch.kv_indices.astype(np.int32)).to(device),
+    }
+    if batch.append:
+        d["k_new"] = bits(batch.k_new)
+        d["v_new"] = bits(batch.v_new)
+    return d
