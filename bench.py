@@ -1,15 +1,16 @@
 """Benchmark of paged-KV split-KV decode attention on one MI355X.
 
 One step = the whole hot path for one layer of one decode step: build the step
-metadata (page prefix sums + split plan), append this step's K/V token of every
-request, split-KV decode kernel, merge kernel.  Inputs are seeded synthetic
+metadata (page prefix sums + work plan), append this step's K/V token of every
+request, then the split-KV decode kernel (partials and their merge in one
+launch).  Inputs are seeded synthetic
 batches already resident in HBM.  Between steps the pool rotates over several
 identical copies whose total size exceeds the 256 MB Infinity Cache, so every
 step streams its K/V from HBM.
 
 Timing: after W warm-up steps, a bounded spin kernel holds the GPU while the
 host enqueues all K timed steps; HIP events then bracket the K steps (step
-time) and every split-kernel launch (kernel time), on the stream the kernels
+time) and every decode-kernel launch (kernel time), on the stream the kernels
 run on.
 
 Prints one JSON line.  `value` is algorithmic GB/s of the whole step:
@@ -42,14 +43,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, help="workload preset 1..5 (3 = B=16 ragged)")
-    ap.add_argument("--target-items", type=int, default=0, help="planner target (0 = library default)")
-    ap.add_argument("--min-chunk", type=int, default=0)
-    ap.add_argument("--max-splits", type=int, default=256)
+    ap.add_argument("--groups", type=int, default=0, help="decode grid (0 = one workgroup per CU)")
+    ap.add_argument("--min-tiles", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0 = enough for 768 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
-                    help="time only whole steps (no events around the split kernel)")
+                    help="time only whole steps (no events around the decode kernel)")
     ap.add_argument("--warm", action="store_true", help="no pool rotation (cache-warm numbers)")
     return ap.parse_args()
 
@@ -132,8 +132,8 @@ def main():
           flush=True)
 
     desc = pkv.Desc(max_batch=batch.B, num_q_heads=batch.Hq, num_kv_heads=batch.Hkv,
-                    head_dim=batch.D, page_size=batch.P, max_splits=args.max_splits,
-                    target_items=args.target_items, min_chunk_pages=args.min_chunk)
+                    head_dim=batch.D, page_size=batch.P, num_workgroups=args.groups,
+                    min_tiles_per_group=args.min_tiles)
     base = W.to_device(batch, dev)
     pool_bytes = 2 * base["k_pool"].numel() * 2
     ncopies = args.copies or max(3, math.ceil(768e6 / pool_bytes))
@@ -155,12 +155,9 @@ def main():
         pkv.pkv_append_kv(pool, k_new, v_new, kv_indptr, idx, seq, stream)
         if ev is not None:
             ev[0].record(stream)
-        pkv.pkv_decode_partials(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, stream)
+        pkv.pkv_decode(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, stream)
         if ev is not None:
             ev[1].record(stream)
-        pkv.pkv_decode_merge(desc, batch.B, ws, out, stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -172,7 +169,7 @@ def main():
     K = args.steps
     evs = None
     if not args.no_kernel_events:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -202,28 +199,23 @@ def main():
         "config": {"workload": batch.name, "seed": batch.seed, "B": batch.B, "Hq": batch.Hq,
                    "Hkv": batch.Hkv, "head_dim": batch.D, "page_size": batch.P,
                    "kv_tokens": batch.kv_tokens, "pool_pages": batch.num_pages,
-                   "pool_copies": ncopies, "target_items": desc.target_items or "default",
-                   "plan_items": plan["items"], "plan_chunk_pages": plan["chunk"],
-                   "parallelism": "single-gpu"},
+                   "pool_copies": ncopies, "decode_grid": desc.groups(),
+                   "plan_workgroups": plan["groups"], "parallelism": "single-gpu"},
         "step_bytes": step_bytes,
         "call_bytes": call_bytes,
     }
     if evs:
-        split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-        call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
-        achieved = call_bytes / (split_ms * 1e-3) / 1e9
+        call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        achieved = call_bytes / (call_ms * 1e-3) / 1e9
         ctr = counters_for_current_kernel()
         traffic = None
         if ctr is not None:
             traffic = ctr.get("traffic_bytes_per_launch", {}).get(batch.name)
         res.update({
             "us_per_call": round(call_ms * 1e3, 2),
-            "split_us": round(split_ms * 1e3, 2),
-            "merge_us": round(merge_ms * 1e3, 2),
-            "call_GBps": round(call_bytes / (call_ms * 1e-3) / 1e9, 1),
-            "call_frac_of_peak": round(call_bytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "roofline": {"bound": "hbm", "kernel": "split_kernel", "achieved": round(achieved, 1),
+            "call_GBps": round(achieved, 1),
+            "call_frac_of_peak": round(achieved / PEAK_HBM_GBPS, 4),
+            "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(achieved, 1),
                          "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
         })

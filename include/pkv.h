@@ -30,12 +30,18 @@
  * page_size); it is built once per step and reused by every layer (AstrAI
  * commit 05739629, astrai/inference: the bind_tasks bullet on the prefix sum).
  *
- * Split KV.  Each request's pages are cut into contiguous chunks.  A first
- * kernel writes each chunk's normalised partial output and log-sum-exp into a
- * caller-owned workspace; a merge kernel combines them with log-sum-exp weights
- * (commits by ViperEkura on the author-search page: split partials o_part /
- * ml_part, one combine kernel, compute_num_splits retuned so the grid fills
- * the chip).  Requests planned with one chunk are written directly.
+ * Split KV.  The work of a call is the list of tiles (request b, group of query
+ * heads u, page p) in that order: every tile is one page of one KV head read
+ * for one group of query heads.  The list is cut into equal contiguous ranges,
+ * one per workgroup, and each workgroup's range again into one range per wave,
+ * so every wave streams the same number of pages whatever the mix of sequence
+ * lengths.  A range may cover a request's pages only in part: each part leaves
+ * an online-softmax partial (normalised output and log-sum-exp); parts of the
+ * same (request, head group) are merged with log-sum-exp weights, first inside
+ * the workgroup through LDS, then across workgroups by the last workgroup to
+ * finish its part (commits by ViperEkura on the author-search page: split
+ * partials o_part / ml_part, one combine kernel, the split count retuned so
+ * the grid fills the chip).  Everything runs in one kernel launch.
  *
  * Conventions for every entry point.
  *  - Pointers documented "device" are device memory owned by the caller; the
@@ -91,22 +97,21 @@ typedef struct pkv_pool {
   void* v;
 } pkv_pool;
 
-/* Fixed capacities and shapes.  They fix the launch grids, so one captured
+/* Fixed capacities and shapes.  They fix the launch grid, so one captured
  * hipGraph per batch size replays for any seq_lens within capacity (a grid
  * that followed the step's longest sequence made graph replay unstable on the
  * pages, which fixed it by sizing the split grid from the context capacity;
  * commits by ViperEkura, PagedKV::host_kv_len bullet).
  *
- *  max_batch          requests per call (>= 1)
- *  num_q_heads        Hq; num_kv_heads must divide it
- *  num_kv_heads       Hkv
- *  head_dim           D, 64 or 128
- *  page_size          P, a multiple of 1024 / D (16 for both head dims)
- *  max_splits         most chunks one request is cut into (1 .. 4096)
- *  target_items       wanted number of (chunk, KV head) work items per call; the
- *                     planner picks the chunk length so the batch yields about
- *                     this many.  0 selects the default (2048).
- *  min_chunk_pages    shortest chunk the planner makes, in pages (0 = default 4)
+ *  max_batch            requests per call (1 .. 65536)
+ *  num_q_heads          Hq; num_kv_heads must divide it
+ *  num_kv_heads         Hkv
+ *  head_dim             D, 64 or 128
+ *  page_size            P, a power of two >= 1024 / D (16 and up for both head dims)
+ *  num_workgroups       workgroups of the decode grid (0 = one per compute unit
+ *                       of the device current at the call; 1 .. 65536)
+ *  min_tiles_per_group  fewest tiles a workgroup is given; small batches use
+ *                       fewer workgroups (0 = default 8)
  */
 typedef struct pkv_desc {
   int32_t max_batch;
@@ -114,9 +119,9 @@ typedef struct pkv_desc {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t page_size;
-  int32_t max_splits;
-  int32_t target_items;
-  int32_t min_chunk_pages;
+  int32_t num_workgroups;
+  int32_t min_tiles_per_group;
+  int32_t reserved; /* must be 0 */
 } pkv_desc;
 
 /* Bytes of workspace a descriptor needs (split plan, partial outputs and
@@ -132,17 +137,18 @@ size_t pkv_workspace_bytes(const pkv_desc* desc);
  * From seq_lens (device int32 [batch]: tokens each request attends to this
  * step, the token appended this step included) it writes
  *   kv_indptr   device int32 [batch + 1], page prefix sums as defined above,
- * and the split plan into the workspace.  Plan rule, N = total pages:
- *   chunk     = max(min_chunk_pages, ceil(num_kv_heads * N / target_items))
- *   nsplit[b] = min(max_splits, ceil(pages_b / chunk))      (0 if pages_b = 0)
- *   forced_splits > 0 overrides: nsplit[b] = min(forced_splits, pages_b, max_splits)
- * and split s of request b covers pages [s*pages_b/nsplit_b, (s+1)*pages_b/nsplit_b).
+ * and the work plan into the workspace.  Plan, with U = num_q_heads / H query
+ * head groups per request (H = G for G <= 4, else 4) and T = kv_indptr[batch] * U
+ * tiles:
+ *   groups   W = min(num_workgroups, max(1, ceil(T / min_tiles_per_group))),
+ *            or min(forced_groups, num_workgroups, T) when forced_groups > 0;
+ *   group i  covers tiles [floor(i*T/W), floor((i+1)*T/W));
+ *   wave w   of a group covers the w-th of 8 equal sub-ranges of the group's range.
  * Negative seq_lens count as 0 and latch the device error word.
- * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_CAPACITY (batch > max_batch, or
- * batch * min(forced_splits, max_splits) above the workspace's chunk capacity),
- * PKV_ERR_WORKSPACE_TOO_SMALL, PKV_ERR_LAUNCH. */
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_CAPACITY
+ * (batch > max_batch), PKV_ERR_WORKSPACE_TOO_SMALL, PKV_ERR_LAUNCH. */
 int pkv_build_metadata(const pkv_desc* desc, const int32_t* seq_lens, int32_t batch,
-                       int32_t forced_splits, int32_t* kv_indptr, void* workspace,
+                       int32_t forced_groups, int32_t* kv_indptr, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 /* KV append (once per layer, after pkv_build_metadata): writes this step's
@@ -161,7 +167,7 @@ int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
                   const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
                   const int32_t* seq_lens, int32_t batch, void* stream);
 
-/* Decode attention for one layer: split kernel, then merge kernel.
+/* Decode attention for one layer (one kernel launch).
  *  q            device bf16 [batch][num_q_heads][head_dim], contiguous
  *  kv_indptr    device int32 [batch + 1] written by pkv_build_metadata this step
  *  kv_indices   device int32 [num_indices]
@@ -170,29 +176,21 @@ int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
  *  workspace    the workspace pkv_build_metadata wrote this step
  *  out          device bf16 [batch][num_q_heads][head_dim]; a request with
  *               seq_len 0 gets a zero row
- * Accumulation is fp32 (scores, online softmax, partials, merge).  For a fixed
- * plan the result is deterministic (no atomics in the arithmetic). */
+ * Accumulation is fp32 (scores, online softmax, partials, merges).  For a fixed
+ * plan the result is deterministic: partials are merged in a fixed order
+ * whichever workgroup merges them.  Calls that share a workspace must be
+ * ordered (same stream): the cross-workgroup merge uses counters in it. */
 int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
                const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
                size_t workspace_bytes, void* out, void* stream);
 
-/* The two halves of pkv_decode, for callers that time or schedule them
- * separately.  pkv_decode == pkv_decode_partials followed by pkv_decode_merge
- * on the same stream with the same arguments. */
-int pkv_decode_partials(const pkv_pool* pool, const pkv_desc* desc, const void* q,
-                        const int32_t* kv_indptr, const int32_t* kv_indices,
-                        int32_t num_indices, const int32_t* seq_lens, int32_t batch,
-                        float sm_scale, void* workspace, size_t workspace_bytes, void* out,
-                        void* stream);
-int pkv_decode_merge(const pkv_desc* desc, int32_t batch, void* workspace,
-                     size_t workspace_bytes, void* out, void* stream);
-
-/* Debug only (synchronises the stream; not capturable).  Copies the plan to
- * host arrays and checks device metadata.
- *  nsplit_out   host int32 [batch] or NULL: chunks per request
- *  chunk_out    host int32 or NULL: planned chunk length in pages
- *  items_out    host int32 or NULL: total (request, chunk) items
+/* Debug only (synchronises the stream; not capturable).  Checks device
+ * metadata and copies the plan to host memory.
+ *  groups_out   host int32 or NULL: workgroups the plan uses (W above)
+ *  waves_out    host int32 [num_workgroups * 8 * 4] or NULL: for every wave of
+ *               the grid, {request, head group, first page, tiles} of its range
+ *               (tiles = 0 for an idle wave)
  * Returns PKV_ERR_DEVICE_DATA if kv_indptr is not the page prefix sum of
  * seq_lens, any listed page id is outside [0, num_pages), kv_indptr[batch]
  * exceeds num_indices, or a kernel latched the device error word (which it
@@ -200,8 +198,7 @@ int pkv_decode_merge(const pkv_desc* desc, int32_t batch, void* workspace,
 int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int32_t* kv_indptr,
                        const int32_t* kv_indices, int32_t num_indices, int32_t num_pages,
                        int32_t batch, void* workspace, size_t workspace_bytes,
-                       int32_t* nsplit_out, int32_t* chunk_out, int32_t* items_out,
-                       void* stream);
+                       int32_t* groups_out, int32_t* waves_out, void* stream);
 
 #ifdef __cplusplus
 }

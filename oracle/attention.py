@@ -39,8 +39,9 @@ Readings taken where the pages are silent:
 kv_indptr in pages; KV head of query head hq is hq // G; seq_len includes
 the token appended this step; empty chunks have lse = -inf and weight 0; a
 request with seq_len 0 gets a zero output row; chunks are contiguous runs of
-pages split as evenly as possible; the split planner rule below is this
-library's own (the pages give only its goal: enough blocks to fill the chip).
+pages; the work plan below (equal contiguous ranges of (request, head group,
+page) tiles) is this library's own (the pages give only its goal: enough
+blocks to fill the chip).
 
 Parity status: every function here is pinned by tests that do not re-type its
 formulas (brute force, closed forms, invariants, a library special case,
@@ -65,8 +66,11 @@ __all__ = [
     "chunk_partial",
     "merge_partials",
     "even_page_ranges",
-    "plan_splits",
+    "head_groups",
+    "tile_of",
+    "plan_stream",
     "decode_split",
+    "decode_pieces",
     "append_kv",
 ]
 
@@ -176,32 +180,53 @@ def even_page_ranges(n_pages: int, nsplit: int) -> List[Tuple[int, int]]:
     return [((s * n_pages) // nsplit, ((s + 1) * n_pages) // nsplit) for s in range(nsplit)]
 
 
-def plan_splits(seq_lens, P: int, Hkv: int, max_splits: int, target_items: int,
-                min_chunk: int, forced: int = 0) -> dict:
-    """This library's split plan (not from the pages, which give only its goal).
+def head_groups(Hq: int, Hkv: int) -> Tuple[int, int]:
+    """(HG, U): query heads per head group and head groups per request.
 
-    chunk  = max(min_chunk, ceil(Hkv * N / target_items)) pages, N = total pages;
-    nsplit = min(max_splits, ceil(n_b / chunk)) for a request of n_b >= 1 pages,
-             0 for an empty request;
-    forced > 0 overrides: nsplit = min(forced, n_b, max_splits).
-    Split s of request b covers even_page_ranges(n_b, nsplit_b)[s].
+    A head group is the query heads of one KV head, at most four of them; a KV
+    head with more query heads gets several head groups.
     """
-    n = page_counts(seq_lens, P)
-    N = int(n.sum())
-    chunk = max(int(min_chunk), -(-Hkv * N // int(target_items))) if N > 0 else int(min_chunk)
-    nsplit = np.zeros(n.size, dtype=np.int64)
-    for b, nb in enumerate(n):
-        nb = int(nb)
-        if nb == 0:
-            continue
-        if forced > 0:
-            nsplit[b] = min(forced, nb, max_splits)
-        else:
-            nsplit[b] = min(max_splits, -(-nb // chunk))
-    split_indptr = np.zeros(n.size + 1, dtype=np.int64)
-    split_indptr[1:] = np.cumsum(nsplit)
-    return {"chunk": chunk, "total_pages": N, "nsplit": nsplit,
-            "split_indptr": split_indptr, "num_items": int(split_indptr[-1])}
+    G = Hq // Hkv
+    HG = G if G <= 4 else 4
+    return HG, Hq // HG
+
+
+def tile_of(indptr, units: int, t: int) -> Tuple[int, int, int]:
+    """(request, head group, page) of tile t in the order request, head group, page."""
+    starts = np.asarray(indptr, dtype=np.int64) * units
+    b = int(np.searchsorted(starts, t, side="right")) - 1
+    n = int(indptr[b + 1] - indptr[b])
+    r = t - int(starts[b])
+    return b, r // n, r % n
+
+
+def plan_stream(seq_lens, P: int, units: int, groups: int, min_tiles: int,
+                forced: int = 0, waves_per_group: int = 8) -> dict:
+    """This library's work plan (not from the pages, which give only its goal).
+
+    T = pages * units tiles; W = min(groups, ceil(T / min_tiles)) workgroups
+    (min(forced, groups, T) if forced > 0, 0 if T = 0); workgroup i covers tiles
+    [floor(i*T/W), floor((i+1)*T/W)) and its wave w the w-th of waves_per_group
+    equal parts of that range.  Returns W and, for every wave of the grid,
+    (request, head group, first page, tiles), zeros for an idle wave.
+    """
+    ip = kv_indptr(seq_lens, P)
+    T = int(ip[-1]) * units
+    if T == 0:
+        W = 0
+    elif forced > 0:
+        W = min(forced, groups, T)
+    else:
+        W = min(groups, -(-T // min_tiles))
+    waves = np.zeros((groups * waves_per_group, 4), dtype=np.int64)
+    for i in range(W):
+        g0, g1 = i * T // W, (i + 1) * T // W
+        for w in range(waves_per_group):
+            t0 = g0 + w * (g1 - g0) // waves_per_group
+            t1 = g0 + (w + 1) * (g1 - g0) // waves_per_group
+            if t1 > t0:
+                waves[i * waves_per_group + w] = (*tile_of(ip, units, t0), t1 - t0)
+    return {"kv_indptr": ip, "tiles": T, "groups": W, "waves": waves}
 
 
 def decode_split(q_bits, k_pool, v_pool, indptr, indices, seq_lens, sm_scale: float,
@@ -247,3 +272,38 @@ def append_kv(k_pool, v_pool, k_new, v_new, indptr, indices, seq_lens, P: int):
         k[page, :, pos % P, :] = k_new[b]
         v[page, :, pos % P, :] = v_new[b]
     return k, v
+
+
+def decode_pieces(q_bits, k_pool, v_pool, indptr, indices, seq_lens, sm_scale: float, P: int,
+                  pieces) -> np.ndarray:
+    """Split-then-merge decode over arbitrary pieces.
+
+    pieces: iterable of (request b, head group u, first page p0, pages n) with
+    the head groups of head_groups(); each (b, u) must be covered exactly once.
+    Every piece yields a partial per query head of its group; each (b, u) merges
+    its partials in the order given.
+    """
+    q = bf16_to_f64(q_bits)
+    B, Hq, D = q.shape
+    Hkv = np.asarray(k_pool).shape[1]
+    G = Hq // Hkv
+    HG, _ = head_groups(Hq, Hkv)
+    parts = {}
+    dense = {}
+    for b, u, p0, n in pieces:
+        b, u, p0, n = int(b), int(u), int(p0), int(n)
+        L = int(seq_lens[b])
+        if b not in dense:
+            dense[b] = (gather_request(k_pool, indptr, indices, b, L, P),
+                        gather_request(v_pool, indptr, indices, b, L, P))
+        Kd, Vd = dense[b]
+        t0, t1 = p0 * P, min(L, (p0 + n) * P)
+        for hq in range(u * HG, (u + 1) * HG):
+            h = kv_head_of(hq, G)
+            parts.setdefault((b, hq), []).append(
+                chunk_partial(q[b, hq], Kd[t0:t1, h, :], Vd[t0:t1, h, :], sm_scale))
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for (b, hq), pl in parts.items():
+        out[b, hq] = merge_partials(pl)
+    return out
+

@@ -34,9 +34,8 @@ __all__ = [
     "pkv_build_metadata",
     "pkv_append_kv",
     "pkv_decode",
-    "pkv_decode_partials",
-    "pkv_decode_merge",
     "pkv_debug_validate",
+    "WAVES_PER_GROUP",
     "PKV_OK",
     "PKV_ERR_INVALID_ARG",
     "PKV_ERR_UNSUPPORTED",
@@ -53,6 +52,7 @@ PKV_ERR_WORKSPACE_TOO_SMALL = 3
 PKV_ERR_CAPACITY = 4
 PKV_ERR_LAUNCH = 5
 PKV_ERR_DEVICE_DATA = 6
+WAVES_PER_GROUP = 8  # waves per decode workgroup (fixed by the kernels)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "pkv.h")
@@ -77,8 +77,8 @@ class _CPool(ctypes.Structure):
 class _CDesc(ctypes.Structure):
     _fields_ = [("max_batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("max_splits", ctypes.c_int32),
-                ("target_items", ctypes.c_int32), ("min_chunk_pages", ctypes.c_int32)]
+                ("page_size", ctypes.c_int32), ("num_workgroups", ctypes.c_int32),
+                ("min_tiles_per_group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -95,13 +95,8 @@ _SIGNATURES = {
     "pkv_decode": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp, _vp,
                                   _i32, _vp, _i32, ctypes.c_float, _vp, ctypes.c_size_t, _vp,
                                   _vp]),
-    "pkv_decode_partials": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp,
-                                           _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
-                                           ctypes.c_size_t, _vp, _vp]),
-    "pkv_decode_merge": (ctypes.c_int, [ctypes.POINTER(_CDesc), _i32, _vp, ctypes.c_size_t, _vp,
-                                        _vp]),
     "pkv_debug_validate": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _vp, _vp, _i32, _i32, _i32,
-                                          _vp, ctypes.c_size_t, _i32p, _i32p, _i32p, _vp]),
+                                          _vp, ctypes.c_size_t, _i32p, _i32p, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -173,13 +168,18 @@ class Desc:
     num_kv_heads: int
     head_dim: int
     page_size: int
-    max_splits: int = 256
-    target_items: int = 0
-    min_chunk_pages: int = 0
+    num_workgroups: int = 0
+    min_tiles_per_group: int = 0
 
     def c(self) -> _CDesc:
         return _CDesc(self.max_batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
-                      self.page_size, self.max_splits, self.target_items, self.min_chunk_pages)
+                      self.page_size, self.num_workgroups, self.min_tiles_per_group, 0)
+
+    def groups(self) -> int:
+        """Decode grid size: num_workgroups, or the current device's compute units."""
+        if self.num_workgroups > 0:
+            return self.num_workgroups
+        return torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
 
 
 @dataclass
@@ -211,11 +211,11 @@ def pkv_workspace_bytes(desc: Desc) -> int:
     return int(n)
 
 
-def pkv_build_metadata(desc: Desc, seq_lens: torch.Tensor, forced_splits: int,
+def pkv_build_metadata(desc: Desc, seq_lens: torch.Tensor, forced_groups: int,
                        kv_indptr: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
     B = seq_lens.numel()
     st = load_library().pkv_build_metadata(
-        ctypes.byref(desc.c()), _ptr(seq_lens, "seq_lens", _I32), B, int(forced_splits),
+        ctypes.byref(desc.c()), _ptr(seq_lens, "seq_lens", _I32), B, int(forced_groups),
         _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check("pkv_build_metadata", st)
@@ -233,55 +233,39 @@ def pkv_append_kv(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor, kv_indpt
     _check("pkv_append_kv", st)
 
 
-def _decode_args(pool, desc, q, kv_indptr, kv_indices, seq_lens, sm_scale, workspace, out, stream):
-    B = seq_lens.numel()
-    n = B * desc.num_q_heads * desc.head_dim
-    return (ctypes.byref(pool.c()), ctypes.byref(desc.c()), _ptr(q, "q", _BF16, n),
-            _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
-            kv_indices.numel(), _ptr(seq_lens, "seq_lens", _I32), B, float(sm_scale),
-            _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-            _ptr(out, "out", _BF16, n), _stream(stream))
-
-
 def pkv_decode(pool: Pool, desc: Desc, q: torch.Tensor, kv_indptr: torch.Tensor,
                kv_indices: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float,
                workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
-    st = load_library().pkv_decode(*_decode_args(pool, desc, q, kv_indptr, kv_indices, seq_lens,
-                                                 sm_scale, workspace, out, stream))
+    B = seq_lens.numel()
+    n = B * desc.num_q_heads * desc.head_dim
+    st = load_library().pkv_decode(
+        ctypes.byref(pool.c()), ctypes.byref(desc.c()), _ptr(q, "q", _BF16, n),
+        _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
+        kv_indices.numel(), _ptr(seq_lens, "seq_lens", _I32), B, float(sm_scale),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, "out", _BF16, n), _stream(stream))
     _check("pkv_decode", st)
-
-
-def pkv_decode_partials(pool: Pool, desc: Desc, q: torch.Tensor, kv_indptr: torch.Tensor,
-                        kv_indices: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float,
-                        workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
-    st = load_library().pkv_decode_partials(*_decode_args(pool, desc, q, kv_indptr, kv_indices,
-                                                          seq_lens, sm_scale, workspace, out,
-                                                          stream))
-    _check("pkv_decode_partials", st)
-
-
-def pkv_decode_merge(desc: Desc, batch: int, workspace: torch.Tensor, out: torch.Tensor,
-                     stream=None) -> None:
-    st = load_library().pkv_decode_merge(
-        ctypes.byref(desc.c()), int(batch), _ptr(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), _ptr(out, "out", _BF16), _stream(stream))
-    _check("pkv_decode_merge", st)
 
 
 def pkv_debug_validate(desc: Desc, seq_lens: torch.Tensor, kv_indptr: torch.Tensor,
                        kv_indices: torch.Tensor, num_pages: int, workspace: torch.Tensor,
                        stream=None) -> dict:
-    """Synchronising check of device metadata; returns the status and the plan."""
+    """Synchronising check of device metadata; returns the status and the plan.
+
+    ``waves`` lists {request, head group, first page, tiles} for every wave of
+    the decode grid, ``groups`` the workgroups the plan uses.
+    """
     B = seq_lens.numel()
-    nsplit = (ctypes.c_int32 * max(B, 1))()
-    chunk = ctypes.c_int32(0)
-    items = ctypes.c_int32(0)
+    nw = desc.groups() * WAVES_PER_GROUP
+    waves = (ctypes.c_int32 * (4 * nw))()
+    groups = ctypes.c_int32(0)
     st = load_library().pkv_debug_validate(
         ctypes.byref(desc.c()), _ptr(seq_lens, "seq_lens", _I32),
         _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
         kv_indices.numel(), int(num_pages), B, _ptr(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), nsplit, ctypes.byref(chunk),
-        ctypes.byref(items), _stream(stream))
+        workspace.numel() * workspace.element_size(), ctypes.byref(groups), waves,
+        _stream(stream))
     if st not in (PKV_OK, PKV_ERR_DEVICE_DATA):
         _check("pkv_debug_validate", st)
-    return {"status": st, "nsplit": list(nsplit)[:B], "chunk": chunk.value, "items": items.value}
+    w = [tuple(waves[4 * i: 4 * i + 4]) for i in range(nw)]
+    return {"status": st, "groups": groups.value, "waves": w}

@@ -1,16 +1,21 @@
-// Split-KV paged decode attention for gfx950 (MI355X): split kernel + merge kernel.
+// Paged split-KV decode attention for gfx950 (MI355X), one kernel per call.
 //
-// Work decomposition.  The step's plan lists (request, chunk) items; every item
-// is expanded into Hq / HG workgroups, one per group of HG query heads sharing
-// a KV head (HG = G for G <= 4).  A workgroup has four waves.  Wave w of a
-// workgroup walks pages p0 + w, p0 + w + 4, ... of the chunk, so the four waves
-// stream four different pages at a time, then combine their online-softmax
-// states through LDS and write one partial (or, for a one-chunk request, the
-// final bf16 row).  The split partials and a separate combine kernel follow the
-// pages' decode design (commits by ViperEkura: o_part / ml_part partials, one
-// combine kernel); staging is different: K and V go straight from HBM into
-// registers with 16-byte loads, since every K/V element is used by exactly one
-// lane and LDS staging would only add traffic.
+// Work decomposition (stream-K style).  The step's tiles, ordered (request,
+// head group, page), are cut into equal contiguous ranges: one per workgroup of
+// eight waves, one eighth of that per wave.  A head group is HG query heads
+// that share one KV head (HG = G for G <= 4), so a tile is one page of one KV
+// head, K and V, read once for HG query heads.  Each wave streams its range,
+// keeping an online-softmax state that it closes whenever the range leaves a
+// (request, head group) segment.  A segment wholly inside a wave is written
+// straight to the output; other pieces go to LDS, where the workgroup merges
+// the pieces of each segment; a segment that also spans other workgroups leaves
+// a normalised partial and its log-sum-exp in the workspace, and the last
+// workgroup to arrive merges them in a fixed order.  Split partials merged by
+// log-sum-exp follow the pages' decode design (commits by ViperEkura: o_part /
+// ml_part partials and their combine kernel); here the merge is fused into the
+// same launch and every wave gets the same number of pages.  K and V go
+// straight from HBM into registers with 16-byte loads: every element is used by
+// exactly one lane, so LDS staging would only add traffic.
 //
 // Lane layout inside a wave (head_dim D, LPT = D / 16 lanes per token,
 // TPR = 64 / LPT tokens per round).  Lane l serves token slot l / LPT of a round
@@ -20,7 +25,7 @@
 // (D=64) contiguous bytes.  q.K partial dot products use v_dot2 on bf16 pairs,
 // then DPP adds inside the LPT-lane group.  Every lane keeps its own online
 // softmax state (running max m, sum l, 16-channel accumulators per head) for
-// the tokens of its slot; slots are merged once, at the end of the chunk.
+// the tokens of its slot; slots are merged once per piece.
 //
 // The running max is updated lazily: the accumulators are rescaled only when
 // a score exceeds the stored max by more than 2^8 in the exp2 domain, so
@@ -34,8 +39,6 @@
 namespace pkv {
 namespace {
 
-constexpr int kWavesPerGroup = 4;
-constexpr int kGroupThreads = kWavesPerGroup * kWave;
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest un-rescaled weight
 constexpr float kMinusInf = -INFINITY;
 constexpr float kFloorMax = -1.0e30f;  // initial running max (finite: exp2 never sees inf - inf)
@@ -62,6 +65,19 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
+
+// Stores and loads coherent across the XCDs' L2 caches (agent scope), used for
+// the partials one workgroup hands to another.  They compile to sc1 accesses:
+// no L2 write-back or invalidate is needed around them.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every earlier store of the wave has been acknowledged (for the
+// sc1 stores above: is visible at agent scope).  s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // DPP lane moves inside a row of 16 lanes.
 enum DppCtrl : int {
@@ -100,7 +116,7 @@ struct Round {
   uint4 k0, k1, v0, v1;
 };
 
-template <int D, int HG, int RS>
+template <int D, int HG>
 struct SplitWave {
   static constexpr int LPT = D / 16;
   static constexpr int TPR = kWave / LPT;
@@ -119,8 +135,7 @@ struct SplitWave {
   }
 
   // One round: TPR tokens, lane slot `tok`; `live` = this lane's token counts.
-  __device__ __forceinline__ void consume(const Round& rd, bool live, bool any_dead,
-                                          float scale_log2) {
+  __device__ __forceinline__ void consume(const Round& rd, bool live, float scale_log2) {
     float s[HG];
 #pragma unroll
     for (int h = 0; h < HG; ++h) {
@@ -136,15 +151,12 @@ struct SplitWave {
       d = token_group_sum<LPT>(d);
       s[h] = live ? d * scale_log2 : kMinusInf;
     }
+    // Slots past the sequence end (or in a skipped page) may hold anything,
+    // NaN included: zero them so a zero weight really contributes zero.
+    const uint32_t keep = live ? 0xffffffffu : 0u;
     uint4 v0 = rd.v0, v1 = rd.v1;
-    if (any_dead) {
-      // Slots past the sequence end (or in a skipped page) may hold anything,
-      // NaN included: zero them so a zero weight really contributes zero.
-      if (!live) {
-        v0 = make_uint4(0, 0, 0, 0);
-        v1 = make_uint4(0, 0, 0, 0);
-      }
-    }
+    v0.x &= keep; v0.y &= keep; v0.z &= keep; v0.w &= keep;
+    v1.x &= keep; v1.y &= keep; v1.z &= keep; v1.w &= keep;
     bool grow = false;
 #pragma unroll
     for (int h = 0; h < HG; ++h) grow |= s[h] > m[h] + kRescaleSlack;
@@ -201,262 +213,300 @@ struct SplitWave {
   }
 };
 
+
+// Online-softmax combine of (m, l, value) triples in the log2 domain.
+struct Combine {
+  float m = kFloorMax, den = 0.f, num = 0.f;
+  __device__ __forceinline__ void add(float mk, float lk, float vk) {
+    const float mn = fmaxf(m, mk);
+    const float ca = fast_exp2(m - mn);
+    const float cb = fast_exp2(mk - mn);
+    den = den * ca + lk * cb;
+    num = num * ca + vk * cb;
+    m = mn;
+  }
+};
+
 template <int D, int HG>
-__global__ void __launch_bounds__(kGroupThreads) split_kernel(DecodeArgs a) {
-  constexpr int RS = 2;  // rounds per pipeline stage
-  using W = SplitWave<D, HG, RS>;
+__global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
+  using W = SplitWave<D, HG>;
   constexpr int LPT = W::LPT;
   constexpr int TPR = W::TPR;
+  static_assert(HG * D <= kGroupThreads, "one output channel per thread");
 
-  __shared__ float s_acc[kWavesPerGroup][HG][D];
-  __shared__ float s_m[kWavesPerGroup][HG];
-  __shared__ float s_l[kWavesPerGroup][HG];
+  // Pieces that leave a wave unfinished: slot 0 = the wave's first piece,
+  // slot 1 = its last piece (every other piece is a whole segment).
+  __shared__ float s_acc[kWavesPerGroup][2][HG][D];
+  __shared__ float s_m[kWavesPerGroup][2][HG];
+  __shared__ float s_l[kWavesPerGroup][2][HG];
+  __shared__ int s_seg[kWavesPerGroup][2];
+  __shared__ int s_glob[2];   // segments this workgroup left as global partials
+  __shared__ int s_merge[2];  // of those, the ones this workgroup merges
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int units = a.num_q_heads / HG;
-  const int item = blockIdx.x / units;
-  if (item >= a.hdr[kHdrNumItems]) return;  // uniform over the workgroup
-  const int hq0 = (blockIdx.x - item * units) * HG;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int grp = blockIdx.x;
+  const int U = a.units;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int g = hq0 / G;
-  const int2 bs = a.items[item];
-  const int b = bs.x, s = bs.y;
-  const int ns = a.split_indptr[b + 1] - a.split_indptr[b];
-  const int ip0 = a.kv_indptr[b];
-  const int npages = a.kv_indptr[b + 1] - ip0;
-  const int L = a.seq_lens[b];
-  const int P = a.page_size;
-  const int p0 = (int)(((long long)s * npages) / ns);
-  const int p1 = (int)(((long long)(s + 1) * npages) / ns);
-  const int log2_r = a.log2_rounds;  // rounds per page = P / TPR, a power of two
+  const int Hq = a.num_q_heads;
+
+  if (grp == 0) {
+    // Requests without tokens get zero rows (no tile covers them).
+    for (int b = tid; b < a.batch; b += kGroupThreads) {
+      if (a.kv_indptr[b + 1] == a.kv_indptr[b]) {
+        uint4* row = reinterpret_cast<uint4*>(a.out + (size_t)b * Hq * D);
+        for (int i = 0; i < Hq * D / 8; ++i) row[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  if (grp >= a.hdr[kHdrGroups]) return;  // uniform over the workgroup
+  if (lane == 0) {
+    s_seg[w][0] = -1;
+    s_seg[w][1] = -1;
+  }
+  if (tid < 2) s_glob[tid] = -1;
+
+  const WaveRange rng = a.waves[grp * kWavesPerGroup + w];
   const int tok = lane / LPT;
   const int e = lane % LPT;
   const int c0 = e * 8;  // first channel of the lane's low half; high half at D/2 + c0
-
-  W st;
-  st.init();
-#pragma unroll
-  for (int h = 0; h < HG; ++h) {
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        a.q + ((size_t)b * a.num_q_heads + hq0 + h) * D + c0);
-    const uint4 lo = qp[0];
-    const uint4 hi = qp[D / 16];
-    st.qw[h][0] = lo.x; st.qw[h][1] = lo.y; st.qw[h][2] = lo.z; st.qw[h][3] = lo.w;
-    st.qw[h][4] = hi.x; st.qw[h][5] = hi.y; st.qw[h][6] = hi.z; st.qw[h][7] = hi.w;
-  }
-
-  // This wave's pages: p0 + w, p0 + w + 4, ...
-  const int mine = p1 - p0 > w ? (p1 - p0 - w + kWavesPerGroup - 1) / kWavesPerGroup : 0;
-  const int nrounds = mine << log2_r;
-  const size_t head_stride = (size_t)P * D;  // elements per (page, head) tile
-  const int lane_off = tok * D + c0;         // element offset of the lane inside a round
-
+  const size_t tile = (size_t)a.page_size * D;               // elements per (page, head) tile
+  const uint32_t lane_boff = (uint32_t)(tok * D + c0) * 2;  // lane's byte offset inside a round
+  const char* kbase = reinterpret_cast<const char*>(a.k);
+  const char* vbase = reinterpret_cast<const char*>(a.v);
+  const int P = a.page_size;
+  const int log2_r = a.log2_rounds;
   int err = 0;
-  // Issue the loads of round rr.  Returns the round's first token (request
-  // coordinates) and whether its page is usable.
-  auto issue = [&](int rr, Round& rd, int& t0, bool& ok) {
-    const int j = rr >> log2_r;
-    const int r = rr & ((1 << log2_r) - 1);
-    const int lp = p0 + w + j * kWavesPerGroup;  // logical page
-    t0 = lp * P + r * TPR;
-    ok = false;
-    rd.k0 = rd.k1 = rd.v0 = rd.v1 = make_uint4(0, 0, 0, 0);
-    if (t0 >= L) return;
-    const int pos = ip0 + lp;
-    if (pos < 0 || pos >= a.num_indices) {
-      err |= kErrBadIndexPos;
-      return;
-    }
-    const int page = a.kv_indices[pos];
-    if (page < 0 || page >= a.num_pages) {
-      err |= kErrBadPageId;
-      return;
-    }
-    ok = true;
-    const size_t base = ((size_t)page * a.num_kv_heads + g) * head_stride + (size_t)r * TPR * D;
-    const uint4* kp = reinterpret_cast<const uint4*>(a.k + base + lane_off);
-    const uint4* vp = reinterpret_cast<const uint4*>(a.v + base + lane_off);
-    rd.k0 = kp[0];
-    rd.k1 = kp[D / 16];
-    rd.v0 = vp[0];
-    rd.v1 = vp[D / 16];
-  };
-  auto consume = [&](const Round& rd, int t0, bool ok) {
-    const bool live = ok && (t0 + tok < L);
-    const bool any_dead = !ok || (t0 + TPR > L);
-    st.consume(rd, live, any_dead, a.scale_log2);
-  };
 
-  // Two-stage software pipeline of RS rounds per stage.
-  Round A[RS], B[RS];
-  int tA[RS], tB[RS];
-  bool okA[RS], okB[RS];
-  const int nstages = (nrounds + RS - 1) / RS;
-  if (nstages > 0) {
+  int b = rng.b, u = rng.u, p = rng.p, left = rng.count, piece = 0;
+  W st;
+  while (left > 0) {  // one piece = the part of segment (b, u) inside this wave's range
+    const int ip0 = a.kv_indptr[b];
+    const int n = a.kv_indptr[b + 1] - ip0;
+    const int L = a.seq_lens[b];
+    const int len = min(left, n - p);
+    if (len <= 0) break;  // only reachable with metadata that does not match kv_indptr
+    const int hq0 = u * HG;
+    const int g = hq0 / G;
+
+    st.init();
 #pragma unroll
-    for (int i = 0; i < RS; ++i) {
-      if (i < nrounds) issue(i, A[i], tA[i], okA[i]);
-      else { okA[i] = false; tA[i] = L; }
+    for (int h = 0; h < HG; ++h) {
+      const uint4* qp = reinterpret_cast<const uint4*>(
+          a.q + ((size_t)b * Hq + hq0 + h) * D + c0);
+      const uint4 lo = qp[0];
+      const uint4 hi = qp[D / 16];
+      st.qw[h][0] = lo.x; st.qw[h][1] = lo.y; st.qw[h][2] = lo.z; st.qw[h][3] = lo.w;
+      st.qw[h][4] = hi.x; st.qw[h][5] = hi.y; st.qw[h][6] = hi.z; st.qw[h][7] = hi.w;
     }
-  }
-  for (int sg = 0; sg < nstages; sg += 2) {
-    if (sg + 1 < nstages) {
-#pragma unroll
-      for (int i = 0; i < RS; ++i) {
-        const int rr = (sg + 1) * RS + i;
-        if (rr < nrounds) issue(rr, B[i], tB[i], okB[i]);
-        else { okB[i] = false; tB[i] = L; }
+    const size_t head_off = (size_t)g * tile;
+
+    for (int jb = 0; jb < len; jb += kWave) {
+      const int nb = min(kWave, len - jb);
+      // One vector load fetches the page ids of the next (up to) 64 pages: lane i
+      // holds the id of page p + jb + i, or -1 if it is unusable.
+      int vpage = -1;
+      {
+        const int pos = ip0 + p + jb + lane;
+        const bool pos_ok = pos >= 0 && pos < a.num_indices;
+        const int pid = a.kv_indices[pos_ok ? pos : 0];
+        if (lane < nb) {
+          if (!pos_ok) err |= kErrBadIndexPos;
+          else if (pid < 0 || pid >= a.num_pages) err |= kErrBadPageId;
+          else vpage = pid;
+        }
+      }
+      const int nr = nb << log2_r;  // rounds in this block, >= 1
+
+      // Round rr of the block: page id (uniform), first token, loads.  Rounds
+      // past the block re-read its last round (a cache hit) and are never
+      // consumed, so the issue sequence has no data-dependent branch.
+      auto issue = [&](int rr, Round& rd) {
+        const int rc = rr < nr ? rr : nr - 1;
+        const int j = rc >> log2_r;
+        const int r = rc & ((1 << log2_r) - 1);
+        const int pid = __builtin_amdgcn_readlane(vpage, j);
+        const size_t off = ((size_t)(pid < 0 ? 0 : pid) * a.num_kv_heads * tile + head_off +
+                            (size_t)r * TPR * D) * 2;
+        const char* kp = kbase + off + lane_boff;
+        const char* vp = vbase + off + lane_boff;
+        rd.k0 = *reinterpret_cast<const uint4*>(kp);
+        rd.k1 = *reinterpret_cast<const uint4*>(kp + D);
+        rd.v0 = *reinterpret_cast<const uint4*>(vp);
+        rd.v1 = *reinterpret_cast<const uint4*>(vp + D);
+      };
+      auto consume = [&](int rr, const Round& rd) {
+        const int j = rr >> log2_r;
+        const int r = rr & ((1 << log2_r) - 1);
+        const int pid = __builtin_amdgcn_readlane(vpage, j);
+        const int t0 = (p + jb + j) * P + r * TPR;
+        const bool live = pid >= 0 && t0 + tok < L;
+        st.consume(rd, live, a.scale_log2);
+      };
+
+      // Two stages of two rounds each: while one stage is consumed the other
+      // is in flight.
+      Round A0, A1, B0, B1;
+      issue(0, A0);
+      issue(1, A1);
+      for (int rr = 0; rr < nr; rr += 4) {
+        issue(rr + 2, B0);
+        issue(rr + 3, B1);
+        consume(rr, A0);
+        if (rr + 1 < nr) consume(rr + 1, A1);
+        issue(rr + 4, A0);
+        issue(rr + 5, A1);
+        if (rr + 2 < nr) consume(rr + 2, B0);
+        if (rr + 3 < nr) consume(rr + 3, B1);
       }
     }
+
+    st.merge_slots();
+    const int seg = b * U + u;
+    if (p == 0 && len == n) {
+      // The whole segment lies in this wave: write its rows.  Lane slot h < HG
+      // writes head h (after the merge every slot holds the totals).
+      float o[16];
+      float lv = st.l[0];
 #pragma unroll
-    for (int i = 0; i < RS; ++i)
-      if (tA[i] < L) consume(A[i], tA[i], okA[i]);
-    if (sg + 2 < nstages) {
+      for (int j = 0; j < 16; ++j) o[j] = st.acc[0][j];
 #pragma unroll
-      for (int i = 0; i < RS; ++i) {
-        const int rr = (sg + 2) * RS + i;
-        if (rr < nrounds) issue(rr, A[i], tA[i], okA[i]);
-        else { okA[i] = false; tA[i] = L; }
+      for (int h = 1; h < HG; ++h) {
+        if (tok == h) {
+          lv = st.l[h];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[j] = st.acc[h][j];
+        }
+      }
+      if (tok < HG) {
+        const float inv = lv > 0.f ? 1.0f / lv : 0.f;
+        uint16_t* op = a.out + ((size_t)b * Hq + hq0 + tok) * D + c0;
+        *reinterpret_cast<uint4*>(op) =
+            make_uint4(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                       pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv));
+        *reinterpret_cast<uint4*>(op + D / 2) =
+            make_uint4(pack_bf16x2(o[8] * inv, o[9] * inv), pack_bf16x2(o[10] * inv, o[11] * inv),
+                       pack_bf16x2(o[12] * inv, o[13] * inv),
+                       pack_bf16x2(o[14] * inv, o[15] * inv));
+      }
+    } else {
+      const int slot = piece == 0 ? 0 : 1;
+      if (tok == 0) {
+#pragma unroll
+        for (int h = 0; h < HG; ++h) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            s_acc[w][slot][h][c0 + j] = st.acc[h][j];
+            s_acc[w][slot][h][D / 2 + c0 + j] = st.acc[h][8 + j];
+          }
+          if (e == 0) {
+            s_m[w][slot][h] = st.m[h];
+            s_l[w][slot][h] = st.l[h];
+          }
+        }
+        if (e == 0) s_seg[w][slot] = seg;
       }
     }
-    if (sg + 1 < nstages) {
-#pragma unroll
-      for (int i = 0; i < RS; ++i)
-        if (tB[i] < L) consume(B[i], tB[i], okB[i]);
+    left -= len;
+    ++piece;
+    if (left > 0) {
+      p = 0;
+      if (++u == U) {
+        u = 0;
+        do { ++b; } while (b < a.batch - 1 && a.kv_indptr[b + 1] == a.kv_indptr[b]);
+      }
     }
   }
   if (err) atomicOr(&a.hdr[kHdrError], err);
-
-  st.merge_slots();
-
-  // Hand the wave's state to LDS: slot 0 lanes hold channels [8e, 8e+8) and
-  // [D/2 + 8e, D/2 + 8e + 8) of every head.
-  if (tok == 0) {
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        s_acc[w][h][c0 + j] = st.acc[h][j];
-        s_acc[w][h][D / 2 + c0 + j] = st.acc[h][8 + j];
-      }
-      if (e == 0) {
-        s_m[w][h] = st.m[h];
-        s_l[w][h] = st.l[h];
-      }
-    }
-  }
   __syncthreads();
 
-  // Combine the four waves and write: two channels per thread.
-  const bool direct = ns == 1;
-  for (int idx = threadIdx.x * 2; idx < HG * D; idx += kGroupThreads * 2) {
-    const int h = idx / D;
-    const int c = idx - h * D;
-    float M = s_m[0][h];
-#pragma unroll
-    for (int v = 1; v < kWavesPerGroup; ++v) M = fmaxf(M, s_m[v][h]);
-    float den = 0.f, n0 = 0.f, n1 = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWavesPerGroup; ++v) {
-      const float wt = fast_exp2(s_m[v][h] - M);
-      den = fmaf(wt, s_l[v][h], den);
-      n0 = fmaf(wt, s_acc[v][h][c], n0);
-      n1 = fmaf(wt, s_acc[v][h][c + 1], n1);
-    }
-    const float inv = den > 0.f ? 1.0f / den : 0.f;
-    const int hq = hq0 + h;
-    if (direct) {
-      uint32_t* op = reinterpret_cast<uint32_t*>(a.out + ((size_t)b * a.num_q_heads + hq) * D + c);
-      *op = pack_bf16x2(n0 * inv, n1 * inv);
+  // Merge the pieces in LDS segment by segment (a segment's pieces are
+  // consecutive in wave order).  Thread t owns channel t % D of head t / D.
+  const int2 gsegs = a.group_segs[grp];
+  const bool act = tid < HG * D;
+  const int h = tid / D;
+  const int c = tid - h * D;
+  auto emit = [&](int sgm, const Combine& cb) {
+    const int eb = sgm / U;
+    const int hq = (sgm - eb * U) * HG + h;
+    const int2 sg = a.seg_groups[sgm];
+    const float val = cb.den > 0.f ? cb.num / cb.den : 0.f;
+    if (sg.x == grp && sg.y == grp) {
+      if (act) a.out[((size_t)eb * Hq + hq) * D + c] = (uint16_t)bf16_rne(val);
     } else {
-      float2* op = reinterpret_cast<float2*>(a.opart + ((size_t)item * a.num_q_heads + hq) * D + c);
-      *op = make_float2(n0 * inv, n1 * inv);
-      if (c == 0) a.lse[(size_t)item * a.num_q_heads + hq] = den > 0.f ? M + fast_log2(den) : kMinusInf;
+      const int slot = sgm == gsegs.x ? 0 : 1;
+      const size_t row = (size_t)(2 * grp + slot) * HG + h;
+      if (act) {
+        store_coherent(&a.opart[row * D + c], val);
+        if (c == 0) store_coherent(&a.lse[row], cb.den > 0.f ? cb.m + fast_log2(cb.den) : kMinusInf);
+      }
+      if (tid == 0) s_glob[slot] = sgm;
     }
+  };
+  {
+    int cur = -1;
+    Combine cb;
+#pragma unroll 1
+    for (int k = 0; k < 2 * kWavesPerGroup; ++k) {
+      const int sgm = s_seg[k >> 1][k & 1];
+      if (sgm < 0) continue;
+      if (sgm != cur) {
+        if (cur >= 0) emit(cur, cb);
+        cur = sgm;
+        cb = Combine();
+      }
+      if (act) cb.add(s_m[k >> 1][k & 1][h], s_l[k >> 1][k & 1][h], s_acc[k >> 1][k & 1][h][c]);
+    }
+    if (cur >= 0) emit(cur, cb);
   }
-}
 
-// Merge: one workgroup per (request, query head).  Waves take every fourth
-// chunk, each thread two channels (D = 128) or one (D = 64); the four waves'
-// sums are combined through LDS.
-template <int D>
-__global__ void __launch_bounds__(kGroupThreads) merge_kernel(DecodeArgs a) {
-  constexpr int CPT = D / kWave;  // channels per thread
-  __shared__ float s_num[kWavesPerGroup][D];
-  __shared__ float s_den[kWavesPerGroup];
-  __shared__ float s_max[kWavesPerGroup];
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int b = blockIdx.x / a.num_q_heads;
-  const int hq = blockIdx.x - b * a.num_q_heads;
-  if (b >= a.batch) return;
-  const int base = a.split_indptr[b];
-  int ns = a.split_indptr[b + 1] - base;
-  if (ns == 1) return;  // written by the split kernel
-  const int nitems = min(a.hdr[kHdrNumItems], a.max_items);
-  if (base + ns > nitems) ns = nitems > base ? nitems - base : 0;
-
-  const size_t hstride = (size_t)a.num_q_heads;
-  float M = kMinusInf;
-  for (int sp = threadIdx.x; sp < ns; sp += kGroupThreads)
-    M = fmaxf(M, a.lse[(base + sp) * hstride + hq]);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
-  if (lane == 0) s_max[w] = M;
+  // Cross-workgroup merge: publish the partials, count arrivals, and let the
+  // last workgroup of each segment combine every workgroup's partial in order.
+  wait_stores();
   __syncthreads();
-  M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-
-  float num[CPT];
+  if (tid == 0) {
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) num[i] = 0.f;
-  float den = 0.f;
-  if (M > kMinusInf) {
-#pragma unroll 4
-    for (int sp = w; sp < ns; sp += kWavesPerGroup) {
-      const size_t row = (base + sp) * hstride + hq;
-      const float wt = fast_exp2(a.lse[row] - M);
-      den += wt;
-      const float* op = a.opart + row * D + lane * CPT;
-      if constexpr (CPT == 2) {
-        const float2 o = *reinterpret_cast<const float2*>(op);
-        num[0] = fmaf(wt, o.x, num[0]);
-        num[1] = fmaf(wt, o.y, num[1]);
-      } else {
-        num[0] = fmaf(wt, op[0], num[0]);
+    for (int k = 0; k < 2; ++k) {
+      const int sgm = s_glob[k];
+      s_merge[k] = -1;
+      if (sgm >= 0 && !(k == 1 && sgm == s_glob[0])) {
+        const int2 sg = a.seg_groups[sgm];
+        const int old = __hip_atomic_fetch_add(&a.counters[sgm], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        if (old == sg.y - sg.x) s_merge[k] = sgm;
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) s_num[w][lane * CPT + i] = num[i];
-  if (lane == 0) s_den[w] = den;
   __syncthreads();
-  if (w == 0) {
-    const float dt = s_den[0] + s_den[1] + s_den[2] + s_den[3];
-    const float inv = dt > 0.f ? 1.0f / dt : 0.f;
-    float r[CPT];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = lane * CPT + i;
-      r[i] = (s_num[0][c] + s_num[1][c] + s_num[2][c] + s_num[3][c]) * inv;
+#pragma unroll 1
+  for (int k = 0; k < 2; ++k) {
+    const int sgm = s_merge[k];
+    if (sgm < 0) continue;
+    const int2 sg = a.seg_groups[sgm];
+    Combine cb;
+    for (int j = sg.x; j <= sg.y; ++j) {
+      const int slot = a.group_segs[j].x == sgm ? 0 : 1;
+      const size_t row = (size_t)(2 * j + slot) * HG + h;
+      if (act) cb.add(load_coherent(&a.lse[row]), 1.0f, load_coherent(&a.opart[row * D + c]));
     }
-    uint16_t* op = a.out + ((size_t)b * a.num_q_heads + hq) * D + lane * CPT;
-    if constexpr (CPT == 2) {
-      *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(r[0], r[1]);
-    } else {
-      *op = (uint16_t)bf16_rne(r[0]);
+    const int eb = sgm / U;
+    const int hq = (sgm - eb * U) * HG + h;
+    if (act) {
+      const float val = cb.den > 0.f ? cb.num / cb.den : 0.f;
+      a.out[((size_t)eb * Hq + hq) * D + c] = (uint16_t)bf16_rne(val);
     }
+    if (tid == 0) __hip_atomic_store(&a.counters[sgm], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 template <int D>
-hipError_t launch_split_d(const DecodeArgs& a, int hg, int grid, hipStream_t s) {
+hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
   switch (hg) {
-    case 1: hipLaunchKernelGGL((split_kernel<D, 1>), dim3(grid), dim3(kGroupThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((split_kernel<D, 2>), dim3(grid), dim3(kGroupThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((split_kernel<D, 3>), dim3(grid), dim3(kGroupThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((split_kernel<D, 4>), dim3(grid), dim3(kGroupThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<D, 1>), dim3(groups), dim3(kGroupThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), dim3(groups), dim3(kGroupThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<D, 3>), dim3(groups), dim3(kGroupThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, 4>), dim3(groups), dim3(kGroupThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -464,25 +514,11 @@ hipError_t launch_split_d(const DecodeArgs& a, int hg, int grid, hipStream_t s) 
 
 }  // namespace
 
-hipError_t launch_split(const DecodeArgs& a, int head_dim, int hg, int max_items, hipStream_t s) {
-  const long long grid = (long long)max_items * (a.num_q_heads / hg);
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (head_dim == 128) return launch_split_d<128>(a, hg, (int)grid, s);
-  if (head_dim == 64) return launch_split_d<64>(a, hg, (int)grid, s);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int hg, int groups, hipStream_t s) {
+  if (groups <= 0) return hipSuccess;
+  if (head_dim == 128) return launch_d<128>(a, hg, groups, s);
+  if (head_dim == 64) return launch_d<64>(a, hg, groups, s);
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_merge(const DecodeArgs& a, int head_dim, hipStream_t s) {
-  const long long grid = (long long)a.batch * a.num_q_heads;
-  if (grid <= 0) return hipSuccess;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)grid), dim3(kGroupThreads), 0, s, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)grid), dim3(kGroupThreads), 0, s, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -11,17 +11,20 @@
 namespace pkv {
 
 constexpr int kWave = 64;
-constexpr int kDefaultTargetItems = 2048;
-constexpr int kDefaultMinChunkPages = 4;
-constexpr int kMaxSplitsLimit = 4096;
+constexpr int kWavesPerGroup = 8;                      // waves of one decode workgroup
+constexpr int kGroupThreads = kWavesPerGroup * kWave;  // 512
+constexpr int kDefaultMinTiles = 8;
+constexpr int kMaxBatch = 65536;
+constexpr int kMaxGroups = 65536;
+constexpr int kMetaLdsRequests = 8192;  // kv_indptr entries the metadata kernel keeps in LDS
 
 // Header words at the start of the workspace (int32).
 enum HeaderWord : int {
-  kHdrNumItems = 0,    // (request, chunk) items planned this step
-  kHdrChunk = 1,       // planned chunk length in pages (0 when splits are forced)
-  kHdrTotalPages = 2,  // pages over the batch
+  kHdrGroups = 0,      // workgroups the plan uses (W)
+  kHdrTiles = 1,       // tiles T = pages * head groups
+  kHdrUnits = 2,       // head groups per request (U)
   kHdrBatch = 3,       // batch of the last pkv_build_metadata
-  kHdrError = 4,       // error bits latched by kernels since the last metadata build
+  kHdrError = 4,       // error bits latched since the last metadata build
   kHdrWords = 64
 };
 
@@ -31,36 +34,37 @@ enum ErrorBit : int {
   kErrBadIndexPos = 4,
 };
 
+// Range of one wave: tiles of request b, head group u, pages p, p+1, ... and
+// on into the following (request, head group) segments, `count` tiles in all.
+struct alignas(16) WaveRange {
+  int32_t b, u, p, count;
+};
+
 // Byte offsets of the workspace sections; every section is 256-byte aligned.
 struct WsLayout {
-  int32_t max_items;  // (request, chunk) items the partial buffers hold
-  size_t hdr, split_indptr, items, lse, opart, total;
+  int32_t groups;    // decode grid size (workgroups)
+  int32_t segments;  // max_batch * U
+  size_t hdr, waves, group_segs, seg_groups, counters, lse, opart, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Returns false for an invalid descriptor.
-bool ws_layout(const pkv_desc& d, WsLayout* out);
+// Query heads one head group covers (the rest of a GQA group of more than four
+// heads goes to sibling head groups that read the same K/V tiles).
+inline int heads_per_group(int G) { return G <= 4 ? G : 4; }
 
-// Resolved per-descriptor tuning values.
-inline int target_items(const pkv_desc& d) {
-  return d.target_items > 0 ? d.target_items : kDefaultTargetItems;
-}
-inline int min_chunk(const pkv_desc& d) {
-  return d.min_chunk_pages > 0 ? d.min_chunk_pages : kDefaultMinChunkPages;
-}
-
-// Query heads one wave of the split kernel handles (the rest of a GQA group
-// goes to sibling waves that read the same K/V tiles).
-inline int heads_per_wave(int G) { return G <= 4 ? G : 4; }
+// Returns false for an invalid descriptor; `groups` is the resolved grid size.
+bool ws_layout(const pkv_desc& d, int groups, WsLayout* out);
 
 struct MetaArgs {
   const int32_t* seq_lens;
   int32_t* kv_indptr;
   int32_t* hdr;
-  int32_t* split_indptr;
-  int2* items;
-  int32_t batch, page_size, num_kv_heads, max_splits, target_items, min_chunk, forced, max_items;
+  WaveRange* waves;    // [groups * kWavesPerGroup]
+  int2* group_segs;    // [groups]: first and last segment a workgroup touches
+  int2* seg_groups;    // [segments]: first and last workgroup touching a segment
+  int32_t* counters;   // [segments]: arrivals for the cross-workgroup merge
+  int32_t batch, page_size, units, groups, min_tiles, forced;
 };
 
 struct AppendArgs {
@@ -82,21 +86,22 @@ struct DecodeArgs {
   const int32_t* kv_indices;
   const int32_t* seq_lens;
   int32_t* hdr;
-  const int32_t* split_indptr;
-  const int2* items;
-  float* lse;    // [max_items][Hq], log2-domain log-sum-exp of each chunk
-  float* opart;  // [max_items][Hq][D], normalised chunk outputs
-  uint16_t* out; // [batch][Hq][D] bf16
+  const WaveRange* waves;
+  const int2* group_segs;
+  const int2* seg_groups;
+  int32_t* counters;
+  float* lse;     // [2 * groups][HG], log2-domain log-sum-exp of workgroup partials
+  float* opart;   // [2 * groups][HG][D], normalised workgroup partials
+  uint16_t* out;  // [batch][Hq][D] bf16
   int32_t num_indices, num_pages, num_q_heads, num_kv_heads, page_size, batch;
-  int32_t max_items;    // capacity of the partial buffers, in (request, chunk) items
+  int32_t units;        // head groups per request
   int32_t log2_rounds;  // log2(page_size / tokens per round); tokens per round = 1024 / head_dim
   float scale_log2;     // sm_scale * log2(e)
 };
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
-hipError_t launch_split(const DecodeArgs& a, int head_dim, int heads_per_wave, int max_items,
-                        hipStream_t s);
-hipError_t launch_merge(const DecodeArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, int groups,
+                         hipStream_t s);
 
 }  // namespace pkv

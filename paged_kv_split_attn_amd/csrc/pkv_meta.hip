@@ -1,12 +1,14 @@
-// Step metadata (page prefix sums + split plan) and the KV-append kernel.
+// Step metadata (page prefix sums + work plan) and the KV-append kernel.
 //
 // The prefix sum is built once per decode step and reused by every layer, as
 // the pages moved it out of the per-layer attention call (AstrAI commit
-// 05739629, astrai/inference, bind_tasks bullets).  The plan sizes chunks so a
-// batch yields about target_items (chunk, KV head) work items: the pages tuned
-// their split count to the number of blocks that saturates bandwidth
-// (commits by ViperEkura, compute_num_splits bullets); here the count is sized
-// for 256 CUs and computed on the device, so the host never reads seq_lens.
+// 05739629, astrai/inference, bind_tasks bullets).  The plan then cuts the
+// step's tiles (request, head group, page) into equal contiguous ranges, one
+// per workgroup and one per wave: the pages tuned their split count to the
+// number of blocks that saturates bandwidth (commits by ViperEkura,
+// compute_num_splits bullets); here every wave gets the same number of pages
+// whatever the length mix, and the plan is computed on the device, so the host
+// never reads seq_lens.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -45,16 +47,45 @@ __device__ int block_inclusive_scan(int x, int* smem, int* total) {
 
 __device__ __forceinline__ int pages_of(int len, int P) { return len > 0 ? (len + P - 1) / P : 0; }
 
+struct Locator {
+  const int32_t* ip;  // page prefix sums (LDS copy or global)
+  int batch, units;
+  // (request, head group, page) of tile t < T: the request is the largest b
+  // with ip[b] * U <= t (requests without pages have empty ranges).
+  __device__ WaveRange at(long long t, int count) const {
+    int lo = 0, hi = batch;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((long long)ip[mid] * units <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    const int n = ip[lo + 1] - ip[lo];
+    const long long r = t - (long long)ip[lo] * units;
+    const int u = (int)(r / n);
+    WaveRange w;
+    w.b = lo;
+    w.u = u;
+    w.p = (int)(r - (long long)u * n);
+    w.count = count;
+    return w;
+  }
+};
+
 __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
   __shared__ int smem[kMetaWaves];
   __shared__ int s_err;
+  __shared__ int32_t s_ip[kMetaLdsRequests + 1];
   const int tid = threadIdx.x;
+  const bool in_lds = a.batch <= kMetaLdsRequests;
   int err = 0;
-  if (tid == 0) s_err = 0;
+  if (tid == 0) {
+    s_err = 0;
+    s_ip[0] = 0;
+    a.kv_indptr[0] = 0;
+  }
 
   // Phase 1: kv_indptr = exclusive prefix sum of page counts.
   int carry = 0;
-  if (tid == 0) a.kv_indptr[0] = 0;
   for (int base = 0; base < a.batch; base += kMetaThreads) {
     const int b = base + tid;
     int n = 0;
@@ -65,41 +96,71 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
     }
     int total;
     const int incl = block_inclusive_scan(n, smem, &total);
-    if (b < a.batch) a.kv_indptr[b + 1] = carry + incl;
+    if (b < a.batch) {
+      a.kv_indptr[b + 1] = carry + incl;
+      if (in_lds) s_ip[b + 1] = carry + incl;
+    }
     carry += total;
   }
-  const int N = carry;
+  __syncthreads();
 
-  // Phase 2: chunks per request and their prefix sum.
-  int chunk = 0;
-  if (a.forced <= 0) {
-    const long long want = ((long long)a.num_kv_heads * N + a.target_items - 1) / a.target_items;
-    chunk = (int)(want > a.min_chunk ? want : a.min_chunk);
+  const int U = a.units;
+  const long long T = (long long)carry * U;
+  int W = 0;
+  if (T > 0) {
+    if (a.forced > 0) {
+      W = min(a.forced, a.groups);
+      if ((long long)W > T) W = (int)T;  // every workgroup gets at least one tile
+    } else {
+      const long long want = (T + a.min_tiles - 1) / a.min_tiles;
+      W = (int)(want < a.groups ? want : a.groups);
+    }
   }
-  carry = 0;
-  if (tid == 0) a.split_indptr[0] = 0;
-  for (int base = 0; base < a.batch; base += kMetaThreads) {
-    const int b = base + tid;
-    int ns = 0;
-    if (b < a.batch) {
-      const int n = pages_of(a.seq_lens[b], a.page_size);
-      if (n > 0) {
-        if (a.forced > 0) {
-          ns = min(min(a.forced, n), a.max_splits);
-        } else {
-          ns = min((n + chunk - 1) / chunk, a.max_splits);
-        }
-      }
+  Locator loc{in_lds ? s_ip : a.kv_indptr, a.batch, U};
+
+  // Phase 2: every wave's range.  Group i covers [i*T/W, (i+1)*T/W); its wave
+  // w covers the w-th of kWavesPerGroup equal parts.
+  for (int gw = tid; gw < a.groups * kWavesPerGroup; gw += kMetaThreads) {
+    const int i = gw / kWavesPerGroup;
+    const int w = gw - i * kWavesPerGroup;
+    WaveRange r{0, 0, 0, 0};
+    if (i < W) {
+      const long long g0 = (long long)i * T / W, g1 = (long long)(i + 1) * T / W;
+      const long long len = g1 - g0;
+      const long long t0 = g0 + (long long)w * len / kWavesPerGroup;
+      const long long t1 = g0 + (long long)(w + 1) * len / kWavesPerGroup;
+      if (t1 > t0) r = loc.at(t0, (int)(t1 - t0));
     }
-    int total;
-    const int incl = block_inclusive_scan(ns, smem, &total);
-    if (b < a.batch) {
-      a.split_indptr[b + 1] = carry + incl;
-      // Phase 3: the work list, ordered by request then chunk.
-      const int first = carry + incl - ns;
-      for (int s = 0; s < ns && first + s < a.max_items; ++s) a.items[first + s] = make_int2(b, s);
+    a.waves[gw] = r;
+  }
+
+  // Phase 3: first and last segment (b * U + u) of every workgroup.
+  for (int i = tid; i < a.groups; i += kMetaThreads) {
+    int2 gs = make_int2(-1, -1);
+    const long long g0 = i < W ? (long long)i * T / W : 0;
+    const long long g1 = i < W ? (long long)(i + 1) * T / W : 0;
+    if (g1 > g0) {
+      const WaveRange f = loc.at(g0, 0), l = loc.at(g1 - 1, 0);
+      gs = make_int2(f.b * U + f.u, l.b * U + l.u);
     }
-    carry += total;
+    a.group_segs[i] = gs;
+  }
+
+  // Phase 4: first and last workgroup of every segment; arrival counters.
+  // Tile t belongs to group floor(((t + 1) * W - 1) / T).
+  for (int sgi = tid; sgi < a.batch * U; sgi += kMetaThreads) {
+    const int b = sgi / U;
+    const int u = sgi - b * U;
+    const int ip0 = loc.ip[b];
+    const int n = loc.ip[b + 1] - ip0;
+    int2 sg = make_int2(-1, -1);
+    if (n > 0 && W > 0) {
+      const long long t0 = (long long)ip0 * U + (long long)u * n;
+      const long long t1 = t0 + n - 1;
+      sg = make_int2((int)(((t0 + 1) * W - 1) / T), (int)(((t1 + 1) * W - 1) / T));
+    }
+    a.seg_groups[sgi] = sg;
+    a.counters[sgi] = 0;
   }
 
   if (err) atomicOr(&s_err, err);
@@ -107,9 +168,9 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
   if (tid == 0) {
     // The metadata build starts a step: its bits replace the previous step's.
     a.hdr[kHdrError] = s_err;
-    a.hdr[kHdrNumItems] = min(carry, a.max_items);
-    a.hdr[kHdrChunk] = chunk;
-    a.hdr[kHdrTotalPages] = N;
+    a.hdr[kHdrGroups] = W;
+    a.hdr[kHdrTiles] = (int)T;
+    a.hdr[kHdrUnits] = U;
     a.hdr[kHdrBatch] = a.batch;
   }
 }

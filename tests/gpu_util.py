@@ -20,17 +20,16 @@ def say(*a):
     sys.stdout.flush()
 
 
-def make_desc(batch, max_splits=256, target_items=0, min_chunk_pages=0, max_batch=None):
+def make_desc(batch, num_workgroups=0, min_tiles=0, max_batch=None):
     return pkv.Desc(max_batch=max_batch or batch.B, num_q_heads=batch.Hq,
                     num_kv_heads=batch.Hkv, head_dim=batch.D, page_size=batch.P,
-                    max_splits=max_splits, target_items=target_items,
-                    min_chunk_pages=min_chunk_pages)
+                    num_workgroups=num_workgroups, min_tiles_per_group=min_tiles)
 
 
-def forced_desc(batch, forced):
-    """Descriptor whose chunk capacity admits `forced` splits for every request."""
-    return make_desc(batch, max_splits=max(forced, 1),
-                     target_items=batch.Hkv * batch.B * max(forced, 1))
+def oracle_plan(batch, desc, forced=0):
+    _, U = oracle.head_groups(batch.Hq, batch.Hkv)
+    return oracle.plan_stream(batch.seq_lens, batch.P, U, desc.groups(),
+                              desc.min_tiles_per_group or 8, forced)
 
 
 class GpuRun:

@@ -24,8 +24,7 @@ def test_header_declares_expected_entry_points():
     names = pkv.declared_functions()
     assert set(names) == {
         "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
-        "pkv_append_kv", "pkv_decode", "pkv_decode_partials", "pkv_decode_merge",
-        "pkv_debug_validate"}
+        "pkv_append_kv", "pkv_decode", "pkv_debug_validate"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -51,12 +50,12 @@ def test_status_strings_and_version(lib):
     for st in range(1, 7):
         assert pkv.pkv_status_str(st) not in ("ok", "unknown status")
     assert pkv.pkv_status_str(99) == "unknown status"
-    assert pkv.pkv_version() >> 16 == 1
+    assert pkv.pkv_version() >> 16 == 2
 
 
 def _desc(**kw):
     base = dict(max_batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
-                max_splits=256, target_items=0, min_chunk_pages=0)
+                num_workgroups=256, min_tiles_per_group=0)
     base.update(kw)
     return pkv.Desc(**base)
 
@@ -64,15 +63,15 @@ def _desc(**kw):
 def test_workspace_bytes(lib):
     d = _desc()
     n = pkv.pkv_workspace_bytes(d)
-    # max items = min(16 * 256, ceil(2048 / 8) + 16) = 272 (request, chunk) items
-    items = 272
+    groups, hg, segs = 256, 4, 16 * 8
     expect = 256  # header
-    for sz in (4 * 17, 8 * items, 4 * items * 32, 4 * items * 32 * 128):
+    for sz in (16 * groups * 8, 8 * groups, 8 * segs, 4 * segs, 4 * 2 * groups * hg,
+               4 * 2 * groups * hg * 128):
         expect += (sz + 255) // 256 * 256
     assert n == expect
-    assert pkv.pkv_workspace_bytes(_desc(max_batch=1, max_splits=3)) < n
-    for bad in (dict(num_q_heads=30), dict(max_batch=0), dict(max_splits=0),
-                dict(max_splits=5000), dict(target_items=-1)):
+    assert pkv.pkv_workspace_bytes(_desc(num_workgroups=16)) < n
+    for bad in (dict(num_q_heads=30), dict(max_batch=0), dict(num_workgroups=-1),
+                dict(num_workgroups=70000), dict(min_tiles_per_group=-1)):
         with pytest.raises(pkv.PkvError):
             pkv.pkv_workspace_bytes(_desc(**bad))
 
@@ -97,8 +96,8 @@ def test_host_checks_reject_before_launch(lib):
     assert _raw(lib, "pkv_build_metadata", B(d), fake, 4, 0, fake, fake, ws_bytes - 1, None) == 3
     assert _raw(lib, "pkv_decode", B(pool), B(d), fake, fake, fake, 10, fake, 4, 0.1, fake,
                 ws_bytes - 1, fake, None) == 3
-    # forced splits beyond the item capacity: 16 requests x 256 splits > 272 items
-    assert _raw(lib, "pkv_build_metadata", B(d), fake, 16, 256, fake, fake, ws_bytes, None) == 4
+    # negative forced workgroup count
+    assert _raw(lib, "pkv_build_metadata", B(d), fake, 4, -1, fake, fake, ws_bytes, None) == 1
     # unsupported head_dim / page_size / group size
     for bad in (dict(head_dim=96), dict(page_size=12), dict(page_size=24),
                 dict(num_q_heads=48, num_kv_heads=8)):

@@ -14,7 +14,7 @@ import torch
 import oracle
 import paged_kv_split_attn_amd as pkv
 import workloads as W
-from gpu_util import GpuRun, compare, forced_desc, make_desc, oracle_out, say
+from gpu_util import GpuRun, compare, make_desc, oracle_out, oracle_plan, say
 
 pytestmark = pytest.mark.gpu
 
@@ -34,12 +34,6 @@ def ref(i):
     return _REFS[i]
 
 
-def plan_of(batch, desc, forced):
-    T = desc.target_items or 2048
-    cmin = desc.min_chunk_pages or 4
-    return oracle.plan_splits(batch.seq_lens, batch.P, batch.Hkv, desc.max_splits, T, cmin, forced)
-
-
 # ------------------------------------------------------------------ metadata
 
 def _random_lengths_batch(seed, B, with_zeros):
@@ -50,16 +44,16 @@ def _random_lengths_batch(seed, B, with_zeros):
 
 
 @pytest.mark.parametrize("case", ["c1", "c2", "c3", "c4", "c5", "rand0", "rand1", "rand_big"])
-@pytest.mark.parametrize("forced", [0, 3])
-def test_metadata_bit_exact(case, forced):
-    say(f"metadata case={case} forced={forced}")
+@pytest.mark.parametrize("grid,forced", [(0, 0), (0, 3), (1000, 0)])
+def test_metadata_bit_exact(case, grid, forced):
+    say(f"metadata case={case} grid={grid} forced={forced}")
     if case.startswith("c"):
         batch = cfg(int(case[1]))
     elif case == "rand_big":
         batch = _random_lengths_batch(77, 1500, True)  # more requests than one block scans at once
     else:
         batch = _random_lengths_batch(int(case[-1]) + 10, 37, case == "rand0")
-    desc = forced_desc(batch, forced) if forced else make_desc(batch)
+    desc = make_desc(batch, num_workgroups=grid)
     run = GpuRun(batch, desc)
     run.metadata(forced)
     torch.cuda.synchronize()
@@ -67,10 +61,9 @@ def test_metadata_bit_exact(case, forced):
     assert np.array_equal(ip, oracle.kv_indptr(batch.seq_lens, batch.P))
     info = run.validate()
     assert info["status"] == pkv.PKV_OK
-    plan = plan_of(batch, desc, forced)
-    assert info["nsplit"] == list(plan["nsplit"])
-    assert info["items"] == plan["num_items"]
-    assert info["chunk"] == (0 if forced else plan["chunk"])
+    plan = oracle_plan(batch, desc, forced)
+    assert info["groups"] == plan["groups"]
+    assert np.array_equal(np.array(info["waves"]), plan["waves"])
 
 
 # -------------------------------------------------------------------- append
@@ -98,27 +91,40 @@ def test_append_bit_exact(which):
 
 # -------------------------------------------------------------------- decode
 
-DECODE_CASES = [
-    (1, 1), (1, 3), (1, 0),
-    (2, 0), (2, 1), (2, 32),
-    (3, 0), (3, 1), (3, 7),
-    (4, 0), (4, 1), (4, 256),
-    (5, 0),
+DECODE_CASES = [  # (workload, grid size (0 = one per CU), forced workgroups (0 = planner))
+    (1, 0, 1), (1, 0, 3), (1, 0, 0),
+    (2, 0, 0), (2, 0, 1), (2, 1024, 1024),
+    (3, 0, 0), (3, 0, 1), (3, 0, 7), (3, 2048, 0),
+    (4, 0, 0), (4, 0, 1), (4, 4096, 0),
+    (5, 0, 0), (5, 64, 0),
 ]
 
 
-@pytest.mark.parametrize("i,forced", DECODE_CASES, ids=[f"cfg{i}-splits{f or 'plan'}" for i, f in DECODE_CASES])
-def test_decode_parity(i, forced):
+@pytest.mark.parametrize("i,grid,forced", DECODE_CASES,
+                         ids=[f"cfg{i}-grid{g or 'cu'}-groups{f or 'plan'}" for i, g, f in DECODE_CASES])
+def test_decode_parity(i, grid, forced):
     batch = cfg(i)
-    say(f"decode cfg{i} ({batch.name}) forced={forced}")
-    desc = forced_desc(batch, forced) if forced else make_desc(batch)
+    say(f"decode cfg{i} ({batch.name}) grid={grid} forced={forced}")
+    desc = make_desc(batch, num_workgroups=grid)
     run = GpuRun(batch, desc)
     got = run.step(forced)
     info = run.validate()
     assert info["status"] == pkv.PKV_OK
-    if forced:
-        assert all(n == min(forced, len(pl)) for n, pl in zip(info["nsplit"], batch.page_lists))
-    compare(got, ref(i), f"cfg{i} splits={forced or 'plan'} items={info['items']}")
+    assert info["groups"] == oracle_plan(batch, desc, forced)["groups"]
+    compare(got, ref(i), f"cfg{i} grid={grid or 'cu'} groups={info['groups']}")
+
+
+def test_repeated_decodes_reuse_one_plan():
+    # several layers per step: one metadata build, many decodes (merge counters reset themselves)
+    batch = cfg(3)
+    say("repeated decodes cfg3")
+    run = GpuRun(batch, make_desc(batch, num_workgroups=512))
+    first = run.step()
+    for _ in range(3):
+        run.decode()
+        torch.cuda.synchronize()
+        assert np.array_equal(run.out_bits(), first)
+    compare(first, ref(3), "cfg3 repeated")
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,P", [
@@ -135,9 +141,8 @@ def test_decode_shapes(Hq, Hkv, D, P):
     batch = W.make_batch(name="shape", seed=Hq * 131 + D + P, B=5, Hq=Hq, Hkv=Hkv, D=D, P=P,
                          lengths=np.array([1, P - 1, P + 1, 5 * P + 3, 700]))
     expect = oracle_out(batch)
-    for forced in (0, 2):
-        desc = forced_desc(batch, forced) if forced else make_desc(batch, min_chunk_pages=1,
-                                                                   target_items=16)
+    for grid, forced in ((0, 0), (0, 2), (300, 300)):
+        desc = make_desc(batch, num_workgroups=grid, min_tiles=1)
         got = GpuRun(batch, desc).step(forced)
         compare(got, expect, f"Hq={Hq} Hkv={Hkv} D={D} P={P} forced={forced}")
 
@@ -158,7 +163,7 @@ def test_zero_length_requests_give_zero_rows():
     say("zero lengths")
     batch = W.make_batch(name="zeros", seed=6, B=5, Hq=32, Hkv=8, D=128, P=16,
                          lengths=np.array([0, 100, 0, 1, 17]))
-    got = GpuRun(batch, make_desc(batch, min_chunk_pages=1, target_items=64)).step()
+    got = GpuRun(batch, make_desc(batch, min_tiles=1)).step()
     assert not got[0].any() and not got[2].any()
     compare(got, oracle_out(batch), "zero-length mix")
 

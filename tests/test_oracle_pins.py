@@ -224,56 +224,100 @@ def pin_kv_indptr(mod):
             assert (n == 0 and L == 0) or ((n - 1) * batch.P < L <= n * batch.P)
 
 
-def _search_plan(seq_lens, P, Hkv, max_splits, target, min_chunk, forced):
-    pages = []
-    for L in seq_lens:
+def _enumerate_tiles(seq_lens, P, U):
+    """Every (request, head group, page) tile, listed one by one."""
+    tiles = []
+    for b, L in enumerate(seq_lens):
         n = 0
         while n * P < L:
             n += 1
-        pages.append(n)
-    N = sum(pages)
-    chunk = min_chunk
-    while chunk * target < Hkv * N:
-        chunk += 1
-    ns = []
-    for n in pages:
-        if n == 0:
-            ns.append(0)
-        elif forced:
-            ns.append(min(forced, n, max_splits))
-        else:
-            k = 1
-            while k * chunk < n:
-                k += 1
-            ns.append(min(k, max_splits))
-    return chunk, ns
+        for u in range(U):
+            for p in range(n):
+                tiles.append((b, u, p))
+    return tiles
+
+
+def _pieces_of_plan(tiles, waves):
+    """(b, u, first page, pages) pieces: each wave's range cut at segment borders."""
+    pieces, pos = [], 0
+    for b, u, p, cnt in waves:
+        if cnt == 0:
+            continue
+        pos = tiles.index((b, u, p), pos)
+        run = tiles[pos:pos + cnt]
+        assert len(run) == cnt
+        start = run[0]
+        n = 1
+        for prev, cur in zip(run, run[1:]):
+            if cur[:2] == prev[:2]:
+                n += 1
+            else:
+                pieces.append((*start, n))
+                start, n = cur, 1
+        pieces.append((*start, n))
+        pos += cnt
+    return pieces
 
 
 def pin_plan(mod):
     rng = np.random.default_rng(7)
-    cases = [(np.array([37]), 16, 2, 4, 64, 1, 3)]
-    for _ in range(60):
-        B = int(rng.integers(1, 20))
-        seq = rng.integers(0, 3000, size=B)
+    cases = [(np.array([37]), 16, 8, 256, 8, 0), (np.array([0, 0]), 16, 8, 4, 8, 0)]
+    for _ in range(40):
+        B = int(rng.integers(1, 12))
+        seq = rng.integers(0, 700, size=B)
         cases.append((seq, int(rng.choice([1, 4, 16])), int(rng.choice([1, 2, 8])),
-                      int(rng.integers(1, 300)), int(rng.choice([64, 512, 2048])),
-                      int(rng.integers(1, 9)), int(rng.choice([0, 0, 1, 3, 7]))))
-    for seq, P, Hkv, smax, target, cmin, forced in cases:
-        plan = mod.plan_splits(seq, P, Hkv, smax, target, cmin, forced)
-        chunk, ns = _search_plan(list(seq), P, Hkv, smax, target, cmin, forced)
-        assert plan["chunk"] == chunk
-        assert list(plan["nsplit"]) == ns
-        assert list(np.diff(plan["split_indptr"])) == ns and plan["split_indptr"][0] == 0
-        if not forced:
-            assert plan["num_items"] <= -(-target // Hkv) + len(seq)
-        for n, k in zip([len(range(0, L, P)) for L in seq], ns):
-            if k == 0:
-                continue
-            ranges = mod.even_page_ranges(n, k)
-            assert ranges[0][0] == 0 and ranges[-1][1] == n
-            assert all(ranges[i][1] == ranges[i + 1][0] for i in range(k - 1))
-            sizes = [r1 - r0 for r0, r1 in ranges]
-            assert max(sizes) - min(sizes) <= 1 and min(sizes) >= 1
+                      int(rng.integers(1, 64)), int(rng.integers(1, 12)),
+                      int(rng.choice([0, 0, 1, 3, 50]))))
+    for seq, P, U, groups, mt, forced in cases:
+        plan = mod.plan_stream(seq, P, U, groups, mt, forced)
+        tiles = _enumerate_tiles(list(seq), P, U)
+        T = len(tiles)
+        assert plan["tiles"] == T
+        # workgroups: fewest with min_tiles each, capped by the grid (or forced)
+        if T == 0:
+            W = 0
+        elif forced:
+            W = min(forced, groups, T)
+        else:
+            W = 1
+            while W * mt < T and W < groups:
+                W += 1
+        assert plan["groups"] == W
+        waves = [tuple(int(x) for x in r) for r in plan["waves"]]
+        assert len(waves) == groups * 8
+        # every tile exactly once, in order, and equal shares per workgroup and wave
+        covered = []
+        pos = 0
+        for i in range(groups):
+            share = []
+            for w in range(8):
+                b, u, p, cnt = waves[i * 8 + w]
+                if cnt:
+                    assert tiles[pos] == (b, u, p)
+                share.append(cnt)
+                covered.extend(tiles[pos:pos + cnt])
+                pos += cnt
+            if i < W:
+                tot = sum(share)
+                assert abs(tot - T / W) < 1 and max(share) - min(share) <= 1
+            else:
+                assert sum(share) == 0
+        assert covered == tiles
+
+
+def pin_stream_pieces(mod):
+    """The plan's pieces merge to the unsplit result for many grid sizes."""
+    for batch in (tiny_batch(), gqa8_batch(), W.config(1)):
+        HG, U = mod.head_groups(batch.Hq, batch.Hkv)
+        ip = mod.kv_indptr(batch.seq_lens, batch.P)
+        ref = run_decode(mod, batch)
+        tiles = _enumerate_tiles(list(batch.seq_lens), batch.P, U)
+        for groups, mt, forced in ((1, 8, 0), (3, 1, 0), (64, 1, 0), (5, 8, 2), (7, 1, 7)):
+            plan = mod.plan_stream(batch.seq_lens, batch.P, U, groups, mt, forced)
+            pieces = _pieces_of_plan(tiles, plan["waves"])
+            got = mod.decode_pieces(batch.q, batch.k_pool, batch.v_pool, ip, batch.kv_indices,
+                                    batch.seq_lens, batch.sm_scale, batch.P, pieces)
+            np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
 def pin_append(mod):
@@ -307,8 +351,8 @@ def pin_poison(mod):
 
 
 PINS = [pin_brute_force, pin_seq_len_one, pin_permutation, pin_split_invariance, pin_q_zero,
-        pin_constant_v, pin_dominant_key, pin_sdpa, pin_kv_indptr, pin_plan, pin_append,
-        pin_poison]
+        pin_constant_v, pin_dominant_key, pin_sdpa, pin_kv_indptr, pin_plan, pin_stream_pieces,
+        pin_append, pin_poison]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -386,12 +430,23 @@ def _mutants():
 
     m["page_count_floor"] = {"page_counts": lambda L, P: np.asarray(L, np.int64) // P}
 
-    def plan_floor_chunk(seq_lens, P, Hkv, max_splits, target_items, min_chunk, forced=0):
-        p = OA.__dict__["_orig_plan_splits"](seq_lens, P, Hkv, max_splits, target_items, min_chunk, forced)
-        N = p["total_pages"]
-        p["chunk"] = max(min_chunk, Hkv * N // target_items)
+    def plan_group_bounds_ceil(seq_lens, P, units, groups, min_tiles, forced=0, waves_per_group=8):
+        p = OA.__dict__["_orig_plan_stream"](seq_lens, P, units, groups, min_tiles, forced,
+                                              waves_per_group)
+        # a plausible slip: the last wave of every group starts one tile late
+        for i in range(p["groups"]):
+            r = p["waves"][i * waves_per_group + waves_per_group - 1]
+            if r[3] > 1:
+                b, u, pg = OA.tile_of(p["kv_indptr"], units,
+                                      sum(int(x[3]) for x in p["waves"][:i * waves_per_group + 7]) + 1)
+                r[:] = (b, u, pg, r[3] - 1)
         return p
-    m["plan_chunk_floor"] = {"plan_splits": plan_floor_chunk}
+    m["plan_wave_start_shifted"] = {"plan_stream": plan_group_bounds_ceil}
+
+    def pieces_drop_first_page(q, k, v, ip, idx, sl, sc, P, pieces):
+        pieces = [(b, u, p0 + (1 if n > 1 else 0), n - (1 if n > 1 else 0)) for b, u, p0, n in pieces]
+        return OA.__dict__["_orig_decode_pieces"](q, k, v, ip, idx, sl, sc, P, pieces)
+    m["pieces_skip_a_page"] = {"decode_pieces": pieces_drop_first_page}
 
     def append_at_len(k_pool, v_pool, k_new, v_new, indptr, indices, seq_lens, P):
         return OA.__dict__["_orig_append_kv"](k_pool, v_pool, k_new, v_new, indptr, indices,
@@ -405,7 +460,7 @@ MUTANTS = _mutants()
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistakes(name, monkeypatch):
-    for fn in ("softmax_attend", "chunk_partial", "plan_splits", "append_kv"):
+    for fn in ("softmax_attend", "chunk_partial", "plan_stream", "decode_pieces", "append_kv"):
         monkeypatch.setitem(OA.__dict__, "_orig_" + fn, getattr(OA, fn))
     for attr, repl in MUTANTS[name].items():
         monkeypatch.setattr(OA, attr, repl)
