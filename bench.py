@@ -9,9 +9,9 @@ identical copies whose total size exceeds the 256 MB Infinity Cache, so every
 step streams its K/V from HBM.
 
 Timing: after W warm-up steps, a bounded spin kernel holds the GPU while the
-host enqueues all K timed steps; HIP events then bracket the K steps (step
-time) and every decode-kernel launch (kernel time), on the stream the kernels
-run on.
+host enqueues all K timed steps; two HIP events on the stream the kernels run
+on bracket the K steps (step time).  The decode kernel alone is then timed the
+same way over K back-to-back launches (kernel time, the roofline figure).
 
 Prints one JSON line.  `value` is algorithmic GB/s of the whole step:
 bytes the method must move (K/V attended, q, output, page ids, appended rows)
@@ -33,7 +33,7 @@ import numpy as np  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "paged decode attention µs/call + achieved HBM GB/s (% of peak), B=16 ragged"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "split_kernel_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kernel_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_split_attn_amd", "csrc", "pkv_decode.hip")
 
 
@@ -48,8 +48,10 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0 = enough for 768 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-kernel-events", action="store_true",
-                    help="time only whole steps (no events around the decode kernel)")
+    ap.add_argument("--no-kernel-loop", action="store_true",
+                    help="time only whole steps (skip the decode-only loop)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--warm", action="store_true", help="no pool rotation (cache-warm numbers)")
     return ap.parse_args()
 
@@ -90,7 +92,7 @@ def cpu_baseline(batch, budget_s):
 
 
 def counters_for_current_kernel():
-    """rocprofv3 FETCH/WRITE per split launch, if taken on the current kernel source."""
+    """rocprofv3 FETCH/WRITE per decode launch, if taken on the current kernel source."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     try:
@@ -103,8 +105,40 @@ def counters_for_current_kernel():
         return None
 
 
+def calibrate_copy(mib, reps=5):
+    """A plain device-to-device copy of a known size, for scaling HBM counters."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": reps}), flush=True)
+
+
+def timed(stream, K, fn):
+    """Mean ms of fn(i) over K calls enqueued behind a bounded spin, events at the ends."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(40e6))  # hold the GPU while the host enqueues the K calls
+    start.record(stream)
+    for i in range(K):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / K
+
+
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
@@ -149,15 +183,15 @@ def main():
     k_new, v_new = base["k_new"], base["v_new"]
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
         pool, q = copies[i % ncopies]
         pkv.pkv_build_metadata(desc, seq, 0, kv_indptr, ws, stream)
         pkv.pkv_append_kv(pool, k_new, v_new, kv_indptr, idx, seq, stream)
-        if ev is not None:
-            ev[0].record(stream)
         pkv.pkv_decode(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, stream)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def decode_only(i):
+        pool, q = copies[i % ncopies]
+        pkv.pkv_decode(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, stream)
 
     for i in range(args.warmup):
         step(i)
@@ -167,20 +201,7 @@ def main():
         raise RuntimeError("device metadata failed validation")
 
     K = args.steps
-    evs = None
-    if not args.no_kernel_events:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    # hold the GPU (bounded spin) while the host enqueues the K steps
-    torch.cuda._sleep(int(40e6))
-    start.record(stream)
-    for i in range(K):
-        step(i, evs[i] if evs else None)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / K
+    ms_step = timed(stream, K, step)
 
     call_bytes, step_bytes = algorithmic_bytes(batch)
     res = {
@@ -204,8 +225,8 @@ def main():
         "step_bytes": step_bytes,
         "call_bytes": call_bytes,
     }
-    if evs:
-        call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    if not args.no_kernel_loop:
+        call_ms = timed(stream, K, decode_only)
         achieved = call_bytes / (call_ms * 1e-3) / 1e9
         ctr = counters_for_current_kernel()
         traffic = None

@@ -17,12 +17,17 @@
  * the newest position, so a causal mask removes nothing.
  *
  * Paged KV pool.  K and V of one layer live in fixed-size pages of a pool shared
- * by all requests.  This library lays a pool out page-major, then head-major:
+ * by all requests.  This library lays a pool out page-major, then head-major,
+ * and stores each (page, KV head) tile in the order its matrix-core loads read
+ * it:
  *
- *     K, V : bf16 [num_pages][Hkv][page_size][head_dim]   (contiguous)
+ *     K : bf16 [num_pages][Hkv][head_dim / 8][page_size][8]
+ *     V : bf16 [num_pages][Hkv][head_dim][page_size]
  *
- * so the page_size x head_dim tile of one (page, KV head) is one contiguous
- * run of bytes.  Token t of request b lives in page
+ * K(t, c) of a tile sits at [c / 8][t][c % 8] and V(t, c) at [c][t].  One tile
+ * is one contiguous run of bytes, and every load instruction of the decode
+ * reads whole contiguous blocks (1 KiB of K, 512 B of V).  Token t of request b
+ * lives in page
  * kv_indices[kv_indptr[b] + t / page_size] at offset t % page_size (the pages'
  * PagePool addressing: page index pos // page_size, offset pos % page_size,
  * astrai/inference/core/cache.py on the compare page).  kv_indptr counts
@@ -70,6 +75,10 @@
 extern "C" {
 #endif
 
+/* Waves (64 lanes each) in one decode workgroup: two per SIMD of a compute
+ * unit.  The plan splits every workgroup's tile range into this many parts. */
+#define PKV_WAVES_PER_WORKGROUP 8
+
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1,          /* null pointer, negative size, inconsistent shapes */
@@ -86,8 +95,9 @@ const char* pkv_status_str(int status);
 /* Library ABI version: (major << 16) | minor. */
 int32_t pkv_version(void);
 
-/* One layer's paged K/V pool (device memory owned by the caller).
- * k, v: bf16 [num_pages][num_kv_heads][page_size][head_dim], contiguous. */
+/* One layer's paged K/V pool (device memory owned by the caller), contiguous:
+ * k: bf16 [num_pages][num_kv_heads][head_dim / 8][page_size][8]
+ * v: bf16 [num_pages][num_kv_heads][head_dim][page_size] */
 typedef struct pkv_pool {
   int32_t num_pages;
   int32_t page_size;
@@ -107,7 +117,7 @@ typedef struct pkv_pool {
  *  num_q_heads          Hq; num_kv_heads must divide it
  *  num_kv_heads         Hkv
  *  head_dim             D, 64 or 128
- *  page_size            P, a power of two >= 1024 / D (16 and up for both head dims)
+ *  page_size            P, a power of two >= 16
  *  num_workgroups       workgroups of the decode grid (0 = one per compute unit
  *                       of the device current at the call; 1 .. 65536)
  *  min_tiles_per_group  fewest tiles a workgroup is given; small batches use
@@ -143,7 +153,8 @@ size_t pkv_workspace_bytes(const pkv_desc* desc);
  *   groups   W = min(num_workgroups, max(1, ceil(T / min_tiles_per_group))),
  *            or min(forced_groups, num_workgroups, T) when forced_groups > 0;
  *   group i  covers tiles [floor(i*T/W), floor((i+1)*T/W));
- *   wave w   of a group covers the w-th of 8 equal sub-ranges of the group's range.
+ *   wave w   of a group covers the w-th of PKV_WAVES_PER_WORKGROUP equal
+ *            sub-ranges of the group's range.
  * Negative seq_lens count as 0 and latch the device error word.
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_CAPACITY
  * (batch > max_batch), PKV_ERR_WORKSPACE_TOO_SMALL, PKV_ERR_LAUNCH. */
@@ -188,7 +199,8 @@ int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
 /* Debug only (synchronises the stream; not capturable).  Checks device
  * metadata and copies the plan to host memory.
  *  groups_out   host int32 or NULL: workgroups the plan uses (W above)
- *  waves_out    host int32 [num_workgroups * 8 * 4] or NULL: for every wave of
+ *  waves_out    host int32 [num_workgroups * PKV_WAVES_PER_WORKGROUP * 4] or
+ *               NULL: for every wave of
  *               the grid, {request, head group, first page, tiles} of its range
  *               (tiles = 0 for an idle wave)
  * Returns PKV_ERR_DEVICE_DATA if kv_indptr is not the page prefix sum of

@@ -52,10 +52,20 @@ PKV_ERR_WORKSPACE_TOO_SMALL = 3
 PKV_ERR_CAPACITY = 4
 PKV_ERR_LAUNCH = 5
 PKV_ERR_DEVICE_DATA = 6
-WAVES_PER_GROUP = 8  # waves per decode workgroup (fixed by the kernels)
-
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "pkv.h")
+
+
+def _header_define(name: str) -> int:
+    """Integer value of a #define in pkv.h (the header is the single source)."""
+    with open(_HEADER) as f:
+        m = re.search(rf"^#define\s+{name}\s+(\d+)", f.read(), re.M)
+    if m is None:
+        raise RuntimeError(f"{name} not defined in {_HEADER}")
+    return int(m.group(1))
+
+
+WAVES_PER_GROUP = _header_define("PKV_WAVES_PER_WORKGROUP")  # waves per decode workgroup
 
 
 def library_path() -> str:
@@ -184,15 +194,19 @@ class Desc:
 
 @dataclass
 class Pool:
-    """One layer's pool: k, v are bf16 [num_pages, Hkv, page_size, head_dim] device tensors."""
+    """One layer's pool: bf16 device tensors k [num_pages, Hkv, head_dim/8, page_size, 8]
+    and v [num_pages, Hkv, head_dim, page_size] (the library's tile layouts)."""
 
     k: torch.Tensor
     v: torch.Tensor
 
     def c(self) -> _CPool:
-        if self.k.shape != self.v.shape or self.k.dim() != 4:
-            raise ValueError("k and v must both be [num_pages, Hkv, page_size, head_dim]")
-        n, h, p, d = self.k.shape
+        if self.k.dim() != 5 or self.v.dim() != 4 or self.k.shape[4] != 8:
+            raise ValueError("k must be [num_pages, Hkv, head_dim/8, page_size, 8] and v 4-D")
+        n, h, d8, p, _ = self.k.shape
+        d = d8 * 8
+        if tuple(self.v.shape) != (n, h, d, p):
+            raise ValueError("v must be [num_pages, Hkv, head_dim, page_size]")
         return _CPool(n, p, h, d, _ptr(self.k, "pool.k", _BF16), _ptr(self.v, "pool.v", _BF16))
 
 

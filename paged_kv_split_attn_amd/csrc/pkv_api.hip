@@ -45,8 +45,8 @@ namespace {
 // Shapes the kernels are compiled for.
 bool supported(int head_dim, int page_size, int G) {
   if (head_dim != 64 && head_dim != 128) return false;
-  const int tpr = 1024 / head_dim;  // tokens per round of one wave
-  if (page_size < tpr || (page_size & (page_size - 1)) != 0) return false;
+  // A wave consumes 16 tokens of one page per step.
+  if (page_size < 16 || (page_size & (page_size - 1)) != 0) return false;
   if (G < 1 || (G > 4 && G % 4 != 0)) return false;
   return true;
 }
@@ -210,7 +210,7 @@ int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
   d.batch = batch;
   const int hg = heads_per_group(desc->num_q_heads / desc->num_kv_heads);
   d.units = desc->num_q_heads / hg;
-  d.log2_rounds = log2i(desc->page_size / (1024 / desc->head_dim));
+  d.log2_steps = log2i(desc->page_size / 16);
   d.scale_log2 = sm_scale * 1.4426950408889634f;
   return launch_status(
       launch_decode(d, desc->head_dim, hg, L.groups, static_cast<hipStream_t>(stream)));
@@ -239,10 +239,10 @@ int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int3
   if (num_indices > 0)
     ok &= hipMemcpyAsync(idx.data(), kv_indices, sizeof(int32_t) * num_indices,
                          hipMemcpyDeviceToHost, s) == hipSuccess;
+  std::vector<WaveRange> waves(waves_out ? (size_t)L.groups * kWavesPerGroup : 0);
   if (waves_out)
-    ok &= hipMemcpyAsync(waves_out, at<WaveRange>(workspace, L.waves),
-                         sizeof(WaveRange) * (size_t)L.groups * kWavesPerGroup,
-                         hipMemcpyDeviceToHost, s) == hipSuccess;
+    ok &= hipMemcpyAsync(waves.data(), at<WaveRange>(workspace, L.waves),
+                         sizeof(WaveRange) * waves.size(), hipMemcpyDeviceToHost, s) == hipSuccess;
   ok &= hipStreamSynchronize(s) == hipSuccess;
   if (!ok) return PKV_ERR_LAUNCH;
 
@@ -259,6 +259,12 @@ int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int3
   for (long long i = 0; i < used; ++i)
     if (idx[i] < 0 || idx[i] >= num_pages) bad = true;
   if (groups_out) *groups_out = hdr[kHdrGroups];
+  for (size_t i = 0; i < waves.size(); ++i) {
+    waves_out[4 * i + 0] = waves[i].b;
+    waves_out[4 * i + 1] = waves[i].u;
+    waves_out[4 * i + 2] = waves[i].p;
+    waves_out[4 * i + 3] = waves[i].count;
+  }
   if (hdr[kHdrError] != 0) {
     const int32_t zero = 0;
     if (hipMemcpyAsync(at<int32_t>(workspace, L.hdr) + kHdrError, &zero, sizeof(zero),

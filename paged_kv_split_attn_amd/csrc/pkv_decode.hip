@@ -2,7 +2,10 @@
 //
 // Work decomposition (stream-K style).  The step's tiles, ordered (request,
 // head group, page), are cut into equal contiguous ranges: one per workgroup of
-// eight waves, one eighth of that per wave.  A head group is HG query heads
+// eight waves (one workgroup per CU, two waves per SIMD), an eighth of that per
+// wave.  Each wave keeps two steps of loads in flight; two waves per SIMD hide
+// each other's tail of a step better than one wave with a deeper register ring
+// (which measured slower at every depth).  A head group is HG query heads
 // that share one KV head (HG = G for G <= 4), so a tile is one page of one KV
 // head, K and V, read once for HG query heads.  Each wave streams its range,
 // keeping an online-softmax state that it closes whenever the range leaves a
@@ -13,25 +16,30 @@
 // workgroup to arrive merges them in a fixed order.  Split partials merged by
 // log-sum-exp follow the pages' decode design (commits by ViperEkura: o_part /
 // ml_part partials and their combine kernel); here the merge is fused into the
-// same launch and every wave gets the same number of pages.  K and V go
-// straight from HBM into registers with 16-byte loads: every element is used by
-// exactly one lane, so LDS staging would only add traffic.
+// same launch and every wave gets the same number of pages.
 //
-// Lane layout inside a wave (head_dim D, LPT = D / 16 lanes per token,
-// TPR = 64 / LPT tokens per round).  Lane l serves token slot l / LPT of a round
-// and holds 16 of the token's D channels: channels [8e, 8e + 8) and
-// [D/2 + 8e, D/2 + 8e + 8) with e = l % LPT.  Each half is one 16-byte load, so
-// one load instruction of the wave reads TPR half-rows of 128 (D=128) or 64
-// (D=64) contiguous bytes.  q.K partial dot products use v_dot2 on bf16 pairs,
-// then DPP adds inside the LPT-lane group.  Every lane keeps its own online
-// softmax state (running max m, sum l, 16-channel accumulators per head) for
-// the tokens of its slot; slots are merged once per piece.
+// Arithmetic on the matrix cores.  A wave consumes 16 tokens of one tile per
+// step.  Scores S^T[token][head] = K . q^T come from D/32
+// v_mfma_f32_16x16x32_bf16 (K rows are the A operand, q the B operand; query
+// heads beyond HG are zero columns).  K tiles are stored [D/8][P][8], so the A
+// operand of one MFMA (channels 32kk .. 32kk+31 of 16 tokens) is one
+// contiguous kilobyte: lane (g, r) reads channel block 4kk + g of token r.  The result leaves lane (g, r) = (l / 16,
+// l % 16) holding the scores of head r for tokens 4g .. 4g+3, which is exactly
+// the A-operand layout of v_mfma_f32_16x16x16_bf16 for P . V, so the softmax
+// weights never move between lanes.  V tiles are stored channel-major, so the
+// B operand (4 tokens of one channel per lane) is one 8-byte load.  The weights
+// enter the product as bf16 hi + lo parts (two MFMAs), keeping the p.V sum
+// accurate to about 2^-16 relative, while the softmax sums stay in fp32.  K and
+// V go straight from HBM into registers: every element is used once.
 //
-// The running max is updated lazily: the accumulators are rescaled only when
-// a score exceeds the stored max by more than 2^8 in the exp2 domain, so
-// weights stay below 256 and the rescale branch is rarely taken after the
-// first round.  Scores are kept in the log2 domain (sm_scale * log2 e folded
-// into one multiply) so every exponential is a single v_exp_f32.
+// Online softmax.  The running max of each head is shared by the four lanes
+// that hold its scores (a two-step cross-lane max per step) and updated lazily:
+// accumulators are rescaled only when a step's max exceeds the stored one by
+// more than 2^8 in the exp2 domain, so weights stay below 256 and the rescale
+// branch (wave-uniform) is rarely taken.  Scores are kept in the log2 domain
+// (sm_scale * log2 e folded into one multiply-add) so every exponential is a
+// single v_exp_f32.
+
 #include <math.h>
 
 #include "pkv_internal.h"
@@ -42,16 +50,6 @@ namespace {
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest un-rescaled weight
 constexpr float kMinusInf = -INFINITY;
 constexpr float kFloorMax = -1.0e30f;  // initial running max (finite: exp2 never sees inf - inf)
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -79,140 +77,103 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 // sc1 stores above: is visible at agent scope).  s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// DPP lane moves inside a row of 16 lanes.
-enum DppCtrl : int {
-  kQuadXor1 = 0xB1,      // quad_perm [1,0,3,2]
-  kQuadXor2 = 0x4E,      // quad_perm [2,3,0,1]
-  kRowHalfMirror = 0x141,
-  kRowRor4 = 0x124,
-  kRowRor8 = 0x128,
-};
+// MFMA operand vectors.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
-}
-
-// Sum over the LPT consecutive lanes that share a token (LPT = 4 or 8).
-template <int LPT>
-__device__ __forceinline__ float token_group_sum(float x) {
-  x += dpp_mov<kQuadXor1>(x);
-  x += dpp_mov<kQuadXor2>(x);
-  if constexpr (LPT == 8) x += dpp_mov<kRowHalfMirror>(x);
-  return x;
-}
-
-// Value of the lane `OFF` token slots away (a rotation inside the 16-lane row
-// for OFF < 16, an xor across rows otherwise).  Any pairing works for the
-// all-reduce below as long as every step pairs distinct slots.
-template <int OFF>
-__device__ __forceinline__ float slot_partner(float x) {
-  if constexpr (OFF == 4) return dpp_mov<kRowRor4>(x);
-  else if constexpr (OFF == 8) return dpp_mov<kRowRor8>(x);
-  else return __shfl_xor(x, OFF, kWave);
-}
-
-struct Round {
-  uint4 k0, k1, v0, v1;
+// One step's operands: 16 tokens of one (page, head) tile.
+template <int D>
+struct Step {
+  uint4 k[D / 32];  // K of token r, channels 8*(4kk + g) .. +8 (A of q.K, block kk)
+  uint2 v[D / 16];  // V^T: channel 16*nb + r, tokens 4g .. 4g+3 (B of p.V)
 };
 
 template <int D, int HG>
-struct SplitWave {
-  static constexpr int LPT = D / 16;
-  static constexpr int TPR = kWave / LPT;
-
-  float m[HG], l[HG], acc[HG][16];
-  uint32_t qw[HG][8];
+struct MfmaWave {
+  static constexpr int KB = D / 32;  // q.K MFMAs per step
+  static constexpr int VB = D / 16;  // p.V channel blocks
+  floatx4_t o[VB];                   // O[head 4g+i][channel 16*nb + r]
+  bf16x8_t qb[KB];                   // q^T operand (zero for heads >= HG)
+  float m, l;                        // head r: running max (log2 domain), partial sum
 
   __device__ __forceinline__ void init() {
 #pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      m[h] = kFloorMax;
-      l[h] = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[h][j] = 0.f;
-    }
+    for (int nb = 0; nb < VB; ++nb) o[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m = kFloorMax;
+    l = 0.f;
   }
 
-  // One round: TPR tokens, lane slot `tok`; `live` = this lane's token counts.
-  __device__ __forceinline__ void consume(const Round& rd, bool live, float scale_log2) {
-    float s[HG];
+  // Consume one step.  `live` = tokens of the step that count (uniform, 0..16);
+  // `g` = lane / 16; `bias` = 0 for heads < HG, -inf otherwise.
+  __device__ __forceinline__ void step(const Step<D>& st, int live, int g, float scale_log2,
+                                       float bias) {
+    floatx4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      float d = 0.f;
-      d = dot2_bf16(rd.k0.x, qw[h][0], d);
-      d = dot2_bf16(rd.k0.y, qw[h][1], d);
-      d = dot2_bf16(rd.k0.z, qw[h][2], d);
-      d = dot2_bf16(rd.k0.w, qw[h][3], d);
-      d = dot2_bf16(rd.k1.x, qw[h][4], d);
-      d = dot2_bf16(rd.k1.y, qw[h][5], d);
-      d = dot2_bf16(rd.k1.z, qw[h][6], d);
-      d = dot2_bf16(rd.k1.w, qw[h][7], d);
-      d = token_group_sum<LPT>(d);
-      s[h] = live ? d * scale_log2 : kMinusInf;
-    }
-    // Slots past the sequence end (or in a skipped page) may hold anything,
-    // NaN included: zero them so a zero weight really contributes zero.
-    const uint32_t keep = live ? 0xffffffffu : 0u;
-    uint4 v0 = rd.v0, v1 = rd.v1;
-    v0.x &= keep; v0.y &= keep; v0.z &= keep; v0.w &= keep;
-    v1.x &= keep; v1.y &= keep; v1.z &= keep; v1.w &= keep;
-    bool grow = false;
+    for (int kk = 0; kk < KB; ++kk)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, st.k[kk]),
+                                                   qb[kk], sc, 0, 0, 0);
+    float s[4];
 #pragma unroll
-    for (int h = 0; h < HG; ++h) grow |= s[h] > m[h] + kRescaleSlack;
-    if (grow) {
+    for (int i = 0; i < 4; ++i) s[i] = fmaf(sc[i], scale_log2, bias);
+    uint2 vv[VB];
 #pragma unroll
-      for (int h = 0; h < HG; ++h) {
-        const float mn = fmaxf(m[h], s[h]);
-        const float alpha = fast_exp2(m[h] - mn);
-        l[h] *= alpha;
+    for (int nb = 0; nb < VB; ++nb) vv[nb] = st.v[nb];
+    if (live < 16) {
+      // Tokens past the sequence end (or in a skipped page) may hold anything,
+      // NaN included: drop their scores and zero their V so that a zero weight
+      // contributes exactly zero.
+      const int t = 4 * g;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[h][j] *= alpha;
-        m[h] = mn;
+      for (int i = 0; i < 4; ++i)
+        if (t + i >= live) s[i] = kMinusInf;
+      const uint32_t m0 = (t + 0 < live ? 0x0000ffffu : 0u) | (t + 1 < live ? 0xffff0000u : 0u);
+      const uint32_t m1 = (t + 2 < live ? 0x0000ffffu : 0u) | (t + 3 < live ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int nb = 0; nb < VB; ++nb) {
+        vv[nb].x &= m0;
+        vv[nb].y &= m1;
       }
     }
-    float vf[16];
-    vf[0] = bf16_lo(v0.x); vf[1] = bf16_hi(v0.x); vf[2] = bf16_lo(v0.y); vf[3] = bf16_hi(v0.y);
-    vf[4] = bf16_lo(v0.z); vf[5] = bf16_hi(v0.z); vf[6] = bf16_lo(v0.w); vf[7] = bf16_hi(v0.w);
-    vf[8] = bf16_lo(v1.x); vf[9] = bf16_hi(v1.x); vf[10] = bf16_lo(v1.y); vf[11] = bf16_hi(v1.y);
-    vf[12] = bf16_lo(v1.z); vf[13] = bf16_hi(v1.z); vf[14] = bf16_lo(v1.w); vf[15] = bf16_hi(v1.w);
+    // Step max of head r over its 16 tokens (4 per lane, 4 lanes).
+    float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    pm = fmaxf(pm, __shfl_xor(pm, 16, kWave));
+    pm = fmaxf(pm, __shfl_xor(pm, 32, kWave));
+    if (__builtin_amdgcn_ballot_w64(pm > m + kRescaleSlack) != 0) {
+      const float mn = fmaxf(m, pm);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+      m = mn;
+      // Lane (0, i) holds head i's factor; O rows of head i sit in register i.
 #pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      const float p = fast_exp2(s[h] - m[h]);
-      l[h] += p;
+      for (int i = 0; i < HG; ++i) {
+        const float ai = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[h][j] = fmaf(p, vf[j], acc[h][j]);
-    }
-  }
-
-  template <int OFF>
-  __device__ __forceinline__ void merge_slot_step() {
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      const float mo = slot_partner<OFF>(m[h]);
-      const float lo = slot_partner<OFF>(l[h]);
-      const float mn = fmaxf(m[h], mo);
-      const float ca = fast_exp2(m[h] - mn);
-      const float cb = fast_exp2(mo - mn);
-      l[h] = l[h] * ca + lo * cb;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float ao = slot_partner<OFF>(acc[h][j]);
-        acc[h][j] = acc[h][j] * ca + ao * cb;
+        for (int nb = 0; nb < VB; ++nb) o[nb][i] *= ai;
       }
-      m[h] = mn;
     }
-  }
-
-  // All-reduce of the lane-local states over the TPR token slots of the wave.
-  __device__ __forceinline__ void merge_slots() {
-    if constexpr (LPT <= 4) merge_slot_step<4>();
-    merge_slot_step<8>();
-    merge_slot_step<16>();
-    merge_slot_step<32>();
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    // p = hi + lo, both bf16: the product keeps ~16 mantissa bits of p.
+    short4_t phi, plo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 h = (__bf16)p[i];
+      const float hf = (float)h;
+      const __bf16 lo = (__bf16)(p[i] - hf);
+      phi[i] = __builtin_bit_cast(short, h);
+      plo[i] = __builtin_bit_cast(short, lo);
+    }
+#pragma unroll
+    for (int nb = 0; nb < VB; ++nb) {
+      const short4_t vb = __builtin_bit_cast(short4_t, vv[nb]);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, o[nb], 0, 0, 0);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, o[nb], 0, 0, 0);
+    }
   }
 };
-
 
 // Online-softmax combine of (m, l, value) triples in the log2 domain.
 struct Combine {
@@ -229,10 +190,8 @@ struct Combine {
 
 template <int D, int HG>
 __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
-  using W = SplitWave<D, HG>;
-  constexpr int LPT = W::LPT;
-  constexpr int TPR = W::TPR;
-  static_assert(HG * D <= kGroupThreads, "one output channel per thread");
+  constexpr int kStages = 2;  // register ring: steps in flight per wave
+  constexpr int kOut = (HG * D + kGroupThreads - 1) / kGroupThreads;  // outputs per thread
 
   // Pieces that leave a wave unfinished: slot 0 = the wave's first piece,
   // slot 1 = its last piece (every other piece is a whole segment).
@@ -240,6 +199,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   __shared__ float s_m[kWavesPerGroup][2][HG];
   __shared__ float s_l[kWavesPerGroup][2][HG];
   __shared__ int s_seg[kWavesPerGroup][2];
+  __shared__ float s_out[kWavesPerGroup][HG][D];  // per-wave transpose of finished rows
   __shared__ int s_glob[2];   // segments this workgroup left as global partials
   __shared__ int s_merge[2];  // of those, the ones this workgroup merges
 
@@ -268,39 +228,41 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   if (tid < 2) s_glob[tid] = -1;
 
   const WaveRange rng = a.waves[grp * kWavesPerGroup + w];
-  const int tok = lane / LPT;
-  const int e = lane % LPT;
-  const int c0 = e * 8;  // first channel of the lane's low half; high half at D/2 + c0
-  const size_t tile = (size_t)a.page_size * D;               // elements per (page, head) tile
-  const uint32_t lane_boff = (uint32_t)(tok * D + c0) * 2;  // lane's byte offset inside a round
+
+  const int g4 = lane >> 4;   // lane group: tokens 4*g4 .. 4*g4+3 of a step
+  const int r16 = lane & 15;  // head of the scores / channel of the outputs
+  const float bias = r16 < HG ? 0.f : kMinusInf;
+  const int P = a.page_size;
+  const int log2_s = a.log2_steps;  // steps of 16 tokens per page
+  const size_t tile_b = (size_t)P * D * 2;  // bytes of one (page, head) tile
+  // Lane byte offsets inside a step: K block g4, token r16; V^T channel r16, tokens 4*g4.
+  const uint32_t k_boff = (uint32_t)(g4 * P + r16) * 16;
+  const uint32_t v_boff = (uint32_t)(r16 * P + 4 * g4) * 2;
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
-  const int P = a.page_size;
-  const int log2_r = a.log2_rounds;
   int err = 0;
 
   int b = rng.b, u = rng.u, p = rng.p, left = rng.count, piece = 0;
-  W st;
+  int ip0 = rng.ip0, n = rng.pages, L = rng.len;  // request b (reloaded when b changes)
+  MfmaWave<D, HG> st;
   while (left > 0) {  // one piece = the part of segment (b, u) inside this wave's range
-    const int ip0 = a.kv_indptr[b];
-    const int n = a.kv_indptr[b + 1] - ip0;
-    const int L = a.seq_lens[b];
     const int len = min(left, n - p);
     if (len <= 0) break;  // only reachable with metadata that does not match kv_indptr
     const int hq0 = u * HG;
     const int g = hq0 / G;
 
     st.init();
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
+    {
+      // q^T operand: lane (g4, r16) supplies head r16, channels 8*(4kk + g4) .. +8.
       const uint4* qp = reinterpret_cast<const uint4*>(
-          a.q + ((size_t)b * Hq + hq0 + h) * D + c0);
-      const uint4 lo = qp[0];
-      const uint4 hi = qp[D / 16];
-      st.qw[h][0] = lo.x; st.qw[h][1] = lo.y; st.qw[h][2] = lo.z; st.qw[h][3] = lo.w;
-      st.qw[h][4] = hi.x; st.qw[h][5] = hi.y; st.qw[h][6] = hi.z; st.qw[h][7] = hi.w;
+          a.q + ((size_t)b * Hq + hq0 + (r16 < HG ? r16 : 0)) * D + g4 * 8);
+#pragma unroll
+      for (int kk = 0; kk < MfmaWave<D, HG>::KB; ++kk) {
+        const uint4 w4 = r16 < HG ? qp[4 * kk] : make_uint4(0, 0, 0, 0);
+        st.qb[kk] = __builtin_bit_cast(bf16x8_t, w4);
+      }
     }
-    const size_t head_off = (size_t)g * tile;
+    const size_t head_b = (size_t)g * tile_b;
 
     for (int jb = 0; jb < len; jb += kWave) {
       const int nb = min(kWave, len - jb);
@@ -317,96 +279,90 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
           else vpage = pid;
         }
       }
-      const int nr = nb << log2_r;  // rounds in this block, >= 1
+      const int ns = nb << log2_s;  // steps in this block, >= 1
 
-      // Round rr of the block: page id (uniform), first token, loads.  Rounds
-      // past the block re-read its last round (a cache hit) and are never
-      // consumed, so the issue sequence has no data-dependent branch.
-      auto issue = [&](int rr, Round& rd) {
-        const int rc = rr < nr ? rr : nr - 1;
-        const int j = rc >> log2_r;
-        const int r = rc & ((1 << log2_r) - 1);
-        const int pid = __builtin_amdgcn_readlane(vpage, j);
-        const size_t off = ((size_t)(pid < 0 ? 0 : pid) * a.num_kv_heads * tile + head_off +
-                            (size_t)r * TPR * D) * 2;
-        const char* kp = kbase + off + lane_boff;
-        const char* vp = vbase + off + lane_boff;
-        rd.k0 = *reinterpret_cast<const uint4*>(kp);
-        rd.k1 = *reinterpret_cast<const uint4*>(kp + D);
-        rd.v0 = *reinterpret_cast<const uint4*>(vp);
-        rd.v1 = *reinterpret_cast<const uint4*>(vp + D);
+      // Step j of the block: page id (uniform) and loads.  Steps past the block
+      // re-read its last step (a cache hit) and are never consumed, so the
+      // issue sequence has no data-dependent branch.
+      auto issue = [&](int j, Step<D>& sd) {
+        const int jc = j < ns ? j : ns - 1;
+        const int pg = jc >> log2_s;
+        const int sub = jc & ((1 << log2_s) - 1);
+        const int pid = __builtin_amdgcn_readlane(vpage, pg);
+        const size_t base = (size_t)(pid < 0 ? 0 : pid) * a.num_kv_heads * tile_b + head_b;
+        const char* kp = kbase + base + (size_t)sub * 16 * 16 + k_boff;
+        const char* vp = vbase + base + (size_t)sub * 16 * 2 + v_boff;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+          sd.k[kk] = *reinterpret_cast<const uint4*>(kp + (size_t)kk * 4 * P * 16);
+#pragma unroll
+        for (int vb = 0; vb < D / 16; ++vb)
+          sd.v[vb] = *reinterpret_cast<const uint2*>(vp + (size_t)vb * 16 * P * 2);
       };
-      auto consume = [&](int rr, const Round& rd) {
-        const int j = rr >> log2_r;
-        const int r = rr & ((1 << log2_r) - 1);
-        const int pid = __builtin_amdgcn_readlane(vpage, j);
-        const int t0 = (p + jb + j) * P + r * TPR;
-        const bool live = pid >= 0 && t0 + tok < L;
-        st.consume(rd, live, a.scale_log2);
+      auto consume = [&](int j, const Step<D>& sd) {
+        const int pg = j >> log2_s;
+        const int sub = j & ((1 << log2_s) - 1);
+        const int pid = __builtin_amdgcn_readlane(vpage, pg);
+        const int t0 = (p + jb + pg) * P + sub * 16;
+        const int live = pid < 0 ? 0 : min(16, max(0, L - t0));
+        st.step(sd, live, g4, a.scale_log2, bias);
       };
 
-      // Two stages of two rounds each: while one stage is consumed the other
-      // is in flight.
-      Round A0, A1, B0, B1;
-      issue(0, A0);
-      issue(1, A1);
-      for (int rr = 0; rr < nr; rr += 4) {
-        issue(rr + 2, B0);
-        issue(rr + 3, B1);
-        consume(rr, A0);
-        if (rr + 1 < nr) consume(rr + 1, A1);
-        issue(rr + 4, A0);
-        issue(rr + 5, A1);
-        if (rr + 2 < nr) consume(rr + 2, B0);
-        if (rr + 3 < nr) consume(rr + 3, B1);
+      // A ring of kStages steps: while one is consumed, kStages - 1 are in flight.
+      Step<D> ring[kStages];
+#pragma unroll
+      for (int i = 0; i < kStages - 1; ++i) issue(i, ring[i]);
+      for (int j = 0; j < ns; j += kStages) {
+#pragma unroll
+        for (int i = 0; i < kStages; ++i) {
+          issue(j + i + kStages - 1, ring[(i + kStages - 1) % kStages]);
+          if (j + i < ns) consume(j + i, ring[i]);
+        }
       }
     }
 
-    st.merge_slots();
+    // Close the piece: total sum of each head over its four lanes; lane (0, i)
+    // then holds head i's max and sum, and lanes 0..15 hold its output rows.
+    float lt = st.l + __shfl_xor(st.l, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
     const int seg = b * U + u;
     if (p == 0 && len == n) {
-      // The whole segment lies in this wave: write its rows.  Lane slot h < HG
-      // writes head h (after the merge every slot holds the totals).
-      float o[16];
-      float lv = st.l[0];
+      // The whole segment lies in this wave: normalise its rows, transpose
+      // them through LDS and write 8 channels (16 bytes) per lane.
 #pragma unroll
-      for (int j = 0; j < 16; ++j) o[j] = st.acc[0][j];
+      for (int i = 0; i < HG; ++i) {
+        const float li = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt), i));
+        const float inv = li > 0.f ? 1.0f / li : 0.f;
+        if (g4 == 0) {
 #pragma unroll
-      for (int h = 1; h < HG; ++h) {
-        if (tok == h) {
-          lv = st.l[h];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) o[j] = st.acc[h][j];
+          for (int vb = 0; vb < MfmaWave<D, HG>::VB; ++vb) s_out[w][i][16 * vb + r16] = st.o[vb][i] * inv;
         }
       }
-      if (tok < HG) {
-        const float inv = lv > 0.f ? 1.0f / lv : 0.f;
-        uint16_t* op = a.out + ((size_t)b * Hq + hq0 + tok) * D + c0;
-        *reinterpret_cast<uint4*>(op) =
-            make_uint4(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
-                       pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv));
-        *reinterpret_cast<uint4*>(op + D / 2) =
-            make_uint4(pack_bf16x2(o[8] * inv, o[9] * inv), pack_bf16x2(o[10] * inv, o[11] * inv),
-                       pack_bf16x2(o[12] * inv, o[13] * inv),
-                       pack_bf16x2(o[14] * inv, o[15] * inv));
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes land first
+      if (lane < HG * (D / 8)) {
+        const int i = lane / (D / 8);
+        const int c8 = (lane - i * (D / 8)) * 8;
+        const float4 x0 = *reinterpret_cast<const float4*>(&s_out[w][i][c8]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&s_out[w][i][c8 + 4]);
+        *reinterpret_cast<uint4*>(a.out + ((size_t)b * Hq + hq0 + i) * D + c8) =
+            make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
+                       pack_bf16x2(x1.z, x1.w));
       }
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before s_out is reused
     } else {
       const int slot = piece == 0 ? 0 : 1;
-      if (tok == 0) {
 #pragma unroll
-        for (int h = 0; h < HG; ++h) {
+      for (int i = 0; i < HG; ++i) {
+        if (g4 == 0) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            s_acc[w][slot][h][c0 + j] = st.acc[h][j];
-            s_acc[w][slot][h][D / 2 + c0 + j] = st.acc[h][8 + j];
-          }
-          if (e == 0) {
-            s_m[w][slot][h] = st.m[h];
-            s_l[w][slot][h] = st.l[h];
-          }
+          for (int vb = 0; vb < MfmaWave<D, HG>::VB; ++vb) s_acc[w][slot][i][16 * vb + r16] = st.o[vb][i];
         }
-        if (e == 0) s_seg[w][slot] = seg;
+        if (lane == i) {
+          s_m[w][slot][i] = st.m;
+          s_l[w][slot][i] = lt;
+        }
       }
+      if (lane == 0) s_seg[w][slot] = seg;
     }
     left -= len;
     ++piece;
@@ -415,6 +371,9 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       if (++u == U) {
         u = 0;
         do { ++b; } while (b < a.batch - 1 && a.kv_indptr[b + 1] == a.kv_indptr[b]);
+        ip0 = a.kv_indptr[b];
+        n = a.kv_indptr[b + 1] - ip0;
+        L = max(a.seq_lens[b], 0);
       }
     }
   }
@@ -422,12 +381,13 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   // Merge the pieces in LDS segment by segment (a segment's pieces are
-  // consecutive in wave order).  Thread t owns channel t % D of head t / D.
+  // consecutive in wave order).  Thread t owns outputs t, t + 256, ... of the
+  // HG x D block (head o / D, channel o % D).
   const int2 gsegs = a.group_segs[grp];
-  const bool act = tid < HG * D;
-  const int h = tid / D;
-  const int c = tid - h * D;
-  auto emit = [&](int sgm, const Combine& cb) {
+  auto emit = [&](int sgm, const Combine& cb, int o) {
+    const int h = o / D;
+    const int c = o - h * D;
+    const bool act = o < HG * D;
     const int eb = sgm / U;
     const int hq = (sgm - eb * U) * HG + h;
     const int2 sg = a.seg_groups[sgm];
@@ -445,20 +405,37 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     }
   };
   {
-    int cur = -1;
-    Combine cb;
-#pragma unroll 1
-    for (int k = 0; k < 2 * kWavesPerGroup; ++k) {
-      const int sgm = s_seg[k >> 1][k & 1];
-      if (sgm < 0) continue;
-      if (sgm != cur) {
-        if (cur >= 0) emit(cur, cb);
-        cur = sgm;
-        cb = Combine();
+    constexpr int NS = 2 * kWavesPerGroup;
+    int segs[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) segs[k] = s_seg[k >> 1][k & 1];
+#pragma unroll
+    for (int oi = 0; oi < kOut; ++oi) {
+      const int o = tid + oi * kGroupThreads;
+      const int h = o < HG * D ? o / D : 0;
+      const int c = o < HG * D ? o - h * D : 0;
+      float mk[NS], lk[NS], vk[NS];
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        mk[k] = s_m[k >> 1][k & 1][h];
+        lk[k] = s_l[k >> 1][k & 1][h];
+        vk[k] = s_acc[k >> 1][k & 1][h][c];
       }
-      if (act) cb.add(s_m[k >> 1][k & 1][h], s_l[k >> 1][k & 1][h], s_acc[k >> 1][k & 1][h][c]);
+      int cur = -1;
+      Combine cb;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int sgm = segs[k];
+        if (sgm < 0) continue;
+        if (sgm != cur) {
+          if (cur >= 0) emit(cur, cb, o);
+          cur = sgm;
+          cb = Combine();
+        }
+        cb.add(mk[k], lk[k], vk[k]);
+      }
+      if (cur >= 0) emit(cur, cb, o);
     }
-    if (cur >= 0) emit(cur, cb);
   }
 
   // Cross-workgroup merge: publish the partials, count arrivals, and let the
@@ -479,24 +456,68 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
+  // Merge every segment this workgroup arrived last for.  All loads of a round
+  // (both segments, every output of the thread, 16 partials each) are issued
+  // before any is used, so a merge costs about one memory round trip.
+  const int msg[2] = {s_merge[0], s_merge[1]};
+  if (msg[0] >= 0 || msg[1] >= 0) {
+    constexpr int kUnroll = 16;
+    int2 sg[2];
+    int slot0[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      sg[k] = msg[k] >= 0 ? a.seg_groups[msg[k]] : make_int2(0, -1);
+      // Workgroup j > sg.x holds the segment as its first segment (slot 0); the
+      // first workgroup holds it in slot 0 only if the segment starts its range.
+      slot0[k] = msg[k] >= 0 && a.group_segs[sg[k].x].x != msg[k] ? 1 : 0;
+    }
+    const int rounds = max(sg[0].y - sg[0].x, sg[1].y - sg[1].x) / kUnroll + 1;
+    Combine cb[2][kOut];
 #pragma unroll 1
-  for (int k = 0; k < 2; ++k) {
-    const int sgm = s_merge[k];
-    if (sgm < 0) continue;
-    const int2 sg = a.seg_groups[sgm];
-    Combine cb;
-    for (int j = sg.x; j <= sg.y; ++j) {
-      const int slot = a.group_segs[j].x == sgm ? 0 : 1;
-      const size_t row = (size_t)(2 * j + slot) * HG + h;
-      if (act) cb.add(load_coherent(&a.lse[row]), 1.0f, load_coherent(&a.opart[row * D + c]));
+    for (int rd = 0; rd < rounds; ++rd) {
+      float ls[2][kOut][kUnroll], ov[2][kOut][kUnroll];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+#pragma unroll
+        for (int oi = 0; oi < kOut; ++oi) {
+          const int o = tid + oi * kGroupThreads;
+          const bool act = msg[k] >= 0 && o < HG * D;
+          const int h = o < HG * D ? o / D : 0;
+          const int c = o - h * D;
+#pragma unroll
+          for (int q = 0; q < kUnroll; ++q) {
+            const int j = min(sg[k].x + rd * kUnroll + q, sg[k].y);
+            const size_t row = (size_t)(2 * j + (j == sg[k].x ? slot0[k] : 0)) * HG + h;
+            ls[k][oi][q] = act ? load_coherent(&a.lse[row]) : kMinusInf;
+            ov[k][oi][q] = act ? load_coherent(&a.opart[row * D + c]) : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int oi = 0; oi < kOut; ++oi)
+#pragma unroll
+          for (int q = 0; q < kUnroll; ++q)
+            if (sg[k].x + rd * kUnroll + q <= sg[k].y) cb[k][oi].add(ls[k][oi][q], 1.0f, ov[k][oi][q]);
     }
-    const int eb = sgm / U;
-    const int hq = (sgm - eb * U) * HG + h;
-    if (act) {
-      const float val = cb.den > 0.f ? cb.num / cb.den : 0.f;
-      a.out[((size_t)eb * Hq + hq) * D + c] = (uint16_t)bf16_rne(val);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (msg[k] < 0) continue;
+      const int eb = msg[k] / U;
+#pragma unroll
+      for (int oi = 0; oi < kOut; ++oi) {
+        const int o = tid + oi * kGroupThreads;
+        if (o >= HG * D) continue;
+        const int h = o / D;
+        const int c = o - h * D;
+        const int hq = (msg[k] - eb * U) * HG + h;
+        const float val = cb[k][oi].den > 0.f ? cb[k][oi].num / cb[k][oi].den : 0.f;
+        a.out[((size_t)eb * Hq + hq) * D + c] = (uint16_t)bf16_rne(val);
+      }
+      if (tid == 0)
+        __hip_atomic_store(&a.counters[msg[k]], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == 0) __hip_atomic_store(&a.counters[sgm], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

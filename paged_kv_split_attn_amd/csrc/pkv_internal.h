@@ -11,7 +11,7 @@
 namespace pkv {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerGroup = 8;                      // waves of one decode workgroup
+constexpr int kWavesPerGroup = PKV_WAVES_PER_WORKGROUP;  // waves of one decode workgroup (two per SIMD)
 constexpr int kGroupThreads = kWavesPerGroup * kWave;  // 512
 constexpr int kDefaultMinTiles = 8;
 constexpr int kMaxBatch = 65536;
@@ -36,8 +36,13 @@ enum ErrorBit : int {
 
 // Range of one wave: tiles of request b, head group u, pages p, p+1, ... and
 // on into the following (request, head group) segments, `count` tiles in all.
+// The rest describes request b, so the wave can start loading at once.
 struct alignas(16) WaveRange {
   int32_t b, u, p, count;
+  int32_t ip0;    // kv_indptr[b]
+  int32_t pages;  // pages of request b
+  int32_t len;    // tokens of request b
+  int32_t pad;
 };
 
 // Byte offsets of the workspace sections; every section is 256-byte aligned.
@@ -95,7 +100,7 @@ struct DecodeArgs {
   uint16_t* out;  // [batch][Hq][D] bf16
   int32_t num_indices, num_pages, num_q_heads, num_kv_heads, page_size, batch;
   int32_t units;        // head groups per request
-  int32_t log2_rounds;  // log2(page_size / tokens per round); tokens per round = 1024 / head_dim
+  int32_t log2_steps;   // log2(page_size / 16): steps of 16 tokens per page
   float scale_log2;     // sm_scale * log2(e)
 };
 

@@ -49,6 +49,7 @@ __device__ __forceinline__ int pages_of(int len, int P) { return len > 0 ? (len 
 
 struct Locator {
   const int32_t* ip;  // page prefix sums (LDS copy or global)
+  const int32_t* seq_lens;
   int batch, units;
   // (request, head group, page) of tile t < T: the request is the largest b
   // with ip[b] * U <= t (requests without pages have empty ranges).
@@ -67,6 +68,10 @@ struct Locator {
     w.u = u;
     w.p = (int)(r - (long long)u * n);
     w.count = count;
+    w.ip0 = ip[lo];
+    w.pages = n;
+    w.len = max(seq_lens[lo], 0);
+    w.pad = 0;
     return w;
   }
 };
@@ -116,14 +121,14 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
       W = (int)(want < a.groups ? want : a.groups);
     }
   }
-  Locator loc{in_lds ? s_ip : a.kv_indptr, a.batch, U};
+  Locator loc{in_lds ? s_ip : a.kv_indptr, a.seq_lens, a.batch, U};
 
   // Phase 2: every wave's range.  Group i covers [i*T/W, (i+1)*T/W); its wave
   // w covers the w-th of kWavesPerGroup equal parts.
   for (int gw = tid; gw < a.groups * kWavesPerGroup; gw += kMetaThreads) {
     const int i = gw / kWavesPerGroup;
     const int w = gw - i * kWavesPerGroup;
-    WaveRange r{0, 0, 0, 0};
+    WaveRange r{0, 0, 0, 0, 0, 0, 0, 0};
     if (i < W) {
       const long long g0 = (long long)i * T / W, g1 = (long long)(i + 1) * T / W;
       const long long len = g1 - g0;
@@ -175,7 +180,10 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
   }
 }
 
-// One thread per 16-byte chunk of (request, KV head, K or V) rows.
+// One thread per 8-channel chunk of (request, KV head, K or V) rows.  A K tile
+// keeps 8-channel blocks of each token together ([D/8][P][8]): one 16-byte
+// store per chunk.  V tiles are channel-major ([D][P]), so a V row is a column
+// of its tile: eight 2-byte stores, page_size apart.
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   const int chunks = a.head_dim / 8;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -193,13 +201,22 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   if (slot < 0 || slot >= a.num_indices) return;
   const int page = a.kv_indices[slot];
   if (page < 0 || page >= a.num_pages) return;
-  const uint16_t* src = which ? a.v_new : a.k_new;
-  uint16_t* dst = which ? a.v : a.k;
   const size_t src_off = ((size_t)b * a.num_kv_heads + h) * a.head_dim + (size_t)c * 8;
-  const size_t dst_off =
-      (((size_t)page * a.num_kv_heads + h) * a.page_size + pos % a.page_size) * a.head_dim +
-      (size_t)c * 8;
-  *reinterpret_cast<uint4*>(dst + dst_off) = *reinterpret_cast<const uint4*>(src + src_off);
+  const size_t tile = (((size_t)page * a.num_kv_heads + h) * a.page_size) * a.head_dim;
+  const int off = pos % a.page_size;
+  if (which == 0) {
+    *reinterpret_cast<uint4*>(a.k + tile + ((size_t)c * a.page_size + off) * 8) =
+        *reinterpret_cast<const uint4*>(a.k_new + src_off);
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(a.v_new + src_off);
+    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+    uint16_t* col = a.v + tile + (size_t)c * 8 * a.page_size + off;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      col[(size_t)(2 * j) * a.page_size] = (uint16_t)(words[j] & 0xffffu);
+      col[(size_t)(2 * j + 1) * a.page_size] = (uint16_t)(words[j] >> 16);
+    }
+  }
 }
 
 }  // namespace

@@ -65,7 +65,7 @@ def test_workspace_bytes(lib):
     n = pkv.pkv_workspace_bytes(d)
     groups, hg, segs = 256, 4, 16 * 8
     expect = 256  # header
-    for sz in (16 * groups * 8, 8 * groups, 8 * segs, 4 * segs, 4 * 2 * groups * hg,
+    for sz in (32 * groups * pkv.WAVES_PER_GROUP, 8 * groups, 8 * segs, 4 * segs, 4 * 2 * groups * hg,
                4 * 2 * groups * hg * 128):
         expect += (sz + 255) // 256 * 256
     assert n == expect
@@ -122,3 +122,27 @@ def test_binding_requires_gpu_tensors(lib):
     with pytest.raises(ValueError):
         pkv.pkv_build_metadata(d, torch.zeros(4, dtype=torch.int32), 0,
                                torch.zeros(5, dtype=torch.int32), torch.zeros(10, dtype=torch.uint8))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # no fallback: every entry point needs the HIP library and says so when it is absent
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import paged_kv_split_attn_amd as p\n"
+            "try:\n"
+            "    p.pkv_version()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    env = dict(os.environ, PKV_LIBRARY=str(tmp_path / "absent" / "libpkv.so"))
+    r = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert "raised: libpkv.so not found" in r.stdout
+
+
+def test_header_wave_count_matches_library(lib):
+    # the workspace holds one 32-byte range per wave of every workgroup
+    one = pkv.pkv_workspace_bytes(_desc(num_workgroups=1024))
+    two = pkv.pkv_workspace_bytes(_desc(num_workgroups=2048))
+    per_group = 32 * pkv.WAVES_PER_GROUP + 8 + 4 * 2 * 4 * (1 + 128)
+    assert two - one == 1024 * per_group

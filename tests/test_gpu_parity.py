@@ -83,8 +83,8 @@ def test_append_bit_exact(which):
     ip = oracle.kv_indptr(batch.seq_lens, batch.P)
     k_ref, v_ref = oracle.append_kv(batch.k_pool, batch.v_pool, batch.k_new, batch.v_new, ip,
                                     batch.kv_indices, batch.seq_lens, batch.P)
-    k = run.t["k_pool"].cpu().numpy().view(np.uint16)
-    v = run.t["v_pool"].cpu().numpy().view(np.uint16)
+    k = W.k_pool_token_major(run.t["k_pool"].cpu().numpy().view(np.uint16))
+    v = W.v_pool_token_major(run.t["v_pool"].cpu().numpy().view(np.uint16))
     assert np.array_equal(k, k_ref)
     assert np.array_equal(v, v_ref)
 

@@ -44,6 +44,10 @@ __all__ = [
     "permute_pool",
     "identity_layout",
     "to_device",
+    "v_pool_channel_major",
+    "v_pool_token_major",
+    "k_pool_blocked",
+    "k_pool_token_major",
 ]
 
 
@@ -349,11 +353,35 @@ def identity_layout(batch: DecodeBatch) -> DecodeBatch:
     return out
 
 
+def v_pool_channel_major(v_pool: np.ndarray) -> np.ndarray:
+    """[pages][Hkv][P][D] -> [pages][Hkv][D][P]: the device layout of V tiles."""
+    return np.ascontiguousarray(np.swapaxes(v_pool, 2, 3))
+
+
+def v_pool_token_major(v_dev: np.ndarray) -> np.ndarray:
+    """Inverse of v_pool_channel_major."""
+    return np.ascontiguousarray(np.swapaxes(v_dev, 2, 3))
+
+
+def k_pool_blocked(k_pool: np.ndarray) -> np.ndarray:
+    """[pages][Hkv][P][D] -> [pages][Hkv][D/8][P][8]: the device layout of K tiles."""
+    n, h, p, d = k_pool.shape
+    return np.ascontiguousarray(k_pool.reshape(n, h, p, d // 8, 8).transpose(0, 1, 3, 2, 4))
+
+
+def k_pool_token_major(k_dev: np.ndarray) -> np.ndarray:
+    """Inverse of k_pool_blocked."""
+    n, h, d8, p, e = k_dev.shape
+    return np.ascontiguousarray(k_dev.transpose(0, 1, 3, 2, 4).reshape(n, h, p, d8 * e))
+
+
 def to_device(batch: DecodeBatch, device="cuda:0") -> dict:
     """Copy a batch's arrays to device tensors (bf16 bits as int16, indices as int32).
 
     Returns a dict with q, k_pool, v_pool, seq_lens, kv_indices and, for an
-    append batch, k_new and v_new.  Data movement only.
+    append batch, k_new and v_new.  The batch keeps K and V token-major; the
+    device copies use the library's tile layouts (K [D/8][P][8], V [D][P] inside
+    each (page, head) tile).  Data movement only.
     """
     import torch
 
@@ -362,8 +390,8 @@ def to_device(batch: DecodeBatch, device="cuda:0") -> dict:
 
     d = {
         "q": bits(batch.q),
-        "k_pool": bits(batch.k_pool),
-        "v_pool": bits(batch.v_pool),
+        "k_pool": bits(k_pool_blocked(batch.k_pool)),
+        "v_pool": bits(v_pool_channel_major(batch.v_pool)),
         "seq_lens": torch.from_numpy(batch.seq_lens.astype(np.int32)).to(device),
         "kv_indices": torch.from_numpy(batch.kv_indices.astype(np.int32)).to(device),
     }
