@@ -25,10 +25,8 @@ bool ws_layout(const pkv_desc& d, int groups, WsLayout* out) {
   off = align256(off + sizeof(int32_t) * kHdrWords);
   L.waves = off;
   off = align256(off + sizeof(WaveRange) * (size_t)groups * kWavesPerGroup);
-  L.group_segs = off;
-  off = align256(off + sizeof(int2) * (size_t)groups);
-  L.seg_groups = off;
-  off = align256(off + sizeof(int2) * (size_t)L.segments);
+  L.ginfo = off;
+  off = align256(off + sizeof(GroupInfo) * (size_t)groups);
   L.counters = off;
   off = align256(off + sizeof(int32_t) * (size_t)L.segments);
   L.lse = off;
@@ -134,8 +132,7 @@ int pkv_build_metadata(const pkv_desc* desc, const int32_t* seq_lens, int32_t ba
   a.kv_indptr = kv_indptr;
   a.hdr = at<int32_t>(workspace, L.hdr);
   a.waves = at<WaveRange>(workspace, L.waves);
-  a.group_segs = at<int2>(workspace, L.group_segs);
-  a.seg_groups = at<int2>(workspace, L.seg_groups);
+  a.ginfo = at<GroupInfo>(workspace, L.ginfo);
   a.counters = at<int32_t>(workspace, L.counters);
   a.batch = batch;
   a.page_size = desc->page_size;
@@ -196,8 +193,7 @@ int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
   d.seq_lens = seq_lens;
   d.hdr = at<int32_t>(workspace, L.hdr);
   d.waves = at<WaveRange>(workspace, L.waves);
-  d.group_segs = at<int2>(workspace, L.group_segs);
-  d.seg_groups = at<int2>(workspace, L.seg_groups);
+  d.ginfo = at<GroupInfo>(workspace, L.ginfo);
   d.counters = at<int32_t>(workspace, L.counters);
   d.lse = at<float>(workspace, L.lse);
   d.opart = at<float>(workspace, L.opart);

@@ -64,18 +64,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
-// Stores and loads coherent across the XCDs' L2 caches (agent scope), used for
-// the partials one workgroup hands to another.  They compile to sc1 accesses:
-// no L2 write-back or invalidate is needed around them.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // Wait until every earlier store of the wave has been acknowledged (for the
-// sc1 stores above: is visible at agent scope).  s_waitcnt vmcnt(0).
+// device-coherent partial stores of the epilogue: is visible to every XCD).
+// s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Re-reads a kernel argument from the argument segment where it is used, so
+// that pointers needed only after the streaming loop do not hold scalar
+// registers through it.
+// A pointer that every lane holds the same value of, moved to scalar
+// registers (readfirstlane works on 32 bits: both halves are read).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Pointers the epilogue needs, parked in LDS at the start so that they do
+// not hold scalar registers through the streaming loop.
+struct EpiloguePtrs {
+  int32_t* hdr;
+  int32_t* counters;
+  float* lse;
+  float* opart;
+};
 
 // MFMA operand vectors.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -175,10 +189,15 @@ struct MfmaWave {
   }
 };
 
-// Online-softmax combine of (m, l, value) triples in the log2 domain.
-struct Combine {
-  float m = kFloorMax, den = 0.f, num = 0.f;
-  __device__ __forceinline__ void add(float mk, float lk, float vk) {
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// Online-softmax combine of (m, l, values) in the log2 domain, four channels
+// that share m and l.
+struct Combine4 {
+  float m = kFloorMax, den = 0.f;
+  f4 num = {0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ void add(float mk, float lk, f4 vk) {
     const float mn = fmaxf(m, mk);
     const float ca = fast_exp2(m - mn);
     const float cb = fast_exp2(mk - mn);
@@ -188,6 +207,13 @@ struct Combine {
   }
 };
 
+// Buffer resource word 3 for raw (untyped) buffer accesses on gfx950, and the
+// cache-policy bit that makes a buffer access coherent at device scope (sc1):
+// the partials one workgroup hands to another on a different XCD.  Buffer
+// accesses outside the resource's size read 0 and write nothing.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCoherent = 16;
+
 template <int D, int HG>
 __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   constexpr int kStages = 2;  // register ring: steps in flight per wave
@@ -195,13 +221,15 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
 
   // Pieces that leave a wave unfinished: slot 0 = the wave's first piece,
   // slot 1 = its last piece (every other piece is a whole segment).
-  __shared__ float s_acc[kWavesPerGroup][2][HG][D];
+  __shared__ __align__(16) float s_acc[kWavesPerGroup][2][HG][D];
   __shared__ float s_m[kWavesPerGroup][2][HG];
   __shared__ float s_l[kWavesPerGroup][2][HG];
   __shared__ int s_seg[kWavesPerGroup][2];
-  __shared__ float s_out[kWavesPerGroup][HG][D];  // per-wave transpose of finished rows
+  __shared__ __align__(16) float s_out[kWavesPerGroup][HG][D];  // per-wave transpose of finished rows
   __shared__ int s_glob[2];   // segments this workgroup left as global partials
   __shared__ int s_merge[2];  // of those, the ones this workgroup merges
+  __shared__ GroupInfo s_gi;  // the workgroup's merge record, for the epilogue
+  __shared__ EpiloguePtrs s_ptr;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -211,23 +239,23 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int Hq = a.num_q_heads;
 
-  if (grp == 0) {
-    // Requests without tokens get zero rows (no tile covers them).
-    for (int b = tid; b < a.batch; b += kGroupThreads) {
-      if (a.kv_indptr[b + 1] == a.kv_indptr[b]) {
-        uint4* row = reinterpret_cast<uint4*>(a.out + (size_t)b * Hq * D);
-        for (int i = 0; i < Hq * D / 8; ++i) row[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  // The plan size, this wave's range and the workgroup's merge record are
+  // fetched together (the test reads all three, so no load waits for another):
+  // the first K/V loads wait on them, and the merges at the end need nothing
+  // else from the plan.
+  const int ngroups = a.hdr[kHdrGroups];
+  const WaveRange rng = a.waves[grp * kWavesPerGroup + w];
+  const GroupInfo gi0 = a.ginfo[grp];
+  if ((grp >= ngroups) | (rng.count < 0) | (gi0.seg[0] < -1)) return;  // uniform over the workgroup
+  if (tid == 0) {  // parked in LDS until the epilogue
+    s_gi = gi0;
+    s_ptr = EpiloguePtrs{a.hdr, a.counters, a.lse, a.opart};
   }
-  if (grp >= a.hdr[kHdrGroups]) return;  // uniform over the workgroup
   if (lane == 0) {
     s_seg[w][0] = -1;
     s_seg[w][1] = -1;
   }
   if (tid < 2) s_glob[tid] = -1;
-
-  const WaveRange rng = a.waves[grp * kWavesPerGroup + w];
 
   const int g4 = lane >> 4;   // lane group: tokens 4*g4 .. 4*g4+3 of a step
   const int r16 = lane & 15;  // head of the scores / channel of the outputs
@@ -377,146 +405,207 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       }
     }
   }
-  if (err) atomicOr(&a.hdr[kHdrError], err);
-  __syncthreads();
+  if (grp == 0 && w == 0) {
+    // Requests without tokens get zero rows (no tile covers them).
+    for (int eb = lane; eb < a.batch; eb += kWave) {
+      if (a.kv_indptr[eb + 1] == a.kv_indptr[eb]) {
+        uint4* row = reinterpret_cast<uint4*>(a.out + (size_t)eb * Hq * D);
+        for (int i = 0; i < Hq * D / 8; ++i) row[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // also publishes s_gi and s_ptr, written before the loop
+  const GroupInfo gi = s_gi;
+  float* const lse_p = uniform_ptr(s_ptr.lse);
+  float* const opart_p = uniform_ptr(s_ptr.opart);
+  int32_t* const counters_p = uniform_ptr(s_ptr.counters);
+  if (err) atomicOr(&uniform_ptr(s_ptr.hdr)[kHdrError], err);
+  // Fields of the record by a run-time slot index, as selects (an indexed
+  // access would move the record to scratch memory).
+  auto lo_of = [&](int k) { return k == 0 ? gi.lo[0] : gi.lo[1]; };
+  auto hi_of = [&](int k) { return k == 0 ? gi.hi[0] : gi.hi[1]; };
+
+  // Epilogue.  Outputs are handled as groups of four channels: thread t < kVec
+  // owns channels 4 (t % (D / 4)) .. +3 of head t / (D / 4) of a segment.
+  constexpr int kVec = HG * D / 4;
+  static_assert(kVec <= 128 && kGroupThreads % 128 == 0, "thread quarters of 128");
+  // Buffer resources of the partials (built where used: they occupy scalar
+  // registers).
+  auto lse_rsrc = [&]() {
+    return __builtin_amdgcn_make_buffer_rsrc(lse_p, 0, (int)(sizeof(float) * 2 * HG * gridDim.x),
+                                             kBufferWord3);
+  };
+  auto opart_rsrc = [&]() {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        opart_p, 0, (int)(sizeof(float) * 2 * HG * D * gridDim.x), kBufferWord3);
+  };
 
   // Merge the pieces in LDS segment by segment (a segment's pieces are
-  // consecutive in wave order).  Thread t owns outputs t, t + 256, ... of the
-  // HG x D block (head o / D, channel o % D).
-  const int2 gsegs = a.group_segs[grp];
-  auto emit = [&](int sgm, const Combine& cb, int o) {
-    const int h = o / D;
-    const int c = o - h * D;
-    const bool act = o < HG * D;
-    const int eb = sgm / U;
-    const int hq = (sgm - eb * U) * HG + h;
-    const int2 sg = a.seg_groups[sgm];
-    const float val = cb.den > 0.f ? cb.num / cb.den : 0.f;
-    if (sg.x == grp && sg.y == grp) {
-      if (act) a.out[((size_t)eb * Hq + hq) * D + c] = (uint16_t)bf16_rne(val);
-    } else {
-      const int slot = sgm == gsegs.x ? 0 : 1;
-      const size_t row = (size_t)(2 * grp + slot) * HG + h;
-      if (act) {
-        store_coherent(&a.opart[row * D + c], val);
-        if (c == 0) store_coherent(&a.lse[row], cb.den > 0.f ? cb.m + fast_log2(cb.den) : kMinusInf);
-      }
-      if (tid == 0) s_glob[slot] = sgm;
-    }
-  };
-  {
+  // consecutive in wave order).  A segment inside this workgroup is written to
+  // the output; the first and the last segment, if they reach other
+  // workgroups, leave a normalised partial and its log-sum-exp.
+  if (tid < kVec) {
+    const int h = tid / (D / 4);
+    const int c = (tid - h * (D / 4)) * 4;
     constexpr int NS = 2 * kWavesPerGroup;
     int segs[NS];
 #pragma unroll
     for (int k = 0; k < NS; ++k) segs[k] = s_seg[k >> 1][k & 1];
+    int cur = -1;
+    Combine4 cb;
+    // Partials of the first and the last segment are kept in registers and
+    // stored after the loop (one store site each).
+    f4 pval[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float plse[2] = {kMinusInf, kMinusInf};
+    bool pub[2] = {false, false};
+    auto emit = [&]() {
+      const int eb = cur / U;
+      const int hq = (cur - eb * U) * HG + h;
+      const int slot = cur == gi.seg[0] ? 0 : (cur == gi.seg[1] ? 1 : -1);
+      const bool local = slot < 0 || (lo_of(slot) == grp && hi_of(slot) == grp);
+      const float inv = cb.den > 0.f ? 1.0f / cb.den : 0.f;
+      const f4 val = cb.num * inv;
+      if (local) {
+        *reinterpret_cast<uint2*>(a.out + ((size_t)eb * Hq + hq) * D + c) =
+            make_uint2(pack_bf16x2(val.x, val.y), pack_bf16x2(val.z, val.w));
+      } else {
+        const float lse = cb.den > 0.f ? cb.m + fast_log2(cb.den) : kMinusInf;
 #pragma unroll
-    for (int oi = 0; oi < kOut; ++oi) {
-      const int o = tid + oi * kGroupThreads;
-      const int h = o < HG * D ? o / D : 0;
-      const int c = o < HG * D ? o - h * D : 0;
-      float mk[NS], lk[NS], vk[NS];
-#pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        mk[k] = s_m[k >> 1][k & 1][h];
-        lk[k] = s_l[k >> 1][k & 1][h];
-        vk[k] = s_acc[k >> 1][k & 1][h][c];
-      }
-      int cur = -1;
-      Combine cb;
-#pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        const int sgm = segs[k];
-        if (sgm < 0) continue;
-        if (sgm != cur) {
-          if (cur >= 0) emit(cur, cb, o);
-          cur = sgm;
-          cb = Combine();
+        for (int k = 0; k < 2; ++k) {
+          if (slot == k) {
+            pval[k] = val;
+            plse[k] = lse;
+            pub[k] = true;
+          }
         }
-        cb.add(mk[k], lk[k], vk[k]);
+        if (tid == 0) s_glob[slot] = cur;  // thread 0 visits every segment
       }
-      if (cur >= 0) emit(cur, cb, o);
+    };
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int sgm = segs[k];
+      if (sgm < 0) continue;
+      if (sgm != cur) {
+        if (cur >= 0) emit();
+        cur = sgm;
+        cb = Combine4();
+      }
+      cb.add(s_m[k >> 1][k & 1][h], s_l[k >> 1][k & 1][h],
+             *reinterpret_cast<const f4*>(&s_acc[k >> 1][k & 1][h][c]));
+    }
+    if (cur >= 0) emit();
+    const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (!pub[k]) continue;
+      const int row = (2 * grp + k) * HG + h;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, pval[k]), opart_rs,
+                                             (row * D + c) * 4, 0, kCoherent);
+      if (c == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(plse[k]), lse_rs, row * 4, 0,
+                                              kCoherent);
     }
   }
 
   // Cross-workgroup merge: publish the partials, count arrivals, and let the
   // last workgroup of each segment combine every workgroup's partial in order.
+  // Lanes 0 and 1 arrive for the first and the last segment at the same time.
   wait_stores();
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 2) {
+    const int k = tid;
+    const int sgm = s_glob[k];
+    int merge = -1;
+    if (sgm >= 0 && !(k == 1 && sgm == s_glob[0])) {
+      const int old = __hip_atomic_fetch_add(&counters_p[sgm], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      if (old == hi_of(k) - lo_of(k)) merge = sgm;
+    }
+    s_merge[k] = merge;
+  }
+  __syncthreads();
+  const int msg[2] = {s_merge[0], s_merge[1]};
+  if (msg[0] < 0 && msg[1] < 0) return;  // uniform over the workgroup
+
+  // Merge every segment this workgroup arrived last for.  The workgroups of a
+  // segment are dealt to four quarters of the threads (quarter q takes
+  // contributors q, q + 4, ...); every load of a round is issued before any is
+  // used, and addresses are clamped so the loads need no branches.  The four
+  // quarter results are then combined in quarter order through LDS, so the
+  // result depends only on the plan.
+  constexpr int kQuarters = kGroupThreads / 128;
+  constexpr int kPer = 8;  // contributors per quarter and segment in one round
+  const int t = tid & 127;
+  const int q = tid >> 7;
+  const bool tact = t < kVec;
+  const int h = tact ? t / (D / 4) : 0;
+  const int c = tact ? (t - h * (D / 4)) * 4 : 0;
+  // Segment k's contributors are workgroups lo[k] .. hi[k] (none if not merged
+  // here).  Workgroup j > lo holds the segment as its first segment (slot 0);
+  // the first workgroup holds it in the slot the plan recorded.
+  const int lo[2] = {msg[0] >= 0 ? gi.lo[0] : 0, msg[1] >= 0 ? gi.lo[1] : 0};
+  const int hi[2] = {msg[0] >= 0 ? gi.hi[0] : -1, msg[1] >= 0 ? gi.hi[1] : -1};
+  const int slot0[2] = {gi.slot_lo[0], gi.slot_lo[1]};
+  const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
+  const int span = max(hi[0] - lo[0], hi[1] - lo[1]) + 1;
+  const int rounds = (span + kQuarters * kPer - 1) / (kQuarters * kPer);
+  Combine4 mc[2];
+#pragma unroll 1
+  for (int rd = 0; rd < rounds; ++rd) {
+    float ls[2][kPer];
+    f4 ov[2][kPer];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int sgm = s_glob[k];
-      s_merge[k] = -1;
-      if (sgm >= 0 && !(k == 1 && sgm == s_glob[0])) {
-        const int2 sg = a.seg_groups[sgm];
-        const int old = __hip_atomic_fetch_add(&a.counters[sgm], 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        if (old == sg.y - sg.x) s_merge[k] = sgm;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int j = max(min(lo[k] + (rd * kPer + i) * kQuarters + q, hi[k]), 0);
+        const int row = (2 * j + (j == lo[k] ? slot0[k] : 0)) * HG + h;
+        ls[k][i] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(lse_rs, row * 4, 0, kCoherent));
+        ov[k][i] = __builtin_bit_cast(
+            f4, __builtin_amdgcn_raw_buffer_load_b128(opart_rs, (row * D + c) * 4, 0, kCoherent));
       }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) mc[k].add(ls[k][i], 1.0f, ov[k][i]);
+  }
+  // Quarter results through LDS (the pieces' LDS is free by now).
+  float* s_qm = &s_acc[0][0][0][0];            // [2][kQuarters][kVec]
+  float* s_qd = s_qm + 2 * kQuarters * kVec;  // [2][kQuarters][kVec]
+  f4* s_qn = reinterpret_cast<f4*>(&s_out[0][0][0]);  // [2][kQuarters][kVec]
+  static_assert(sizeof(s_acc) >= 2 * 2 * kQuarters * kVec * sizeof(float), "LDS reuse");
+  static_assert(sizeof(s_out) >= 2 * kQuarters * kVec * sizeof(f4), "LDS reuse");
+  if (tact) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = (k * kQuarters + q) * kVec + t;
+      s_qm[i] = mc[k].m;
+      s_qd[i] = mc[k].den;
+      s_qn[i] = mc[k].num;
     }
   }
   __syncthreads();
-  // Merge every segment this workgroup arrived last for.  All loads of a round
-  // (both segments, every output of the thread, 16 partials each) are issued
-  // before any is used, so a merge costs about one memory round trip.
-  const int msg[2] = {s_merge[0], s_merge[1]};
-  if (msg[0] >= 0 || msg[1] >= 0) {
-    constexpr int kUnroll = 16;
-    int2 sg[2];
-    int slot0[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      sg[k] = msg[k] >= 0 ? a.seg_groups[msg[k]] : make_int2(0, -1);
-      // Workgroup j > sg.x holds the segment as its first segment (slot 0); the
-      // first workgroup holds it in slot 0 only if the segment starts its range.
-      slot0[k] = msg[k] >= 0 && a.group_segs[sg[k].x].x != msg[k] ? 1 : 0;
-    }
-    const int rounds = max(sg[0].y - sg[0].x, sg[1].y - sg[1].x) / kUnroll + 1;
-    Combine cb[2][kOut];
-#pragma unroll 1
-    for (int rd = 0; rd < rounds; ++rd) {
-      float ls[2][kOut][kUnroll], ov[2][kOut][kUnroll];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-#pragma unroll
-        for (int oi = 0; oi < kOut; ++oi) {
-          const int o = tid + oi * kGroupThreads;
-          const bool act = msg[k] >= 0 && o < HG * D;
-          const int h = o < HG * D ? o / D : 0;
-          const int c = o - h * D;
-#pragma unroll
-          for (int q = 0; q < kUnroll; ++q) {
-            const int j = min(sg[k].x + rd * kUnroll + q, sg[k].y);
-            const size_t row = (size_t)(2 * j + (j == sg[k].x ? slot0[k] : 0)) * HG + h;
-            ls[k][oi][q] = act ? load_coherent(&a.lse[row]) : kMinusInf;
-            ov[k][oi][q] = act ? load_coherent(&a.opart[row * D + c]) : 0.f;
-          }
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-#pragma unroll
-        for (int oi = 0; oi < kOut; ++oi)
-#pragma unroll
-          for (int q = 0; q < kUnroll; ++q)
-            if (sg[k].x + rd * kUnroll + q <= sg[k].y) cb[k][oi].add(ls[k][oi][q], 1.0f, ov[k][oi][q]);
-    }
+  if (q == 0 && tact) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       if (msg[k] < 0) continue;
-      const int eb = msg[k] / U;
+      Combine4 cb;
 #pragma unroll
-      for (int oi = 0; oi < kOut; ++oi) {
-        const int o = tid + oi * kGroupThreads;
-        if (o >= HG * D) continue;
-        const int h = o / D;
-        const int c = o - h * D;
-        const int hq = (msg[k] - eb * U) * HG + h;
-        const float val = cb[k][oi].den > 0.f ? cb[k][oi].num / cb[k][oi].den : 0.f;
-        a.out[((size_t)eb * Hq + hq) * D + c] = (uint16_t)bf16_rne(val);
+      for (int qq = 0; qq < kQuarters; ++qq) {
+        const int i = (k * kQuarters + qq) * kVec + t;
+        cb.add(s_qm[i], s_qd[i], s_qn[i]);
       }
-      if (tid == 0)
-        __hip_atomic_store(&a.counters[msg[k]], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int eb = msg[k] / U;
+      const int hq = (msg[k] - eb * U) * HG + h;
+      const float inv = cb.den > 0.f ? 1.0f / cb.den : 0.f;
+      const f4 val = cb.num * inv;
+      *reinterpret_cast<uint2*>(a.out + ((size_t)eb * Hq + hq) * D + c) =
+          make_uint2(pack_bf16x2(val.x, val.y), pack_bf16x2(val.z, val.w));
+      if (t == 0)
+        __hip_atomic_store(&counters_p[msg[k]], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -45,11 +45,22 @@ struct alignas(16) WaveRange {
   int32_t pad;
 };
 
+// What a workgroup needs for its merges, prepared by the metadata kernel so
+// the decode reads it in one load at its start.  A segment is one (request,
+// head group); only the first and the last segment of a workgroup's tile range
+// can extend into other workgroups.
+struct alignas(16) GroupInfo {
+  int32_t seg[2];      // first and last segment of the range (-1: no range)
+  int32_t lo[2];       // first workgroup whose range touches seg[k]
+  int32_t hi[2];       // last workgroup whose range touches seg[k]
+  int32_t slot_lo[2];  // partial slot (0 = first segment, 1 = last) seg[k] has in workgroup lo[k]
+};
+
 // Byte offsets of the workspace sections; every section is 256-byte aligned.
 struct WsLayout {
   int32_t groups;    // decode grid size (workgroups)
   int32_t segments;  // max_batch * U
-  size_t hdr, waves, group_segs, seg_groups, counters, lse, opart, total;
+  size_t hdr, waves, ginfo, counters, lse, opart, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -66,8 +77,7 @@ struct MetaArgs {
   int32_t* kv_indptr;
   int32_t* hdr;
   WaveRange* waves;    // [groups * kWavesPerGroup]
-  int2* group_segs;    // [groups]: first and last segment a workgroup touches
-  int2* seg_groups;    // [segments]: first and last workgroup touching a segment
+  GroupInfo* ginfo;    // [groups]
   int32_t* counters;   // [segments]: arrivals for the cross-workgroup merge
   int32_t batch, page_size, units, groups, min_tiles, forced;
 };
@@ -92,8 +102,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int32_t* hdr;
   const WaveRange* waves;
-  const int2* group_segs;
-  const int2* seg_groups;
+  const GroupInfo* ginfo;
   int32_t* counters;
   float* lse;     // [2 * groups][HG], log2-domain log-sum-exp of workgroup partials
   float* opart;   // [2 * groups][HG][D], normalised workgroup partials

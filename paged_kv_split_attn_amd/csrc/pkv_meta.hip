@@ -139,34 +139,33 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
     a.waves[gw] = r;
   }
 
-  // Phase 3: first and last segment (b * U + u) of every workgroup.
+  // Phase 3: the merge record of every workgroup.  Its first and last segment
+  // (b * U + u), and for each the workgroups its tiles span: tile t belongs to
+  // workgroup floor(((t + 1) * W - 1) / T).  A segment is the first segment of
+  // a workgroup exactly when that workgroup's range starts inside it.
   for (int i = tid; i < a.groups; i += kMetaThreads) {
-    int2 gs = make_int2(-1, -1);
+    GroupInfo gi{{-1, -1}, {0, 0}, {-1, -1}, {0, 0}};
     const long long g0 = i < W ? (long long)i * T / W : 0;
     const long long g1 = i < W ? (long long)(i + 1) * T / W : 0;
     if (g1 > g0) {
-      const WaveRange f = loc.at(g0, 0), l = loc.at(g1 - 1, 0);
-      gs = make_int2(f.b * U + f.u, l.b * U + l.u);
+      const WaveRange ends[2] = {loc.at(g0, 0), loc.at(g1 - 1, 0)};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const WaveRange& e = ends[k];
+        const long long t0 = (long long)e.ip0 * U + (long long)e.u * e.pages;
+        const long long t1 = t0 + e.pages - 1;
+        const int lo = (int)(((t0 + 1) * W - 1) / T);
+        gi.seg[k] = e.b * U + e.u;
+        gi.lo[k] = lo;
+        gi.hi[k] = (int)(((t1 + 1) * W - 1) / T);
+        gi.slot_lo[k] = (long long)lo * T / W >= t0 ? 0 : 1;
+      }
     }
-    a.group_segs[i] = gs;
+    a.ginfo[i] = gi;
   }
 
-  // Phase 4: first and last workgroup of every segment; arrival counters.
-  // Tile t belongs to group floor(((t + 1) * W - 1) / T).
-  for (int sgi = tid; sgi < a.batch * U; sgi += kMetaThreads) {
-    const int b = sgi / U;
-    const int u = sgi - b * U;
-    const int ip0 = loc.ip[b];
-    const int n = loc.ip[b + 1] - ip0;
-    int2 sg = make_int2(-1, -1);
-    if (n > 0 && W > 0) {
-      const long long t0 = (long long)ip0 * U + (long long)u * n;
-      const long long t1 = t0 + n - 1;
-      sg = make_int2((int)(((t0 + 1) * W - 1) / T), (int)(((t1 + 1) * W - 1) / T));
-    }
-    a.seg_groups[sgi] = sg;
-    a.counters[sgi] = 0;
-  }
+  // Phase 4: arrival counters of the cross-workgroup merge.
+  for (int sgi = tid; sgi < a.batch * U; sgi += kMetaThreads) a.counters[sgi] = 0;
 
   if (err) atomicOr(&s_err, err);
   __syncthreads();

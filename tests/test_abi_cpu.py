@@ -65,7 +65,7 @@ def test_workspace_bytes(lib):
     n = pkv.pkv_workspace_bytes(d)
     groups, hg, segs = 256, 4, 16 * 8
     expect = 256  # header
-    for sz in (32 * groups * pkv.WAVES_PER_GROUP, 8 * groups, 8 * segs, 4 * segs, 4 * 2 * groups * hg,
+    for sz in (32 * groups * pkv.WAVES_PER_GROUP, 32 * groups, 4 * segs, 4 * 2 * groups * hg,
                4 * 2 * groups * hg * 128):
         expect += (sz + 255) // 256 * 256
     assert n == expect
@@ -144,5 +144,5 @@ def test_header_wave_count_matches_library(lib):
     # the workspace holds one 32-byte range per wave of every workgroup
     one = pkv.pkv_workspace_bytes(_desc(num_workgroups=1024))
     two = pkv.pkv_workspace_bytes(_desc(num_workgroups=2048))
-    per_group = 32 * pkv.WAVES_PER_GROUP + 8 + 4 * 2 * 4 * (1 + 128)
+    per_group = 32 * pkv.WAVES_PER_GROUP + 32 + 4 * 2 * 4 * (1 + 128)
     assert two - one == 1024 * per_group
