@@ -440,70 +440,85 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         opart_p, 0, (int)(sizeof(float) * 2 * HG * D * gridDim.x), kBufferWord3);
   };
 
-  // Merge the pieces in LDS segment by segment (a segment's pieces are
-  // consecutive in wave order).  A segment inside this workgroup is written to
-  // the output; the first and the last segment, if they reach other
-  // workgroups, leave a normalised partial and its log-sum-exp.
-  if (tid < kVec) {
-    const int h = tid / (D / 4);
-    const int c = (tid - h * (D / 4)) * 4;
-    constexpr int NS = 2 * kWavesPerGroup;
-    int segs[NS];
+  // Merge the pieces in LDS segment by segment (a segment's pieces are the
+  // valid slots between two changes of segment, in wave order).  A segment
+  // inside this workgroup is written to the output; the first and the last
+  // segment, if they reach other workgroups, leave a normalised partial and its
+  // log-sum-exp.  Pass 1 (one thread per slot and head): the segment's max and
+  // sum, the slot's normalised weight, and per slot where its segment goes.
+  // Pass 2 (one thread per output element): weighted sums of the slots.
+  constexpr int NS = 2 * kWavesPerGroup;
+  static_assert(NS * HG <= kGroupThreads, "pass 1: one thread per slot and head");
+  __shared__ float s_w[NS][HG];    // normalised weight of slot k for head h
+  __shared__ float s_lse[NS][HG];  // log2-domain log-sum-exp of slot k's segment
+  __shared__ int s_row[NS];        // output row of head 0 of slot k's segment
+  __shared__ int s_kind[NS];       // -1: written here; 0 / 1: partial slot
+  __shared__ int s_end[NS];        // slot k is its segment's last valid slot
+  int segs[NS];
 #pragma unroll
-    for (int k = 0; k < NS; ++k) segs[k] = s_seg[k >> 1][k & 1];
-    int cur = -1;
-    Combine4 cb;
-    // Partials of the first and the last segment are kept in registers and
-    // stored after the loop (one store site each).
-    f4 pval[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    float plse[2] = {kMinusInf, kMinusInf};
-    bool pub[2] = {false, false};
-    auto emit = [&]() {
-      const int eb = cur / U;
-      const int hq = (cur - eb * U) * HG + h;
-      const int slot = cur == gi.seg[0] ? 0 : (cur == gi.seg[1] ? 1 : -1);
+  for (int k = 0; k < NS; ++k) segs[k] = s_seg[k >> 1][k & 1];
+  if (tid < NS * HG) {
+    const int k = tid / HG;
+    const int h = tid - k * HG;
+    int sk = -1;
+#pragma unroll
+    for (int k2 = 0; k2 < NS; ++k2) sk = k2 == k ? segs[k2] : sk;
+    float mk[NS], lk[NS];
+#pragma unroll
+    for (int k2 = 0; k2 < NS; ++k2) {
+      mk[k2] = s_m[k2 >> 1][k2 & 1][h];
+      lk[k2] = s_l[k2 >> 1][k2 & 1][h];
+    }
+    float M = kFloorMax, mine = kFloorMax;
+#pragma unroll
+    for (int k2 = 0; k2 < NS; ++k2) {
+      if (segs[k2] == sk) M = fmaxf(M, mk[k2]);
+      if (k2 == k) mine = mk[k2];
+    }
+    float L = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < NS; ++k2)
+      if (segs[k2] == sk) L += fast_exp2(mk[k2] - M) * lk[k2];
+    const bool live = sk >= 0 && L > 0.f;
+    s_w[k][h] = live ? fast_exp2(mine - M) * __builtin_amdgcn_rcpf(L) : 0.f;
+    s_lse[k][h] = live ? M + fast_log2(L) : kMinusInf;
+    if (h == 0) {
+      int next = -1;  // segment of the next valid slot
+#pragma unroll
+      for (int k2 = NS - 1; k2 >= 0; --k2)
+        if (k2 > k && segs[k2] >= 0) next = segs[k2];
+      const int slot = sk < 0 ? -1 : (sk == gi.seg[0] ? 0 : (sk == gi.seg[1] ? 1 : -1));
       const bool local = slot < 0 || (lo_of(slot) == grp && hi_of(slot) == grp);
-      const float inv = cb.den > 0.f ? 1.0f / cb.den : 0.f;
-      const f4 val = cb.num * inv;
-      if (local) {
-        *reinterpret_cast<uint2*>(a.out + ((size_t)eb * Hq + hq) * D + c) =
-            make_uint2(pack_bf16x2(val.x, val.y), pack_bf16x2(val.z, val.w));
-      } else {
-        const float lse = cb.den > 0.f ? cb.m + fast_log2(cb.den) : kMinusInf;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          if (slot == k) {
-            pval[k] = val;
-            plse[k] = lse;
-            pub[k] = true;
-          }
-        }
-        if (tid == 0) s_glob[slot] = cur;  // thread 0 visits every segment
-      }
-    };
+      const int eb = sk >= 0 ? sk / U : 0;
+      s_row[k] = eb * Hq + (sk - eb * U) * HG;
+      s_kind[k] = local ? -1 : slot;
+      s_end[k] = sk >= 0 && next != sk;
+      if (sk >= 0 && !local) s_glob[slot] = sk;
+    }
+  }
+  __syncthreads();
+  if (tid < HG * D) {
+    const int h = tid / D;
+    const int c = tid - h * D;
+    const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
+    float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      const int sgm = segs[k];
-      if (sgm < 0) continue;
-      if (sgm != cur) {
-        if (cur >= 0) emit();
-        cur = sgm;
-        cb = Combine4();
+      if (segs[k] < 0) continue;
+      acc += s_w[k][h] * s_acc[k >> 1][k & 1][h][c];
+      if (__builtin_amdgcn_readfirstlane(s_end[k]) == 0) continue;
+      const int kind = __builtin_amdgcn_readfirstlane(s_kind[k]);
+      if (kind < 0) {
+        a.out[(size_t)(s_row[k] + h) * D + c] = (uint16_t)bf16_rne(acc);
+      } else {
+        const int row = (2 * grp + kind) * HG + h;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), opart_rs, (row * D + c) * 4,
+                                              0, kCoherent);
+        if (c == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_lse[k][h]), lse_rs, row * 4, 0,
+                                                kCoherent);
       }
-      cb.add(s_m[k >> 1][k & 1][h], s_l[k >> 1][k & 1][h],
-             *reinterpret_cast<const f4*>(&s_acc[k >> 1][k & 1][h][c]));
-    }
-    if (cur >= 0) emit();
-    const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      if (!pub[k]) continue;
-      const int row = (2 * grp + k) * HG + h;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, pval[k]), opart_rs,
-                                             (row * D + c) * 4, 0, kCoherent);
-      if (c == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(plse[k]), lse_rs, row * 4, 0,
-                                              kCoherent);
+      acc = 0.f;
     }
   }
 
@@ -527,16 +542,18 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const int msg[2] = {s_merge[0], s_merge[1]};
   if (msg[0] < 0 && msg[1] < 0) return;  // uniform over the workgroup
 
-  // Merge every segment this workgroup arrived last for.  The workgroups of a
-  // segment are dealt to four quarters of the threads (quarter q takes
-  // contributors q, q + 4, ...); every load of a round is issued before any is
-  // used, and addresses are clamped so the loads need no branches.  The four
-  // quarter results are then combined in quarter order through LDS, so the
-  // result depends only on the plan.
-  constexpr int kQuarters = kGroupThreads / 128;
+  // Merge every segment this workgroup arrived last for.  Wave w merges output
+  // groups 16 w .. 16 w + 15; the four 16-lane quarters of the wave take the
+  // segment's workgroups in turn (quarter q: contributors q, q + 4, ...).  Every
+  // load of a round is issued before any is used, and addresses are clamped so
+  // the loads need no branches.  The quarters' results are then combined
+  // across lanes (quarter pairs 0+1 and 2+3, then the two pairs, lower first),
+  // so the result depends only on the plan and no barrier is needed.
+  static_assert(kWavesPerGroup * 16 >= kVec, "one output group per lane of a quarter");
+  constexpr int kQuarters = 4;
   constexpr int kPer = 8;  // contributors per quarter and segment in one round
-  const int t = tid & 127;
-  const int q = tid >> 7;
+  const int q = lane >> 4;
+  const int t = w * 16 + (lane & 15);
   const bool tact = t < kVec;
   const int h = tact ? t / (D / 4) : 0;
   const int c = tact ? (t - h * (D / 4)) * 4 : 0;
@@ -566,47 +583,55 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
             f4, __builtin_amdgcn_raw_buffer_load_b128(opart_rs, (row * D + c) * 4, 0, kCoherent));
       }
     }
+    // This round's contributors: max first, then one exponential each.
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 2; ++k) {
+      float mr = kFloorMax;
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) mc[k].add(ls[k][i], 1.0f, ov[k][i]);
-  }
-  // Quarter results through LDS (the pieces' LDS is free by now).
-  float* s_qm = &s_acc[0][0][0][0];            // [2][kQuarters][kVec]
-  float* s_qd = s_qm + 2 * kQuarters * kVec;  // [2][kQuarters][kVec]
-  f4* s_qn = reinterpret_cast<f4*>(&s_out[0][0][0]);  // [2][kQuarters][kVec]
-  static_assert(sizeof(s_acc) >= 2 * 2 * kQuarters * kVec * sizeof(float), "LDS reuse");
-  static_assert(sizeof(s_out) >= 2 * kQuarters * kVec * sizeof(f4), "LDS reuse");
-  if (tact) {
+        if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) mr = fmaxf(mr, ls[k][i]);
+      float den = 0.f;
+      f4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = (k * kQuarters + q) * kVec + t;
-      s_qm[i] = mc[k].m;
-      s_qd[i] = mc[k].den;
-      s_qn[i] = mc[k].num;
+      for (int i = 0; i < kPer; ++i) {
+        if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) {
+          const float wi = fast_exp2(ls[k][i] - mr);
+          den += wi;
+          num += ov[k][i] * wi;
+        }
+      }
+      mc[k].add(mr, den, num);
     }
   }
-  __syncthreads();
-  if (q == 0 && tact) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      if (msg[k] < 0) continue;
-      Combine4 cb;
+  for (int k = 0; k < 2; ++k) {
+    if (msg[k] < 0) continue;
+    Combine4 x = mc[k];
 #pragma unroll
-      for (int qq = 0; qq < kQuarters; ++qq) {
-        const int i = (k * kQuarters + qq) * kVec + t;
-        cb.add(s_qm[i], s_qd[i], s_qn[i]);
-      }
+    for (int off = 16; off <= 32; off <<= 1) {
+      Combine4 y;
+      y.m = __shfl_xor(x.m, off, kWave);
+      y.den = __shfl_xor(x.den, off, kWave);
+      y.num.x = __shfl_xor(x.num.x, off, kWave);
+      y.num.y = __shfl_xor(x.num.y, off, kWave);
+      y.num.z = __shfl_xor(x.num.z, off, kWave);
+      y.num.w = __shfl_xor(x.num.w, off, kWave);
+      const bool lower = (lane & off) == 0;
+      Combine4 r = lower ? x : y;
+      const Combine4& other = lower ? y : x;
+      r.add(other.m, other.den, other.num);
+      x = r;
+    }
+    if (q == 0 && tact) {
       const int eb = msg[k] / U;
       const int hq = (msg[k] - eb * U) * HG + h;
-      const float inv = cb.den > 0.f ? 1.0f / cb.den : 0.f;
-      const f4 val = cb.num * inv;
+      const float inv = x.den > 0.f ? 1.0f / x.den : 0.f;
+      const f4 val = x.num * inv;
       *reinterpret_cast<uint2*>(a.out + ((size_t)eb * Hq + hq) * D + c) =
           make_uint2(pack_bf16x2(val.x, val.y), pack_bf16x2(val.z, val.w));
-      if (t == 0)
-        __hip_atomic_store(&counters_p[msg[k]], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (tid == 0)
+      __hip_atomic_store(&counters_p[msg[k]], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
