@@ -2,8 +2,9 @@
 
 One step = the whole hot path for one layer of one decode step: build the step
 metadata (page prefix sums + work plan), append this step's K/V token of every
-request, then the split-KV decode kernel (partials and their merge in one
-launch).  Inputs are seeded synthetic
+request and run the split-KV decode (partials and their merge).  By default the
+append and the decode are one launch (pkv_decode_append); --append separate
+runs pkv_append_kv and pkv_decode as two launches.  Inputs are seeded synthetic
 batches already resident in HBM.  Between steps the pool rotates over several
 identical copies whose total size exceeds the 256 MB Infinity Cache, so every
 step streams its K/V from HBM.
@@ -48,6 +49,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0 = enough for 768 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--append", choices=("fused", "separate"), default="fused",
+                    help="KV append fused into the decode launch, or its own launch")
     ap.add_argument("--no-kernel-loop", action="store_true",
                     help="time only whole steps (skip the decode-only loop)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -186,8 +189,12 @@ def main():
     def step(i):
         pool, q = copies[i % ncopies]
         pkv.pkv_build_metadata(desc, seq, 0, kv_indptr, ws, stream)
-        pkv.pkv_append_kv(pool, k_new, v_new, kv_indptr, idx, seq, stream)
-        pkv.pkv_decode(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, stream)
+        if args.append == "fused":
+            pkv.pkv_decode_append(pool, desc, q, k_new, v_new, kv_indptr, idx, seq,
+                                  batch.sm_scale, ws, out, stream)
+        else:
+            pkv.pkv_append_kv(pool, k_new, v_new, kv_indptr, idx, seq, stream)
+            pkv.pkv_decode(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, stream)
 
     def decode_only(i):
         pool, q = copies[i % ncopies]
@@ -221,7 +228,8 @@ def main():
                    "Hkv": batch.Hkv, "head_dim": batch.D, "page_size": batch.P,
                    "kv_tokens": batch.kv_tokens, "pool_pages": batch.num_pages,
                    "pool_copies": ncopies, "decode_grid": desc.groups(),
-                   "plan_workgroups": plan["groups"], "parallelism": "single-gpu"},
+                   "plan_workgroups": plan["groups"], "append": args.append,
+                   "parallelism": "single-gpu"},
         "step_bytes": step_bytes,
         "call_bytes": call_bytes,
     }

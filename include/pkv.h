@@ -173,7 +173,10 @@ int pkv_build_metadata(const pkv_desc* desc, const int32_t* seq_lens, int32_t ba
  *  seq_lens       device int32 [batch], post-append lengths; <= 0 writes nothing
  * Two requests must not target the same slot (the writes would race).
  * Page ids outside [0, num_pages) or index positions outside [0, num_indices)
- * are skipped. */
+ * are skipped.
+ * Errors: PKV_ERR_INVALID_ARG (null pointer, negative size, or more than
+ * 2^31 - 1 row chunks), PKV_ERR_UNSUPPORTED (head_dim other than 64 or 128),
+ * PKV_ERR_LAUNCH. */
 int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
                   const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
                   const int32_t* seq_lens, int32_t batch, void* stream);
@@ -195,6 +198,24 @@ int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
                const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
                size_t workspace_bytes, void* out, void* stream);
+
+/* KV append and decode attention of one layer in one kernel launch: the same
+ * result, pool contents included, as pkv_append_kv(pool, k_new, v_new, ...)
+ * followed by pkv_decode(...) with the same arguments, without the separate
+ * append launch.  On the pages the per-layer step is exactly this pair: the
+ * new token's K and V are stored into the layer's buffers, then attention runs
+ * over the cache that includes them (attention_backend.py, CudaBackend.
+ * fwd_decode, on the compare page).  The wave that reads the page holding
+ * token seq_lens[b] - 1 takes that token from k_new / v_new and writes it into
+ * the pool.
+ *  k_new, v_new   device bf16 [batch][num_kv_heads][head_dim], both non-NULL
+ * Every other argument, the layouts and the errors are those of pkv_decode and
+ * pkv_append_kv (PKV_ERR_INVALID_ARG for a NULL k_new or v_new). */
+int pkv_decode_append(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                      const void* k_new, const void* v_new, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, int32_t num_indices, const int32_t* seq_lens,
+                      int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
+                      void* out, void* stream);
 
 /* Debug only (synchronises the stream; not capturable).  Checks device
  * metadata and copies the plan to host memory.

@@ -34,6 +34,7 @@ __all__ = [
     "pkv_build_metadata",
     "pkv_append_kv",
     "pkv_decode",
+    "pkv_decode_append",
     "pkv_debug_validate",
     "WAVES_PER_GROUP",
     "PKV_OK",
@@ -105,6 +106,9 @@ _SIGNATURES = {
     "pkv_decode": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp, _vp,
                                   _i32, _vp, _i32, ctypes.c_float, _vp, ctypes.c_size_t, _vp,
                                   _vp]),
+    "pkv_decode_append": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp,
+                                         _vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
+                                         ctypes.c_size_t, _vp, _vp]),
     "pkv_debug_validate": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _vp, _vp, _i32, _i32, _i32,
                                           _vp, ctypes.c_size_t, _i32p, _i32p, _vp]),
 }
@@ -259,6 +263,24 @@ def pkv_decode(pool: Pool, desc: Desc, q: torch.Tensor, kv_indptr: torch.Tensor,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(out, "out", _BF16, n), _stream(stream))
     _check("pkv_decode", st)
+
+
+def pkv_decode_append(pool: Pool, desc: Desc, q: torch.Tensor, k_new: torch.Tensor,
+                      v_new: torch.Tensor, kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
+                      seq_lens: torch.Tensor, sm_scale: float, workspace: torch.Tensor,
+                      out: torch.Tensor, stream=None) -> None:
+    """pkv_append_kv followed by pkv_decode, in one launch."""
+    B = seq_lens.numel()
+    n = B * desc.num_q_heads * desc.head_dim
+    nkv = B * desc.num_kv_heads * desc.head_dim
+    st = load_library().pkv_decode_append(
+        ctypes.byref(pool.c()), ctypes.byref(desc.c()), _ptr(q, "q", _BF16, n),
+        _ptr(k_new, "k_new", _BF16, nkv), _ptr(v_new, "v_new", _BF16, nkv),
+        _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
+        kv_indices.numel(), _ptr(seq_lens, "seq_lens", _I32), B, float(sm_scale),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, "out", _BF16, n), _stream(stream))
+    _check("pkv_decode_append", st)
 
 
 def pkv_debug_validate(desc: Desc, seq_lens: torch.Tensor, kv_indptr: torch.Tensor,

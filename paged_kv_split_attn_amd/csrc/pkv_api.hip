@@ -109,7 +109,7 @@ const char* pkv_status_str(int status) {
   }
 }
 
-int32_t pkv_version(void) { return (2 << 16) | 0; }
+int32_t pkv_version(void) { return (2 << 16) | 1; }
 
 size_t pkv_workspace_bytes(const pkv_desc* desc) {
   WsLayout L;
@@ -151,7 +151,10 @@ int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
   if (!k_new || !v_new || !kv_indptr || !kv_indices || !seq_lens || batch < 0 ||
       num_indices < 0 || pool->page_size < 1 || pool->num_kv_heads < 1)
     return PKV_ERR_INVALID_ARG;
-  if (pool->head_dim < 8 || pool->head_dim % 8 != 0) return PKV_ERR_UNSUPPORTED;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  // One thread per 8 channels of every K and V row; the kernel indexes in 32 bits.
+  if ((long long)batch * pool->num_kv_heads * 2 * (pool->head_dim / 8) > 0x7fffffffLL)
+    return PKV_ERR_INVALID_ARG;
   AppendArgs a;
   a.k = static_cast<uint16_t*>(pool->k);
   a.v = static_cast<uint16_t*>(pool->v);
@@ -169,24 +172,32 @@ int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
   return launch_status(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
-int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
-               const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
-               const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
-               size_t workspace_bytes, void* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pkv_decode and pkv_decode_append: the same launch, with or without the
+// token to append.
+int decode_impl(const pkv_pool* pool, const pkv_desc* desc, const void* q, const void* k_new,
+                const void* v_new, const int32_t* kv_indptr, const int32_t* kv_indices,
+                int32_t num_indices, const int32_t* seq_lens, int32_t batch, float sm_scale,
+                void* workspace, size_t workspace_bytes, void* out, void* stream) {
   WsLayout L;
   int st = check_desc(desc, &L);
   if (st != PKV_OK) return st;
   st = check_pool(pool, desc);
   if (st != PKV_OK) return st;
   if (!q || !kv_indptr || !kv_indices || !seq_lens || !workspace || !out || batch < 0 ||
-      num_indices < 0 || !(sm_scale == sm_scale))
+      num_indices < 0 || !(sm_scale == sm_scale) || (k_new == nullptr) != (v_new == nullptr))
     return PKV_ERR_INVALID_ARG;
   if (batch > desc->max_batch) return PKV_ERR_CAPACITY;
   if (workspace_bytes < L.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
   if (batch == 0) return PKV_OK;
   DecodeArgs d;
-  d.k = static_cast<const uint16_t*>(pool->k);
-  d.v = static_cast<const uint16_t*>(pool->v);
+  d.k = static_cast<uint16_t*>(pool->k);
+  d.v = static_cast<uint16_t*>(pool->v);
+  d.k_new = static_cast<const uint16_t*>(k_new);
+  d.v_new = static_cast<const uint16_t*>(v_new);
   d.q = static_cast<const uint16_t*>(q);
   d.kv_indptr = kv_indptr;
   d.kv_indices = kv_indices;
@@ -210,6 +221,28 @@ int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
   d.scale_log2 = sm_scale * 1.4426950408889634f;
   return launch_status(
       launch_decode(d, desc->head_dim, hg, L.groups, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+               const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
+               const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
+               size_t workspace_bytes, void* out, void* stream) {
+  return decode_impl(pool, desc, q, nullptr, nullptr, kv_indptr, kv_indices, num_indices,
+                     seq_lens, batch, sm_scale, workspace, workspace_bytes, out, stream);
+}
+
+int pkv_decode_append(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                      const void* k_new, const void* v_new, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, int32_t num_indices, const int32_t* seq_lens,
+                      int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
+                      void* out, void* stream) {
+  if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
+  return decode_impl(pool, desc, q, k_new, v_new, kv_indptr, kv_indices, num_indices, seq_lens,
+                     batch, sm_scale, workspace, workspace_bytes, out, stream);
 }
 
 int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int32_t* kv_indptr,

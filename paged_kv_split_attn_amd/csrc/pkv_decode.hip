@@ -120,7 +120,8 @@ struct MfmaWave {
 
   // Consume one step.  `live` = tokens of the step that count (uniform, 0..16);
   // `g` = lane / 16; `bias` = 0 for heads < HG, -inf otherwise.
-  __device__ __forceinline__ void step(const Step<D>& st, int live, int g, float scale_log2,
+  template <class S>
+  __device__ __forceinline__ void step(const S& st, int live, int g, float scale_log2,
                                        float bias) {
     floatx4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -214,7 +215,7 @@ struct Combine4 {
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kCoherent = 16;
 
-template <int D, int HG>
+template <int D, int HG, bool APPEND>
 __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   constexpr int kStages = 2;  // register ring: steps in flight per wave
   constexpr int kOut = (HG * D + kGroupThreads - 1) / kGroupThreads;  // outputs per thread
@@ -230,6 +231,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   __shared__ int s_merge[2];  // of those, the ones this workgroup merges
   __shared__ GroupInfo s_gi;  // the workgroup's merge record, for the epilogue
   __shared__ EpiloguePtrs s_ptr;
+  __shared__ uint32_t s_vn[APPEND ? kWavesPerGroup : 1][kWave];  // appended V row, per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -244,6 +246,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // the first K/V loads wait on them, and the merges at the end need nothing
   // else from the plan.
   const int ngroups = a.hdr[kHdrGroups];
+  const int nempty = a.hdr[kHdrEmpty];
   const WaveRange rng = a.waves[grp * kWavesPerGroup + w];
   const GroupInfo gi0 = a.ginfo[grp];
   if ((grp >= ngroups) | (rng.count < 0) | (gi0.seg[0] < -1)) return;  // uniform over the workgroup
@@ -268,6 +271,10 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const uint32_t v_boff = (uint32_t)(r16 * P + 4 * g4) * 2;
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
+  // Fused KV append (k_new / v_new given): the step that holds token seq_len - 1
+  // takes that token's K and V from k_new / v_new instead of the pool, and the
+  // wave of the KV head's first head group writes them into the pool.
+  constexpr bool fuse_append = APPEND;
   int err = 0;
 
   int b = rng.b, u = rng.u, p = rng.p, left = rng.count, piece = 0;
@@ -291,6 +298,17 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       }
     }
     const size_t head_b = (size_t)g * tile_b;
+    // Rows of the appended token (only formed when there is one to append).
+    const size_t new_off = fuse_append ? ((size_t)b * a.num_kv_heads + g) * D : 0;
+    const char* knew_row = reinterpret_cast<const char*>(fuse_append ? a.k_new + new_off : a.k);
+    const uint16_t* vnew_row = fuse_append ? a.v_new + new_off : a.v;
+    const bool writer = hq0 % G == 0;  // first head group of KV head g
+    // V row of the appended token, two channels per lane, fetched when this
+    // piece reaches the request's last page.
+    uint32_t vnew2 = 0;
+    if constexpr (APPEND) {
+      if (p + len == n && lane < D / 2) vnew2 = reinterpret_cast<const uint32_t*>(vnew_row)[lane];
+    }
 
     for (int jb = 0; jb < len; jb += kWave) {
       const int nb = min(kWave, len - jb);
@@ -312,6 +330,12 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       // Step j of the block: page id (uniform) and loads.  Steps past the block
       // re-read its last step (a cache hit) and are never consumed, so the
       // issue sequence has no data-dependent branch.
+      // Token of step j that was appended in this call (0..15), or -1.
+      auto fresh_token = [&](int j) {
+        const int t0 = (p + jb + (j >> log2_s)) * P + (j & ((1 << log2_s) - 1)) * 16;
+        const int tok = L - 1 - t0;
+        return fuse_append && j < ns && tok >= 0 && tok < 16 ? tok : -1;
+      };
       auto issue = [&](int j, Step<D>& sd) {
         const int jc = j < ns ? j : ns - 1;
         const int pg = jc >> log2_s;
@@ -320,19 +344,68 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         const size_t base = (size_t)(pid < 0 ? 0 : pid) * a.num_kv_heads * tile_b + head_b;
         const char* kp = kbase + base + (size_t)sub * 16 * 16 + k_boff;
         const char* vp = vbase + base + (size_t)sub * 16 * 2 + v_boff;
+        const int tok = fresh_token(j);
+        // The lanes of the appended token read its K row from k_new.
+        const bool knew = tok >= 0 && r16 == tok;
+        const char* kq = knew ? knew_row + g4 * 16 : kp;
+        const size_t kstride = knew ? 4 * 16 : (size_t)4 * P * 16;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
-          sd.k[kk] = *reinterpret_cast<const uint4*>(kp + (size_t)kk * 4 * P * 16);
+          sd.k[kk] = *reinterpret_cast<const uint4*>(kq + (size_t)kk * kstride);
 #pragma unroll
         for (int vb = 0; vb < D / 16; ++vb)
           sd.v[vb] = *reinterpret_cast<const uint2*>(vp + (size_t)vb * 16 * P * 2);
       };
-      auto consume = [&](int j, const Step<D>& sd) {
+      auto consume = [&](int j, Step<D>& sd) {
         const int pg = j >> log2_s;
         const int sub = j & ((1 << log2_s) - 1);
         const int pid = __builtin_amdgcn_readlane(vpage, pg);
         const int t0 = (p + jb + pg) * P + sub * 16;
         const int live = pid < 0 ? 0 : min(16, max(0, L - t0));
+        const int tok = fresh_token(j);
+        if (!APPEND || tok < 0) {
+          st.step(sd, live, g4, a.scale_log2, bias);
+          return;
+        }
+        // Lanes whose four V tokens include the appended one take its value
+        // from v_new (in place: the ring slot is reloaded after this step).
+        // The row, fetched at the start of the piece two channels per lane,
+        // is passed between lanes through this wave's LDS row.  The KV head's
+        // first head group also writes the token into the pool (K row from
+        // the lanes that read it, V column from these lanes).
+        if (lane < D / 2) s_vn[w][lane] = vnew2;
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const uint16_t* vrow = reinterpret_cast<const uint16_t*>(&s_vn[w][0]);
+        uint16_t vn[D / 16];
+#pragma unroll
+        for (int vb = 0; vb < D / 16; ++vb) vn[vb] = vrow[16 * vb + r16];
+        const bool vlane = g4 == (tok >> 2);
+        const int shift = (tok & 1) * 16;
+        const uint32_t keep = ~(0xffffu << shift);
+#pragma unroll
+        for (int vb = 0; vb < D / 16; ++vb) {
+          const uint32_t nv = (uint32_t)vn[vb] << shift;
+          if (vlane) {
+            if (tok & 2) sd.v[vb].y = (sd.v[vb].y & keep) | nv;
+            else sd.v[vb].x = (sd.v[vb].x & keep) | nv;
+          }
+        }
+        if (writer && pid >= 0) {
+          const size_t base = (size_t)pid * a.num_kv_heads * tile_b + head_b;
+          const int off = sub * 16 + tok;  // token offset inside the page
+          if (r16 == tok) {
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk)
+              *reinterpret_cast<uint4*>(const_cast<char*>(kbase) + base +
+                                        ((size_t)(4 * kk + g4) * P + off) * 16) = sd.k[kk];
+          }
+          if (vlane) {
+#pragma unroll
+            for (int vb = 0; vb < D / 16; ++vb)
+              *reinterpret_cast<uint16_t*>(const_cast<char*>(vbase) + base +
+                                           ((size_t)(16 * vb + r16) * P + off) * 2) = vn[vb];
+          }
+        }
         st.step(sd, live, g4, a.scale_log2, bias);
       };
 
@@ -405,7 +478,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       }
     }
   }
-  if (grp == 0 && w == 0) {
+  if (nempty > 0 && grp == 0 && w == 0) {
     // Requests without tokens get zero rows (no tile covers them).
     for (int eb = lane; eb < a.batch; eb += kWave) {
       if (a.kv_indptr[eb + 1] == a.kv_indptr[eb]) {
@@ -635,13 +708,14 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool APPEND>
 hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
+  const dim3 grid(groups), block(kGroupThreads);
   switch (hg) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, 1>), dim3(groups), dim3(kGroupThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), dim3(groups), dim3(kGroupThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_kernel<D, 3>), dim3(groups), dim3(kGroupThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, 4>), dim3(groups), dim3(kGroupThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<D, 1, APPEND>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, APPEND>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<D, 3, APPEND>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, APPEND>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -651,8 +725,11 @@ hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int hg, int groups, hipStream_t s) {
   if (groups <= 0) return hipSuccess;
-  if (head_dim == 128) return launch_d<128>(a, hg, groups, s);
-  if (head_dim == 64) return launch_d<64>(a, hg, groups, s);
+  const bool append = a.k_new != nullptr;
+  if (head_dim == 128) return append ? launch_d<128, true>(a, hg, groups, s)
+                                     : launch_d<128, false>(a, hg, groups, s);
+  if (head_dim == 64) return append ? launch_d<64, true>(a, hg, groups, s)
+                                    : launch_d<64, false>(a, hg, groups, s);
   return hipErrorInvalidValue;
 }
 

@@ -25,6 +25,7 @@ enum HeaderWord : int {
   kHdrUnits = 2,       // head groups per request (U)
   kHdrBatch = 3,       // batch of the last pkv_build_metadata
   kHdrError = 4,       // error bits latched since the last metadata build
+  kHdrEmpty = 5,       // requests without tokens (their output rows are zeroed)
   kHdrWords = 64
 };
 
@@ -94,8 +95,10 @@ struct AppendArgs {
 };
 
 struct DecodeArgs {
-  const uint16_t* k;
-  const uint16_t* v;
+  uint16_t* k;              // written only by a fused append
+  uint16_t* v;
+  const uint16_t* k_new;    // [batch][Hkv][D] token to append, or null (no append)
+  const uint16_t* v_new;
   const uint16_t* q;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;

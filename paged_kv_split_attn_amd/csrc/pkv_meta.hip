@@ -79,18 +79,20 @@ struct Locator {
 __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
   __shared__ int smem[kMetaWaves];
   __shared__ int s_err;
+  __shared__ int s_empty;
   __shared__ int32_t s_ip[kMetaLdsRequests + 1];
   const int tid = threadIdx.x;
   const bool in_lds = a.batch <= kMetaLdsRequests;
   int err = 0;
   if (tid == 0) {
     s_err = 0;
+    s_empty = 0;
     s_ip[0] = 0;
     a.kv_indptr[0] = 0;
   }
 
   // Phase 1: kv_indptr = exclusive prefix sum of page counts.
-  int carry = 0;
+  int carry = 0, empty = 0;
   for (int base = 0; base < a.batch; base += kMetaThreads) {
     const int b = base + tid;
     int n = 0;
@@ -98,6 +100,7 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
       const int L = a.seq_lens[b];
       if (L < 0) err |= kErrNegativeLength;
       n = pages_of(L, a.page_size);
+      empty += n == 0;
     }
     int total;
     const int incl = block_inclusive_scan(n, smem, &total);
@@ -168,6 +171,7 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
   for (int sgi = tid; sgi < a.batch * U; sgi += kMetaThreads) a.counters[sgi] = 0;
 
   if (err) atomicOr(&s_err, err);
+  if (empty) atomicAdd(&s_empty, empty);
   __syncthreads();
   if (tid == 0) {
     // The metadata build starts a step: its bits replace the previous step's.
@@ -176,6 +180,7 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
     a.hdr[kHdrTiles] = (int)T;
     a.hdr[kHdrUnits] = U;
     a.hdr[kHdrBatch] = a.batch;
+    a.hdr[kHdrEmpty] = s_empty;
   }
 }
 
@@ -184,30 +189,32 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
 // store per chunk.  V tiles are channel-major ([D][P]), so a V row is a column
 // of its tile: eight 2-byte stores, page_size apart.
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
-  const int chunks = a.head_dim / 8;
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int c = (int)(idx % chunks);
-  long long rest = idx / chunks;
-  const int which = (int)(rest & 1);  // 0 = K, 1 = V
-  rest >>= 1;
-  const int h = (int)(rest % a.num_kv_heads);
-  const long long b = rest / a.num_kv_heads;
+  // 32-bit index arithmetic: the host checks that the grid fits.
+  const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t lc = a.head_dim == 128 ? 4u : 3u;  // log2 of 8-channel chunks per row
+  const int c = (int)(idx & ((1u << lc) - 1));
+  const uint32_t rest = idx >> (lc + 1);
+  const int which = (int)((idx >> lc) & 1);  // 0 = K, 1 = V
+  const int h = (int)(rest % (uint32_t)a.num_kv_heads);
+  const int b = (int)(rest / (uint32_t)a.num_kv_heads);
   if (b >= a.batch) return;
-  const int L = a.seq_lens[b];
-  if (L <= 0) return;
-  const int pos = L - 1;
-  const long long slot = (long long)a.kv_indptr[b] + pos / a.page_size;
-  if (slot < 0 || slot >= a.num_indices) return;
-  const int page = a.kv_indices[slot];
-  if (page < 0 || page >= a.num_pages) return;
+  // The length, the prefix sum and the new row are loaded together; only the
+  // page id waits for them.  Invalid entries read a clamped index and write
+  // nothing.
   const size_t src_off = ((size_t)b * a.num_kv_heads + h) * a.head_dim + (size_t)c * 8;
+  const int L = a.seq_lens[b];
+  const int ip = a.kv_indptr[b];
+  const uint4 w = *reinterpret_cast<const uint4*>((which == 0 ? a.k_new : a.v_new) + src_off);
+  const int pos = L - 1;
+  const long long slot = (long long)ip + (pos >= 0 ? pos / a.page_size : 0);
+  const bool slot_ok = L > 0 && slot >= 0 && slot < a.num_indices;
+  const int page = a.kv_indices[slot_ok ? slot : 0];
+  if (!slot_ok || page < 0 || page >= a.num_pages) return;
   const size_t tile = (((size_t)page * a.num_kv_heads + h) * a.page_size) * a.head_dim;
   const int off = pos % a.page_size;
   if (which == 0) {
-    *reinterpret_cast<uint4*>(a.k + tile + ((size_t)c * a.page_size + off) * 8) =
-        *reinterpret_cast<const uint4*>(a.k_new + src_off);
+    *reinterpret_cast<uint4*>(a.k + tile + ((size_t)c * a.page_size + off) * 8) = w;
   } else {
-    const uint4 w = *reinterpret_cast<const uint4*>(a.v_new + src_off);
     const uint32_t words[4] = {w.x, w.y, w.z, w.w};
     uint16_t* col = a.v + tile + (size_t)c * 8 * a.page_size + off;
 #pragma unroll

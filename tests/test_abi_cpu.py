@@ -24,7 +24,7 @@ def test_header_declares_expected_entry_points():
     names = pkv.declared_functions()
     assert set(names) == {
         "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
-        "pkv_append_kv", "pkv_decode", "pkv_debug_validate"}
+        "pkv_append_kv", "pkv_decode", "pkv_decode_append", "pkv_debug_validate"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -108,6 +108,9 @@ def test_host_checks_reject_before_launch(lib):
     pool_bad = pkv._CPool(100, 16, 4, 128, 0x1000, 0x2000)
     assert _raw(lib, "pkv_decode", B(pool_bad), B(d), fake, fake, fake, 10, fake, 4, 0.1, fake,
                 ws_bytes, fake, None) == 1
+    # fused append without its rows
+    assert _raw(lib, "pkv_decode_append", B(pool), B(d), fake, None, fake, fake, fake, 10, fake, 4,
+                0.1, fake, ws_bytes, fake, None) == 1
     # NaN scale
     assert _raw(lib, "pkv_decode", B(pool), B(d), fake, fake, fake, 10, fake, 4, float("nan"),
                 fake, ws_bytes, fake, None) == 1

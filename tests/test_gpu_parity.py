@@ -89,6 +89,43 @@ def test_append_bit_exact(which):
     assert np.array_equal(v, v_ref)
 
 
+# ------------------------------------------------------ fused append + decode
+
+FUSED_CASES = {  # name: (Hq, Hkv, D, P, lengths)
+    "g4_p16": (8, 2, 64, 16, [1, 15, 16, 17, 40, 33]),
+    "g8_p64": (32, 4, 128, 64, [100, 64, 65, 1, 300, 128]),
+    "g1_p32": (8, 8, 128, 32, [31, 32, 33, 2, 257]),
+}
+
+
+@pytest.mark.parametrize("case", ["c5"] + list(FUSED_CASES))
+@pytest.mark.parametrize("forced", [0, 3])
+def test_fused_append_decode_matches_separate(case, forced):
+    # pkv_decode_append must leave the pool and the output exactly as
+    # pkv_append_kv followed by pkv_decode does, and match the oracle.
+    say(f"fused append+decode {case} forced={forced}")
+    if case == "c5":
+        batch = cfg(5)
+    else:
+        Hq, Hkv, D, P, lens = FUSED_CASES[case]
+        batch = W.make_batch(name=case, seed=Hq + 7 * D + P, B=len(lens), Hq=Hq, Hkv=Hkv, D=D,
+                             P=P, lengths=np.array(lens), append=True)
+    desc = make_desc(batch, min_tiles=1)
+    sep = GpuRun(batch, desc)
+    sep_bits = sep.step(forced).copy()
+    fus = GpuRun(batch, desc)
+    fus.metadata(forced)
+    pkv.pkv_decode_append(fus.pool, desc, fus.t["q"], fus.t["k_new"], fus.t["v_new"],
+                          fus.kv_indptr, fus.t["kv_indices"], fus.t["seq_lens"], batch.sm_scale,
+                          fus.ws, fus.out)
+    torch.cuda.synchronize()
+    assert torch.equal(fus.t["k_pool"], sep.t["k_pool"]), "K pool differs"
+    assert torch.equal(fus.t["v_pool"], sep.t["v_pool"]), "V pool differs"
+    fus_bits = fus.out_bits()
+    assert np.array_equal(fus_bits, sep_bits), "fused output differs from append + decode"
+    compare(fus_bits, ref(5) if case == "c5" else oracle_out(batch), f"fused {case}")
+
+
 # -------------------------------------------------------------------- decode
 
 DECODE_CASES = [  # (workload, grid size (0 = one per CU), forced workgroups (0 = planner))
