@@ -605,9 +605,17 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     const int sgm = s_glob[k];
     int merge = -1;
     if (sgm >= 0 && !(k == 1 && sgm == s_glob[0])) {
+      // The last arrival of a call brings the counter to a multiple of the
+      // contributor count n (the metadata build zeroes it).  That workgroup
+      // takes n off again at once (no result needed), so the counter is back
+      // at zero by the end of the call without a store at the end of the merge.
+      const int n = hi_of(k) - lo_of(k) + 1;
       const int old = __hip_atomic_fetch_add(&counters_p[sgm], 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-      if (old == hi_of(k) - lo_of(k)) merge = sgm;
+      if ((old + 1) % n == 0) {
+        merge = sgm;
+        __hip_atomic_fetch_add(&counters_p[sgm], -n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     s_merge[k] = merge;
   }
@@ -703,8 +711,6 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       *reinterpret_cast<uint2*>(a.out + ((size_t)eb * Hq + hq) * D + c) =
           make_uint2(pack_bf16x2(val.x, val.y), pack_bf16x2(val.z, val.w));
     }
-    if (tid == 0)
-      __hip_atomic_store(&counters_p[msg[k]], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
