@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append", choices=("fused", "separate"), default="fused",
                     help="KV append fused into the decode launch, or its own launch")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured hipGraph (one graph per pool copy)")
     ap.add_argument("--no-kernel-loop", action="store_true",
                     help="time only whole steps (skip the decode-only loop)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -186,15 +188,18 @@ def main():
     k_new, v_new = base["k_new"], base["v_new"]
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step_on(i, st):
         pool, q = copies[i % ncopies]
-        pkv.pkv_build_metadata(desc, seq, 0, kv_indptr, ws, stream)
+        pkv.pkv_build_metadata(desc, seq, 0, kv_indptr, ws, st)
         if args.append == "fused":
             pkv.pkv_decode_append(pool, desc, q, k_new, v_new, kv_indptr, idx, seq,
-                                  batch.sm_scale, ws, out, stream)
+                                  batch.sm_scale, ws, out, st)
         else:
-            pkv.pkv_append_kv(pool, k_new, v_new, kv_indptr, idx, seq, stream)
-            pkv.pkv_decode(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, stream)
+            pkv.pkv_append_kv(pool, k_new, v_new, kv_indptr, idx, seq, st)
+            pkv.pkv_decode(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, st)
+
+    def step(i):
+        step_on(i, stream)
 
     def decode_only(i):
         pool, q = copies[i % ncopies]
@@ -208,7 +213,23 @@ def main():
         raise RuntimeError("device metadata failed validation")
 
     K = args.steps
-    ms_step = timed(stream, K, step)
+    if args.graph:
+        # One graph per pool copy, captured on a side stream after the eager
+        # warm-up; replays run on the timing stream.
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        for i in range(ncopies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    step_on(i, cap)
+            graphs.append(g)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        ms_step = timed(stream, K, lambda i: graphs[i % ncopies].replay())
+    else:
+        ms_step = timed(stream, K, step)
 
     call_bytes, step_bytes = algorithmic_bytes(batch)
     res = {
@@ -229,6 +250,7 @@ def main():
                    "kv_tokens": batch.kv_tokens, "pool_pages": batch.num_pages,
                    "pool_copies": ncopies, "decode_grid": desc.groups(),
                    "plan_workgroups": plan["groups"], "append": args.append,
+                   "graph": bool(args.graph),
                    "parallelism": "single-gpu"},
         "step_bytes": step_bytes,
         "call_bytes": call_bytes,

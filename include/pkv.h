@@ -169,7 +169,8 @@ int pkv_build_metadata(const pkv_desc* desc, const int32_t* seq_lens, int32_t ba
  *   K[kv_indices[kv_indptr[b] + pos / P]][h][pos % P][:] = k_new[b][h][:], same for V.
  *  k_new, v_new   device bf16 [batch][num_kv_heads][head_dim]
  *  kv_indptr      device int32 [batch + 1] (from pkv_build_metadata)
- *  kv_indices     device int32 [num_indices], physical page ids
+ *  kv_indices     device int32 [num_indices], physical page ids (may be NULL
+ *                 when num_indices is 0)
  *  seq_lens       device int32 [batch], post-append lengths; <= 0 writes nothing
  * Two requests must not target the same slot (the writes would race).
  * Page ids outside [0, num_pages) or index positions outside [0, num_indices)
@@ -184,7 +185,7 @@ int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
 /* Decode attention for one layer (one kernel launch).
  *  q            device bf16 [batch][num_q_heads][head_dim], contiguous
  *  kv_indptr    device int32 [batch + 1] written by pkv_build_metadata this step
- *  kv_indices   device int32 [num_indices]
+ *  kv_indices   device int32 [num_indices] (may be NULL when num_indices is 0)
  *  seq_lens     device int32 [batch], the same array pkv_build_metadata read
  *  sm_scale     softmax scale (usually 1 / sqrt(head_dim))
  *  workspace    the workspace pkv_build_metadata wrote this step

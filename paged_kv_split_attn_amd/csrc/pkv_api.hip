@@ -148,7 +148,7 @@ int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
                   const int32_t* seq_lens, int32_t batch, void* stream) {
   int st = check_pool(pool, nullptr);
   if (st != PKV_OK) return st;
-  if (!k_new || !v_new || !kv_indptr || !kv_indices || !seq_lens || batch < 0 ||
+  if (!k_new || !v_new || !kv_indptr || (num_indices > 0 && !kv_indices) || !seq_lens || batch < 0 ||
       num_indices < 0 || pool->page_size < 1 || pool->num_kv_heads < 1)
     return PKV_ERR_INVALID_ARG;
   if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
@@ -187,7 +187,8 @@ int decode_impl(const pkv_pool* pool, const pkv_desc* desc, const void* q, const
   if (st != PKV_OK) return st;
   st = check_pool(pool, desc);
   if (st != PKV_OK) return st;
-  if (!q || !kv_indptr || !kv_indices || !seq_lens || !workspace || !out || batch < 0 ||
+  if (!q || !kv_indptr || (num_indices > 0 && !kv_indices) || !seq_lens || !workspace || !out ||
+      batch < 0 ||
       num_indices < 0 || !(sm_scale == sm_scale) || (k_new == nullptr) != (v_new == nullptr))
     return PKV_ERR_INVALID_ARG;
   if (batch > desc->max_batch) return PKV_ERR_CAPACITY;

@@ -249,7 +249,22 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const int nempty = a.hdr[kHdrEmpty];
   const WaveRange rng = a.waves[grp * kWavesPerGroup + w];
   const GroupInfo gi0 = a.ginfo[grp];
-  if ((grp >= ngroups) | (rng.count < 0) | (gi0.seg[0] < -1)) return;  // uniform over the workgroup
+  // Requests without tokens get zero rows (no tile covers them); workgroup 0
+  // writes them, after its stream, or at once when the plan has no tile at all.
+  auto zero_empty_rows = [&]() {
+    if (nempty > 0 && w == 0) {
+      for (int eb = lane; eb < a.batch; eb += kWave) {
+        if (a.kv_indptr[eb + 1] == a.kv_indptr[eb]) {
+          uint4* row = reinterpret_cast<uint4*>(a.out + (size_t)eb * Hq * D);
+          for (int i = 0; i < Hq * D / 8; ++i) row[i] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+  if ((grp >= ngroups) | (rng.count < 0) | (gi0.seg[0] < -1)) {  // uniform over the workgroup
+    if (grp == 0) zero_empty_rows();
+    return;
+  }
   if (tid == 0) {  // parked in LDS until the epilogue
     s_gi = gi0;
     s_ptr = EpiloguePtrs{a.hdr, a.counters, a.lse, a.opart};
@@ -318,7 +333,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       {
         const int pos = ip0 + p + jb + lane;
         const bool pos_ok = pos >= 0 && pos < a.num_indices;
-        const int pid = a.kv_indices[pos_ok ? pos : 0];
+        const int pid = pos_ok ? a.kv_indices[pos] : -1;
         if (lane < nb) {
           if (!pos_ok) err |= kErrBadIndexPos;
           else if (pid < 0 || pid >= a.num_pages) err |= kErrBadPageId;
@@ -478,15 +493,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       }
     }
   }
-  if (nempty > 0 && grp == 0 && w == 0) {
-    // Requests without tokens get zero rows (no tile covers them).
-    for (int eb = lane; eb < a.batch; eb += kWave) {
-      if (a.kv_indptr[eb + 1] == a.kv_indptr[eb]) {
-        uint4* row = reinterpret_cast<uint4*>(a.out + (size_t)eb * Hq * D);
-        for (int i = 0; i < Hq * D / 8; ++i) row[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
+  if (grp == 0) zero_empty_rows();
   __syncthreads();  // also publishes s_gi and s_ptr, written before the loop
   const GroupInfo gi = s_gi;
   float* const lse_p = uniform_ptr(s_ptr.lse);

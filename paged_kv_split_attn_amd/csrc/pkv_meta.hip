@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   const int pos = L - 1;
   const long long slot = (long long)ip + (pos >= 0 ? pos / a.page_size : 0);
   const bool slot_ok = L > 0 && slot >= 0 && slot < a.num_indices;
-  const int page = a.kv_indices[slot_ok ? slot : 0];
+  const int page = slot_ok ? a.kv_indices[slot] : -1;
   if (!slot_ok || page < 0 || page >= a.num_pages) return;
   const size_t tile = (((size_t)page * a.num_kv_heads + h) * a.page_size) * a.head_dim;
   const int off = pos % a.page_size;

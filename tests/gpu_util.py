@@ -58,6 +58,11 @@ class GpuRun:
         pkv.pkv_decode(self.pool, self.desc, self.t["q"], self.kv_indptr, self.t["kv_indices"],
                        self.t["seq_lens"], self.batch.sm_scale, self.ws, self.out)
 
+    def decode_append(self):
+        pkv.pkv_decode_append(self.pool, self.desc, self.t["q"], self.t["k_new"], self.t["v_new"],
+                              self.kv_indptr, self.t["kv_indices"], self.t["seq_lens"],
+                              self.batch.sm_scale, self.ws, self.out)
+
     def step(self, forced=0):
         self.metadata(forced)
         if self.batch.append:

@@ -205,6 +205,39 @@ def test_zero_length_requests_give_zero_rows():
     compare(got, oracle_out(batch), "zero-length mix")
 
 
+def test_all_requests_empty():
+    # no tile at all: the plan uses no workgroup and every output row is zero
+    say("all empty")
+    batch = W.make_batch(name="allzero", seed=8, B=6, Hq=8, Hkv=2, D=64, P=16,
+                         lengths=np.zeros(6, dtype=np.int64), num_pages=8)
+    run = GpuRun(batch, make_desc(batch))
+    got = run.step()
+    info = run.validate()
+    assert info["status"] == pkv.PKV_OK and info["groups"] == 0
+    assert not got.any()
+
+
+def test_batch_beyond_metadata_lds():
+    # more requests than the metadata kernel keeps in LDS (8192): the prefix sums
+    # are then searched in global memory
+    say("batch of 10000")
+    rng = np.random.default_rng(123)
+    lens = rng.integers(0, 40, size=10000)
+    batch = W.make_batch(name="big_b", seed=124, B=10000, Hq=8, Hkv=2, D=64, P=16, lengths=lens,
+                         poison=False)
+    desc = make_desc(batch)
+    run = GpuRun(batch, desc)
+    got = run.step()
+    ip = run.kv_indptr.cpu().numpy()
+    assert np.array_equal(ip, oracle.kv_indptr(batch.seq_lens, batch.P))
+    info = run.validate()
+    assert info["status"] == pkv.PKV_OK
+    plan = oracle_plan(batch, desc)
+    assert info["groups"] == plan["groups"]
+    assert np.array_equal(np.array(info["waves"]), plan["waves"])
+    compare(got, oracle_out(batch), "B=10000")
+
+
 def test_deterministic_and_page_permutation_invariant():
     say("determinism / permutation cfg3")
     batch = cfg(3)
@@ -232,8 +265,9 @@ def test_bad_page_id_is_skipped_and_reported():
     compare(got[[0, 2]], expect[[0, 2]], "untouched requests")
 
 
-def test_graph_capture_replay_matches_eager():
-    say("graph replay")
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_graph_capture_replay_matches_eager(fused):
+    say(f"graph replay fused={fused}")
     batch = W.make_batch(name="graph", seed=9, B=8, Hq=32, Hkv=8, D=128, P=16,
                          lengths=np.array([3000, 1, 700, 2048, 16, 4096, 999, 64]), append=True)
     desc = make_desc(batch)
@@ -248,8 +282,11 @@ def test_graph_capture_replay_matches_eager():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run.metadata()
-        run.append()
-        run.decode()
+        if fused:
+            run.decode_append()
+        else:
+            run.append()
+            run.decode()
     hk, hv = batch.k_pool.copy(), batch.v_pool.copy()
     for rep in range(4):
         lens = np.maximum(1, (full * rng.uniform(0.2, 1.0, size=batch.B)).astype(np.int32))
