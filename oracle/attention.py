@@ -63,6 +63,7 @@ __all__ = [
     "gather_request",
     "softmax_attend",
     "decode",
+    "decode_masked",
     "chunk_partial",
     "merge_partials",
     "even_page_ranges",
@@ -134,6 +135,34 @@ def decode(q_bits, k_pool, v_pool, indptr, indices, seq_lens, sm_scale: float, P
         L = int(seq_lens[b])
         Kd = gather_request(k_pool, indptr, indices, b, L, P)
         Vd = gather_request(v_pool, indptr, indices, b, L, P)
+        for hq in range(Hq):
+            h = kv_head_of(hq, G)
+            out[b, hq] = softmax_attend(q[b, hq], Kd[:, h, :], Vd[:, h, :], sm_scale)
+    return out
+
+
+def decode_masked(q_bits, k_pool, v_pool, indptr, indices, seq_lens, sm_scale: float, P: int,
+                  mask) -> np.ndarray:
+    """Decode attention with a per-token keep mask -> float64 [B, Hq, D].
+
+    ``mask`` is bool [B, S] with S at least every seq_len; True keeps the token
+    (the optional 2-D mask [batch, max_seq_len], True = keep, of the paged
+    decode wrapper: AstrAI compare v1.3.12..6f09b1d, attention_ops.py,
+    attn_paged_decode docstring).  Token t of request b attends iff t < seq_len
+    and mask[b, t]; mask entries past seq_len are ignored.  A request that keeps
+    no token gets a zero row, as an empty request does.
+    """
+    q = bf16_to_f64(q_bits)
+    B, Hq, D = q.shape
+    Hkv = np.asarray(k_pool).shape[1]
+    G = Hq // Hkv
+    keep_all = np.asarray(mask, dtype=bool)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        keep = keep_all[b, :L]
+        Kd = gather_request(k_pool, indptr, indices, b, L, P)[keep]
+        Vd = gather_request(v_pool, indptr, indices, b, L, P)[keep]
         for hq in range(Hq):
             h = kv_head_of(hq, G)
             out[b, hq] = softmax_attend(q[b, hq], Kd[:, h, :], Vd[:, h, :], sm_scale)

@@ -16,7 +16,11 @@ mathematics of softmax attention and from invariants the method must keep:
 8. integer parts: kv_indptr page counts bracket the lengths, the split plan
    equals a search-based re-derivation of its rule, the append writes exactly
    the slot of the newest token;
-9. NaN poison in free pages and past-the-end slots never reaches an output.
+9. NaN poison in free pages and past-the-end slots never reaches an output;
+10. the keep mask: brute force over the kept tokens only, an all-true mask is the
+    unmasked decode bit for bit, an all-false row is zero, masking a request's
+    newest token equals decoding one token shorter, and mask entries past
+    seq_len change nothing.
 
 ``test_planted_mistakes`` plants plausible mistakes in the oracle (on the CPU)
 and checks that at least one pin fails for each.
@@ -350,9 +354,67 @@ def pin_poison(mod):
         assert np.isfinite(out).all()
 
 
+# -------------------------------------------------------------- mask (pin 10)
+
+def brute_force_masked(batch, mask):
+    """Pin-1 brute force over the kept tokens only (its own walk of the pages)."""
+    B, Hq, Hkv, D = batch.B, batch.Hq, batch.Hkv, batch.D
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        slots = [s for t, s in enumerate(_token_slots(batch, b)) if mask[b][t]]
+        if not slots:
+            continue
+        for hq in range(Hq):
+            h = (hq * Hkv) // Hq
+            qv = [_bf16_py(batch.q[b, hq, d]) for d in range(D)]
+            xs = [batch.sm_scale * math.fsum(a * _bf16_py(batch.k_pool[p, h, o, d])
+                                             for d, a in enumerate(qv)) for p, o in slots]
+            m = max(xs)
+            ws = [math.exp(x - m) for x in xs]
+            den = math.fsum(ws)
+            for d in range(D):
+                out[b, hq, d] = math.fsum(w * _bf16_py(batch.v_pool[p, h, o, d])
+                                          for w, (p, o) in zip(ws, slots)) / den
+    return out
+
+
+def run_masked(mod, batch, mask):
+    ip = mod.kv_indptr(batch.seq_lens, batch.P)
+    return mod.decode_masked(batch.q, batch.k_pool, batch.v_pool, ip, batch.kv_indices,
+                             batch.seq_lens, batch.sm_scale, batch.P, mask)
+
+
+def pin_mask(mod):
+    batch = tiny_batch(seed=21)
+    S = int(batch.seq_lens.max()) + 5
+    rng = np.random.default_rng(22)
+    mask = rng.random((batch.B, S)) < 0.6
+    mask[1, :] = False  # a request that keeps nothing
+    got = run_masked(mod, batch, mask)
+    assert np.max(np.abs(got - brute_force_masked(batch, mask))) < 1e-12
+    assert not got[1].any()
+    # all kept: the unmasked decode, bit for bit
+    assert np.array_equal(run_masked(mod, batch, np.ones((batch.B, S), bool)), run_decode(mod, batch))
+    # entries past seq_len are ignored
+    tail = mask.copy()
+    for b in range(batch.B):
+        tail[b, int(batch.seq_lens[b]):] = ~tail[b, int(batch.seq_lens[b]):]
+    assert np.array_equal(run_masked(mod, batch, tail), got)
+    # masking the newest token of every request = decoding one token shorter
+    g8 = gqa8_batch(seed=23)
+    S8 = int(g8.seq_lens.max())
+    newest = np.ones((g8.B, S8), bool)
+    for b in range(g8.B):
+        newest[b, int(g8.seq_lens[b]) - 1] = False
+    ip = mod.kv_indptr(g8.seq_lens, g8.P)
+    short = mod.decode(g8.q, g8.k_pool, g8.v_pool, ip, g8.kv_indices, g8.seq_lens - 1,
+                       g8.sm_scale, g8.P)
+    assert np.array_equal(run_masked(mod, g8, newest), short)
+
+
 PINS = [pin_brute_force, pin_seq_len_one, pin_permutation, pin_split_invariance, pin_q_zero,
         pin_constant_v, pin_dominant_key, pin_sdpa, pin_kv_indptr, pin_plan, pin_stream_pieces,
-        pin_append, pin_poison]
+        pin_append, pin_poison, pin_mask]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -452,6 +514,16 @@ def _mutants():
         return OA.__dict__["_orig_append_kv"](k_pool, v_pool, k_new, v_new, indptr, indices,
                                               np.asarray(seq_lens) + 1, P)
     m["append_one_slot_late"] = {"append_kv": append_at_len}
+
+    def masked_inverted(q, k, v, ip, idx, sl, sc, P, mask):
+        return OA.__dict__["_orig_decode_masked"](q, k, v, ip, idx, sl, sc, P,
+                                                  ~np.asarray(mask, bool))
+    m["mask_inverted"] = {"decode_masked": masked_inverted}
+
+    def masked_shifted(q, k, v, ip, idx, sl, sc, P, mask):
+        return OA.__dict__["_orig_decode_masked"](q, k, v, ip, idx, sl, sc, P,
+                                                  np.roll(np.asarray(mask, bool), 1, axis=1))
+    m["mask_shifted_one_token"] = {"decode_masked": masked_shifted}
     return m
 
 
@@ -460,7 +532,8 @@ MUTANTS = _mutants()
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistakes(name, monkeypatch):
-    for fn in ("softmax_attend", "chunk_partial", "plan_stream", "decode_pieces", "append_kv"):
+    for fn in ("softmax_attend", "chunk_partial", "plan_stream", "decode_pieces", "append_kv",
+               "decode_masked"):
         monkeypatch.setitem(OA.__dict__, "_orig_" + fn, getattr(OA, fn))
     for attr, repl in MUTANTS[name].items():
         monkeypatch.setattr(OA, attr, repl)
