@@ -53,6 +53,8 @@ def parse():
                     help="KV append fused into the decode launch, or its own launch")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured hipGraph (one graph per pool copy)")
+    ap.add_argument("--mask-keep", type=float, default=None, metavar="P",
+                    help="also time pkv_decode_masked with a random keep mask of density P")
     ap.add_argument("--no-kernel-loop", action="store_true",
                     help="time only whole steps (skip the decode-only loop)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -270,6 +272,18 @@ def main():
                          "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
         })
+    if args.mask_keep is not None:
+        S = -(-int(batch.seq_lens.max()) // 4) * 4
+        rng = np.random.default_rng(np.random.PCG64(2000 + args.config))
+        mask = torch.from_numpy((rng.random((batch.B, S)) < args.mask_keep).astype(np.uint8)).to(dev)
+
+        def masked_only(i):
+            pool, q = copies[i % ncopies]
+            pkv.pkv_decode_masked(pool, desc, q, mask, kv_indptr, idx, seq, batch.sm_scale, ws,
+                                  out, stream)
+        masked_ms = timed(stream, K, masked_only)
+        res["masked"] = {"keep": args.mask_keep, "us_per_call": round(masked_ms * 1e3, 2),
+                         "GBps": round((call_bytes + batch.B * S) / (masked_ms * 1e-3) / 1e9, 1)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)

@@ -218,6 +218,24 @@ int pkv_decode_append(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                       int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
                       void* out, void* stream);
 
+/* Decode attention with a per-token keep mask (one launch): the optional 2-D
+ * bool mask [batch, max_seq_len], True = keep, of the pages' paged decode
+ * wrapper (attention_ops.py, attn_paged_decode docstring, on the compare page).
+ * Token t of request b attends iff t < seq_lens[b] and mask[b * mask_stride + t]
+ * is nonzero; a request that keeps no token gets a zero row.
+ *  mask          device uint8 [batch][mask_stride]; row b must hold at least
+ *                seq_lens[b] entries (entries past seq_lens[b] are ignored;
+ *                reads past batch * mask_stride bytes return 0)
+ *  mask_stride   bytes between rows, a multiple of 4, with
+ *                batch * mask_stride < 2^31
+ * Every other argument is as for pkv_decode.  Errors: those of pkv_decode, and
+ * PKV_ERR_INVALID_ARG for a NULL mask or a bad stride. */
+int pkv_decode_masked(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                      const uint8_t* mask, int32_t mask_stride, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, int32_t num_indices, const int32_t* seq_lens,
+                      int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
+                      void* out, void* stream);
+
 /* Debug only (synchronises the stream; not capturable).  Checks device
  * metadata and copies the plan to host memory.
  *  groups_out   host int32 or NULL: workgroups the plan uses (W above)

@@ -35,6 +35,7 @@ __all__ = [
     "pkv_append_kv",
     "pkv_decode",
     "pkv_decode_append",
+    "pkv_decode_masked",
     "pkv_debug_validate",
     "WAVES_PER_GROUP",
     "PKV_OK",
@@ -108,6 +109,9 @@ _SIGNATURES = {
                                   _vp]),
     "pkv_decode_append": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp,
                                          _vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
+                                         ctypes.c_size_t, _vp, _vp]),
+    "pkv_decode_masked": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp,
+                                         _i32, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
                                          ctypes.c_size_t, _vp, _vp]),
     "pkv_debug_validate": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _vp, _vp, _i32, _i32, _i32,
                                           _vp, ctypes.c_size_t, _i32p, _i32p, _vp]),
@@ -281,6 +285,25 @@ def pkv_decode_append(pool: Pool, desc: Desc, q: torch.Tensor, k_new: torch.Tens
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(out, "out", _BF16, n), _stream(stream))
     _check("pkv_decode_append", st)
+
+
+def pkv_decode_masked(pool: Pool, desc: Desc, q: torch.Tensor, mask: torch.Tensor,
+                      kv_indptr: torch.Tensor, kv_indices: torch.Tensor, seq_lens: torch.Tensor,
+                      sm_scale: float, workspace: torch.Tensor, out: torch.Tensor,
+                      stream=None) -> None:
+    """Decode with a keep mask: bool or uint8 [batch, S], S a multiple of 4."""
+    B = seq_lens.numel()
+    n = B * desc.num_q_heads * desc.head_dim
+    if mask.dim() != 2 or mask.shape[0] != B:
+        raise ValueError(f"mask must be [batch, S], got {tuple(mask.shape)}")
+    st = load_library().pkv_decode_masked(
+        ctypes.byref(pool.c()), ctypes.byref(desc.c()), _ptr(q, "q", _BF16, n),
+        _ptr(mask, "mask", (torch.bool, torch.uint8)), int(mask.shape[1]),
+        _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
+        kv_indices.numel(), _ptr(seq_lens, "seq_lens", _I32), B, float(sm_scale),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, "out", _BF16, n), _stream(stream))
+    _check("pkv_decode_masked", st)
 
 
 def pkv_debug_validate(desc: Desc, seq_lens: torch.Tensor, kv_indptr: torch.Tensor,

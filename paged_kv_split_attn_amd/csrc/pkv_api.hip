@@ -109,7 +109,7 @@ const char* pkv_status_str(int status) {
   }
 }
 
-int32_t pkv_version(void) { return (2 << 16) | 1; }
+int32_t pkv_version(void) { return (2 << 16) | 2; }
 
 size_t pkv_workspace_bytes(const pkv_desc* desc) {
   WsLayout L;
@@ -179,9 +179,10 @@ namespace {
 // pkv_decode and pkv_decode_append: the same launch, with or without the
 // token to append.
 int decode_impl(const pkv_pool* pool, const pkv_desc* desc, const void* q, const void* k_new,
-                const void* v_new, const int32_t* kv_indptr, const int32_t* kv_indices,
-                int32_t num_indices, const int32_t* seq_lens, int32_t batch, float sm_scale,
-                void* workspace, size_t workspace_bytes, void* out, void* stream) {
+                const void* v_new, const uint8_t* mask, int32_t mask_stride,
+                const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
+                const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
+                size_t workspace_bytes, void* out, void* stream) {
   WsLayout L;
   int st = check_desc(desc, &L);
   if (st != PKV_OK) return st;
@@ -193,8 +194,13 @@ int decode_impl(const pkv_pool* pool, const pkv_desc* desc, const void* q, const
     return PKV_ERR_INVALID_ARG;
   if (batch > desc->max_batch) return PKV_ERR_CAPACITY;
   if (workspace_bytes < L.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (mask && (mask_stride < 0 || mask_stride % 4 != 0 ||
+               (long long)mask_stride * batch > 0x7fffffffLL))
+    return PKV_ERR_INVALID_ARG;
   if (batch == 0) return PKV_OK;
   DecodeArgs d;
+  d.mask = mask;
+  d.mask_stride = mask ? mask_stride : 0;
   d.k = static_cast<uint16_t*>(pool->k);
   d.v = static_cast<uint16_t*>(pool->v);
   d.k_new = static_cast<const uint16_t*>(k_new);
@@ -232,8 +238,20 @@ int pkv_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
                const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
                size_t workspace_bytes, void* out, void* stream) {
-  return decode_impl(pool, desc, q, nullptr, nullptr, kv_indptr, kv_indices, num_indices,
-                     seq_lens, batch, sm_scale, workspace, workspace_bytes, out, stream);
+  return decode_impl(pool, desc, q, nullptr, nullptr, nullptr, 0, kv_indptr, kv_indices,
+                     num_indices, seq_lens, batch, sm_scale, workspace, workspace_bytes, out,
+                     stream);
+}
+
+int pkv_decode_masked(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                      const uint8_t* mask, int32_t mask_stride, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, int32_t num_indices, const int32_t* seq_lens,
+                      int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
+                      void* out, void* stream) {
+  if (!mask) return PKV_ERR_INVALID_ARG;
+  return decode_impl(pool, desc, q, nullptr, nullptr, mask, mask_stride, kv_indptr, kv_indices,
+                     num_indices, seq_lens, batch, sm_scale, workspace, workspace_bytes, out,
+                     stream);
 }
 
 int pkv_decode_append(const pkv_pool* pool, const pkv_desc* desc, const void* q,
@@ -242,8 +260,8 @@ int pkv_decode_append(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                       int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
                       void* out, void* stream) {
   if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
-  return decode_impl(pool, desc, q, k_new, v_new, kv_indptr, kv_indices, num_indices, seq_lens,
-                     batch, sm_scale, workspace, workspace_bytes, out, stream);
+  return decode_impl(pool, desc, q, k_new, v_new, nullptr, 0, kv_indptr, kv_indices, num_indices,
+                     seq_lens, batch, sm_scale, workspace, workspace_bytes, out, stream);
 }
 
 int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int32_t* kv_indptr,

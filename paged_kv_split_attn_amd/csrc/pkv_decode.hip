@@ -101,7 +101,12 @@ template <int D>
 struct Step {
   uint4 k[D / 32];  // K of token r, channels 8*(4kk + g) .. +8 (A of q.K, block kk)
   uint2 v[D / 16];  // V^T: channel 16*nb + r, tokens 4g .. 4g+3 (B of p.V)
+  uint32_t keep;    // masked decode: keep bytes of tokens 4g .. 4g+3
 };
+
+// Kernel variants: plain decode, KV append fused into the decode, decode with
+// a per-token keep mask.
+enum Kind : int { kPlain = 0, kAppend = 1, kMasked = 2 };
 
 template <int D, int HG>
 struct MfmaWave {
@@ -122,7 +127,7 @@ struct MfmaWave {
   // `g` = lane / 16; `bias` = 0 for heads < HG, -inf otherwise.
   template <class S>
   __device__ __forceinline__ void step(const S& st, int live, int g, float scale_log2,
-                                       float bias) {
+                                       float bias, uint32_t keep = 0x01010101u) {
     floatx4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk)
@@ -150,6 +155,11 @@ struct MfmaWave {
         vv[nb].y &= m1;
       }
     }
+    // Keep mask: byte i of `keep` is zero for a dropped token 4g + i (its V is
+    // real data, so a zero weight suffices).
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (((keep >> (8 * i)) & 0xffu) == 0) s[i] = kMinusInf;
     // Step max of head r over its 16 tokens (4 per lane, 4 lanes).
     float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     pm = fmaxf(pm, __shfl_xor(pm, 16, kWave));
@@ -215,8 +225,10 @@ struct Combine4 {
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kCoherent = 16;
 
-template <int D, int HG, bool APPEND>
+template <int D, int HG, int KIND>
 __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
+  constexpr bool APPEND = KIND == kAppend;
+  constexpr bool MASKED = KIND == kMasked;
   constexpr int kStages = 2;  // register ring: steps in flight per wave
   constexpr int kOut = (HG * D + kGroupThreads - 1) / kGroupThreads;  // outputs per thread
 
@@ -290,6 +302,11 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // takes that token's K and V from k_new / v_new instead of the pool, and the
   // wave of the KV head's first head group writes them into the pool.
   constexpr bool fuse_append = APPEND;
+  // Keep mask of the masked variant: bytes [batch][mask_stride] behind a
+  // bounds-checked buffer resource (reads past the end return 0).
+  const __amdgpu_buffer_rsrc_t mask_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(MASKED ? a.mask : reinterpret_cast<const uint8_t*>(a.q)), 0,
+      MASKED ? a.mask_stride * a.batch : 0, kBufferWord3);
   int err = 0;
 
   int b = rng.b, u = rng.u, p = rng.p, left = rng.count, piece = 0;
@@ -318,6 +335,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     const char* knew_row = reinterpret_cast<const char*>(fuse_append ? a.k_new + new_off : a.k);
     const uint16_t* vnew_row = fuse_append ? a.v_new + new_off : a.v;
     const bool writer = hq0 % G == 0;  // first head group of KV head g
+    const int mask_row = MASKED ? b * a.mask_stride : 0;  // byte offset of request b's keep row
     // V row of the appended token, two channels per lane, fetched when this
     // piece reaches the request's last page.
     uint32_t vnew2 = 0;
@@ -370,6 +388,12 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int vb = 0; vb < D / 16; ++vb)
           sd.v[vb] = *reinterpret_cast<const uint2*>(vp + (size_t)vb * 16 * P * 2);
+        if constexpr (MASKED) {
+          // Keep bytes of this lane's four tokens; a row shorter than the
+          // request reads 0 (dropped) past the end of the mask buffer.
+          const int t0 = (p + jb + pg) * P + sub * 16 + 4 * g4;
+          sd.keep = __builtin_amdgcn_raw_buffer_load_b32(mask_rs, mask_row + t0, 0, 0);
+        }
       };
       auto consume = [&](int j, Step<D>& sd) {
         const int pg = j >> log2_s;
@@ -378,6 +402,10 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         const int t0 = (p + jb + pg) * P + sub * 16;
         const int live = pid < 0 ? 0 : min(16, max(0, L - t0));
         const int tok = fresh_token(j);
+        if constexpr (MASKED) {
+          st.step(sd, live, g4, a.scale_log2, bias, sd.keep);
+          return;
+        }
         if (!APPEND || tok < 0) {
           st.step(sd, live, g4, a.scale_log2, bias);
           return;
@@ -721,14 +749,14 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, bool APPEND>
+template <int D, int KIND>
 hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
   const dim3 grid(groups), block(kGroupThreads);
   switch (hg) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, 1, APPEND>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, APPEND>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_kernel<D, 3, APPEND>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, APPEND>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<D, 1, KIND>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, KIND>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<D, 3, KIND>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, KIND>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -738,11 +766,17 @@ hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int hg, int groups, hipStream_t s) {
   if (groups <= 0) return hipSuccess;
-  const bool append = a.k_new != nullptr;
-  if (head_dim == 128) return append ? launch_d<128, true>(a, hg, groups, s)
-                                     : launch_d<128, false>(a, hg, groups, s);
-  if (head_dim == 64) return append ? launch_d<64, true>(a, hg, groups, s)
-                                    : launch_d<64, false>(a, hg, groups, s);
+  const int kind = a.k_new != nullptr ? kAppend : (a.mask != nullptr ? kMasked : kPlain);
+  if (head_dim == 128) {
+    if (kind == kAppend) return launch_d<128, kAppend>(a, hg, groups, s);
+    if (kind == kMasked) return launch_d<128, kMasked>(a, hg, groups, s);
+    return launch_d<128, kPlain>(a, hg, groups, s);
+  }
+  if (head_dim == 64) {
+    if (kind == kAppend) return launch_d<64, kAppend>(a, hg, groups, s);
+    if (kind == kMasked) return launch_d<64, kMasked>(a, hg, groups, s);
+    return launch_d<64, kPlain>(a, hg, groups, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -99,6 +99,8 @@ struct DecodeArgs {
   uint16_t* v;
   const uint16_t* k_new;    // [batch][Hkv][D] token to append, or null (no append)
   const uint16_t* v_new;
+  const uint8_t* mask;      // [batch][mask_stride] keep bytes, or null (no mask)
+  int32_t mask_stride;
   const uint16_t* q;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;

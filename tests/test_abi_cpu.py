@@ -24,7 +24,8 @@ def test_header_declares_expected_entry_points():
     names = pkv.declared_functions()
     assert set(names) == {
         "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
-        "pkv_append_kv", "pkv_decode", "pkv_decode_append", "pkv_debug_validate"}
+        "pkv_append_kv", "pkv_decode", "pkv_decode_append", "pkv_decode_masked",
+        "pkv_debug_validate"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -50,7 +51,7 @@ def test_status_strings_and_version(lib):
     for st in range(1, 7):
         assert pkv.pkv_status_str(st) not in ("ok", "unknown status")
     assert pkv.pkv_status_str(99) == "unknown status"
-    assert pkv.pkv_version() >> 16 == 2
+    assert pkv.pkv_version() >> 16 == 2 and pkv.pkv_version() & 0xffff >= 2
 
 
 def _desc(**kw):
@@ -110,6 +111,11 @@ def test_host_checks_reject_before_launch(lib):
                 ws_bytes, fake, None) == 1
     # fused append without its rows
     assert _raw(lib, "pkv_decode_append", B(pool), B(d), fake, None, fake, fake, fake, 10, fake, 4,
+                0.1, fake, ws_bytes, fake, None) == 1
+    # masked decode: no mask, or a stride that is not a multiple of 4
+    assert _raw(lib, "pkv_decode_masked", B(pool), B(d), fake, None, 16, fake, fake, 10, fake, 4,
+                0.1, fake, ws_bytes, fake, None) == 1
+    assert _raw(lib, "pkv_decode_masked", B(pool), B(d), fake, fake, 18, fake, fake, 10, fake, 4,
                 0.1, fake, ws_bytes, fake, None) == 1
     # NaN scale
     assert _raw(lib, "pkv_decode", B(pool), B(d), fake, fake, fake, 10, fake, 4, float("nan"),

@@ -126,6 +126,63 @@ def test_fused_append_decode_matches_separate(case, forced):
     compare(fus_bits, ref(5) if case == "c5" else oracle_out(batch), f"fused {case}")
 
 
+# ---------------------------------------------------------------- keep mask
+
+def _masked_run(batch, desc, mask_np, forced=0):
+    """metadata (+ append) + masked decode on the GPU; the oracle's answer."""
+    run = GpuRun(batch, desc)
+    run.metadata(forced)
+    k, v = batch.k_pool, batch.v_pool
+    ip = oracle.kv_indptr(batch.seq_lens, batch.P)
+    if batch.append:
+        run.append()
+        k, v = oracle.append_kv(k, v, batch.k_new, batch.v_new, ip, batch.kv_indices,
+                                batch.seq_lens, batch.P)
+    mask = torch.from_numpy(mask_np.astype(np.uint8)).to("cuda:0")
+    pkv.pkv_decode_masked(run.pool, desc, run.t["q"], mask, run.kv_indptr, run.t["kv_indices"],
+                          run.t["seq_lens"], batch.sm_scale, run.ws, run.out)
+    torch.cuda.synchronize()
+    expect = oracle.decode_masked(batch.q, k, v, ip, batch.kv_indices, batch.seq_lens,
+                                  batch.sm_scale, batch.P, mask_np)
+    return run.out_bits(), expect
+
+
+MASK_CASES = [  # (workload, keep density, forced workgroups)
+    ("c1", 0.5, 3), ("c2", 0.5, 0), ("c3", 0.5, 0), ("c3", 0.02, 0), ("c4", 0.9, 0),
+    ("c5", 0.7, 0), ("g8_p64", 0.3, 2), ("g1_p32", 0.6, 0),
+]
+
+
+@pytest.mark.parametrize("case,density,forced", MASK_CASES,
+                         ids=[f"{c}-keep{d}-groups{f or 'plan'}" for c, d, f in MASK_CASES])
+def test_masked_decode(case, density, forced):
+    say(f"masked decode {case} keep={density} forced={forced}")
+    if case.startswith("c"):
+        batch = cfg(int(case[1]))
+    else:
+        Hq, Hkv, D, P, lens = FUSED_CASES[case]
+        batch = W.make_batch(name=case, seed=Hq + 11 * D + P, B=len(lens), Hq=Hq, Hkv=Hkv, D=D,
+                             P=P, lengths=np.array(lens))
+    S = -(-int(batch.seq_lens.max()) // 4) * 4 + 4
+    rng = np.random.default_rng(int(density * 1000) + batch.B)
+    mask = rng.random((batch.B, S)) < density
+    mask[0, :] = False  # one request keeps nothing: zero row
+    got, expect = _masked_run(batch, make_desc(batch, min_tiles=1), mask, forced)
+    assert not W.bf16_bits_to_f32(got[0]).any()
+    compare(got, expect, f"masked {case} keep={density}")
+
+
+def test_all_true_mask_is_plain_decode():
+    # the masked kernel keeping every token does the plain kernel's arithmetic
+    batch = cfg(3)
+    say("all-true mask cfg3")
+    desc = make_desc(batch)
+    plain = GpuRun(batch, desc).step().copy()
+    S = -(-int(batch.seq_lens.max()) // 4) * 4
+    got, _ = _masked_run(batch, desc, np.ones((batch.B, S), bool))
+    assert np.array_equal(got, plain)
+
+
 # -------------------------------------------------------------------- decode
 
 DECODE_CASES = [  # (workload, grid size (0 = one per CU), forced workgroups (0 = planner))
