@@ -64,6 +64,7 @@ __all__ = [
     "softmax_attend",
     "decode",
     "decode_masked",
+    "prefill",
     "chunk_partial",
     "merge_partials",
     "even_page_ranges",
@@ -166,6 +167,40 @@ def decode_masked(q_bits, k_pool, v_pool, indptr, indices, seq_lens, sm_scale: f
         for hq in range(Hq):
             h = kv_head_of(hq, G)
             out[b, hq] = softmax_attend(q[b, hq], Kd[:, h, :], Vd[:, h, :], sm_scale)
+    return out
+
+
+def prefill(q_rows, k_pool, v_pool, kv_indptr, kv_indices, seq_lens, qo_indptr, sm_scale: float,
+            P: int, causal: bool) -> np.ndarray:
+    """Paged prefill / extend attention -> float64 [total_q, Hq, D].
+
+    Request b has qo_indptr[b+1] - qo_indptr[b] = n query rows and attends to
+    its L = seq_lens[b] cached tokens (the new tokens included), read through
+    the page table as in decode.  The pages' paged prefill wrapper takes
+    flattened query rows with per-request offsets, per-request KV lengths and
+    a causal flag with offset 0 (AstrAI compare v1.3.12..6f09b1d,
+    attention_ops.py, attn_paged_prefill).  Reading of offset 0: the causal
+    mask is aligned to the end of the KV, so query row i (0-based) is the
+    token at position L - n + i and sees keys 0 .. L - n + i; with n = 1 this
+    is decode.  Without the causal flag every row sees all L keys.  A row that
+    sees no key gets zeros.
+    """
+    q = bf16_to_f64(q_rows)
+    total, Hq, D = q.shape
+    Hkv = np.asarray(k_pool).shape[1]
+    G = Hq // Hkv
+    out = np.zeros((total, Hq, D), dtype=np.float64)
+    for b in range(len(qo_indptr) - 1):
+        q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        n, L = q1 - q0, max(int(seq_lens[b]), 0)
+        Kd = gather_request(k_pool, kv_indptr, kv_indices, b, L, P)
+        Vd = gather_request(v_pool, kv_indptr, kv_indices, b, L, P)
+        for i in range(n):
+            vis = min(L, max(0, L - n + i + 1)) if causal else L
+            for hq in range(Hq):
+                h = kv_head_of(hq, G)
+                out[q0 + i, hq] = softmax_attend(q[q0 + i, hq], Kd[:vis, h, :], Vd[:vis, h, :],
+                                                 sm_scale)
     return out
 
 

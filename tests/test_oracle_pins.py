@@ -20,7 +20,12 @@ mathematics of softmax attention and from invariants the method must keep:
 10. the keep mask: brute force over the kept tokens only, an all-true mask is the
     unmasked decode bit for bit, an all-false row is zero, masking a request's
     newest token equals decoding one token shorter, and mask entries past
-    seq_len change nothing.
+    seq_len change nothing;
+11. prefill: brute force over each row's visible keys, one-row requests are the
+    decode bit for bit, causal row i is the decode of the first L - n + i + 1
+    tokens, the non-causal rows all see L tokens, and with an identity page
+    table and no prefix the causal result is torch's scaled_dot_product_attention
+    (is_causal) in float64.
 
 ``test_planted_mistakes`` plants plausible mistakes in the oracle (on the CPU)
 and checks that at least one pin fails for each.
@@ -412,9 +417,94 @@ def pin_mask(mod):
     assert np.array_equal(run_masked(mod, g8, newest), short)
 
 
+# ----------------------------------------------------------- prefill (pin 11)
+
+def prefill_batch(seed=31, q_lens=(3, 1, 6, 2), prefix_lens=(5, 0, 3, 9), **kw):
+    args = dict(name="pf", seed=seed, Hq=4, Hkv=2, D=8, P=4, q_lens=q_lens,
+                prefix_lens=prefix_lens)
+    args.update(kw)
+    return W.make_prefill(**args)
+
+
+def run_prefill(mod, batch, causal, seq_lens=None):
+    sl = batch.seq_lens if seq_lens is None else seq_lens
+    ip = mod.kv_indptr(batch.seq_lens, batch.P)
+    return mod.prefill(batch.q_rows, batch.k_pool, batch.v_pool, ip, batch.kv_indices, sl,
+                       batch.qo_indptr, batch.sm_scale, batch.P, causal)
+
+
+def brute_force_prefill(batch, causal):
+    total, Hq, D = batch.q_rows.shape
+    Hkv = batch.Hkv
+    out = np.zeros((total, Hq, D))
+    for b in range(batch.B):
+        q0, q1 = int(batch.qo_indptr[b]), int(batch.qo_indptr[b + 1])
+        n, L = q1 - q0, int(batch.seq_lens[b])
+        slots = _token_slots(batch, b)
+        for i in range(n):
+            vis = slots[: L - n + i + 1] if causal else slots
+            if not vis:
+                continue
+            for hq in range(Hq):
+                h = (hq * Hkv) // Hq
+                qv = [_bf16_py(batch.q_rows[q0 + i, hq, d]) for d in range(D)]
+                xs = [batch.sm_scale * math.fsum(a * _bf16_py(batch.k_pool[p, h, o, d])
+                                                 for d, a in enumerate(qv)) for p, o in vis]
+                m = max(xs)
+                ws = [math.exp(x - m) for x in xs]
+                den = math.fsum(ws)
+                for d in range(D):
+                    out[q0 + i, hq, d] = math.fsum(w * _bf16_py(batch.v_pool[p, h, o, d])
+                                                   for w, (p, o) in zip(ws, vis)) / den
+    return out
+
+
+def pin_prefill(mod):
+    batch = prefill_batch()
+    for causal in (True, False):
+        got = run_prefill(mod, batch, causal)
+        assert np.max(np.abs(got - brute_force_prefill(batch, causal))) < 1e-12
+    causal = run_prefill(mod, batch, True)
+    full = run_prefill(mod, batch, False)
+    ip = mod.kv_indptr(batch.seq_lens, batch.P)
+    for b in range(batch.B):
+        q0, q1 = int(batch.qo_indptr[b]), int(batch.qo_indptr[b + 1])
+        n, L = q1 - q0, int(batch.seq_lens[b])
+        for i in range(n):
+            # the row as a decode query: all L keys, or the first L - n + i + 1
+            qd = np.repeat(batch.q_rows[q0 + i][None], batch.B, axis=0)
+            for lim, ref in ((L, full), (L - n + i + 1, causal)):
+                sl = batch.seq_lens.copy()
+                sl[b] = lim
+                dec = mod.decode(qd, batch.k_pool, batch.v_pool, ip, batch.kv_indices, sl,
+                                 batch.sm_scale, batch.P)
+                assert np.array_equal(dec[b], ref[q0 + i])
+    # one-row requests: the decode of those rows, bit for bit
+    one = prefill_batch(seed=32, q_lens=(1, 1, 1), prefix_lens=(6, 0, 11))
+    ip1 = mod.kv_indptr(one.seq_lens, one.P)
+    dec = mod.decode(one.q_rows, one.k_pool, one.v_pool, ip1, one.kv_indices, one.seq_lens,
+                     one.sm_scale, one.P)
+    assert np.array_equal(run_prefill(mod, one, True), dec)
+    # identity page table, no prefix, causal: torch SDPA (square, so both
+    # alignments of the causal mask agree) in float64
+    sq = W.identity_layout(prefill_batch(seed=33, q_lens=(7,), prefix_lens=(0,), poison=False))
+    got = run_prefill(mod, sq, True)
+    L = int(sq.seq_lens[0])
+    # token-major [pages, P, Hkv, D] -> [tokens, Hkv, D]
+    k = torch.from_numpy(np.swapaxes(mod.bf16_to_f64(sq.k_pool), 1, 2).reshape(-1, sq.Hkv, sq.D)[:L])
+    v = torch.from_numpy(np.swapaxes(mod.bf16_to_f64(sq.v_pool), 1, 2).reshape(-1, sq.Hkv, sq.D)[:L])
+    G = sq.Hq // sq.Hkv
+    qt = torch.from_numpy(mod.bf16_to_f64(sq.q_rows)).permute(1, 0, 2)  # [Hq, L, D]
+    kt = k.permute(1, 0, 2).repeat_interleave(G, dim=0)
+    vt = v.permute(1, 0, 2).repeat_interleave(G, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                           scale=sq.sm_scale)
+    assert np.max(np.abs(got - ref.permute(1, 0, 2).numpy())) < 1e-12
+
+
 PINS = [pin_brute_force, pin_seq_len_one, pin_permutation, pin_split_invariance, pin_q_zero,
         pin_constant_v, pin_dominant_key, pin_sdpa, pin_kv_indptr, pin_plan, pin_stream_pieces,
-        pin_append, pin_poison, pin_mask]
+        pin_append, pin_poison, pin_mask, pin_prefill]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -524,6 +614,37 @@ def _mutants():
         return OA.__dict__["_orig_decode_masked"](q, k, v, ip, idx, sl, sc, P,
                                                   np.roll(np.asarray(mask, bool), 1, axis=1))
     m["mask_shifted_one_token"] = {"decode_masked": masked_shifted}
+
+    def prefill_causal_top_left(q, k, v, ip, idx, sl, qo, sc, P, causal):
+        # a plausible slip: the causal mask aligned to the start of the keys
+        out = OA.__dict__["_orig_prefill"](q, k, v, ip, idx, sl, qo, sc, P, False)
+        if not causal:
+            return out
+        for b in range(len(qo) - 1):
+            n = int(qo[b + 1]) - int(qo[b])
+            sl_b = np.zeros_like(np.asarray(sl))
+            for i in range(n):
+                sl_b[:] = 0
+                sl_b[b] = min(i + 1, int(sl[b]))
+                qi = np.repeat(np.asarray(q)[int(qo[b]) + i][None], len(sl), axis=0)
+                out[int(qo[b]) + i] = OA.decode(qi, k, v, ip, idx, sl_b, sc, P)[b]
+        return out
+    m["prefill_causal_top_left"] = {"prefill": prefill_causal_top_left}
+
+    def prefill_causal_one_short(q, k, v, ip, idx, sl, qo, sc, P, causal):
+        out = OA.__dict__["_orig_prefill"](q, k, v, ip, idx, sl, qo, sc, P, causal)
+        if causal:
+            # each row loses its own key
+            for b in range(len(qo) - 1):
+                n = int(qo[b + 1]) - int(qo[b])
+                L = int(sl[b])
+                for i in range(n):
+                    sl_b = np.zeros_like(np.asarray(sl))
+                    sl_b[b] = max(0, L - n + i)
+                    qi = np.repeat(np.asarray(q)[int(qo[b]) + i][None], len(sl), axis=0)
+                    out[int(qo[b]) + i] = OA.decode(qi, k, v, ip, idx, sl_b, sc, P)[b]
+        return out
+    m["prefill_causal_one_short"] = {"prefill": prefill_causal_one_short}
     return m
 
 
@@ -533,7 +654,7 @@ MUTANTS = _mutants()
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistakes(name, monkeypatch):
     for fn in ("softmax_attend", "chunk_partial", "plan_stream", "decode_pieces", "append_kv",
-               "decode_masked"):
+               "decode_masked", "prefill"):
         monkeypatch.setitem(OA.__dict__, "_orig_" + fn, getattr(OA, fn))
     for attr, repl in MUTANTS[name].items():
         monkeypatch.setattr(OA, attr, repl)

@@ -39,6 +39,7 @@ __all__ = [
     "bf16_bits_to_f32",
     "normal_bf16",
     "make_batch",
+    "make_prefill",
     "config",
     "CONFIG_NAMES",
     "permute_pool",
@@ -109,6 +110,9 @@ class DecodeBatch:
     poisoned: bool = False
     shared_pages: int = 0  # pages referenced by more than one request
     notes: dict = field(default_factory=dict)
+    # Prefill batches: query rows of every request, flattened, and their offsets.
+    q_rows: Optional[np.ndarray] = None  # uint16 [total_q, Hq, D]
+    qo_indptr: Optional[np.ndarray] = None  # int32 [B + 1]
 
     @property
     def kv_indices(self) -> np.ndarray:
@@ -216,6 +220,25 @@ def make_batch(
     )
     if poison:
         _poison(batch)
+    return batch
+
+
+def make_prefill(*, name: str, seed: int, Hq: int, Hkv: int, D: int, P: int, q_lens,
+                 prefix_lens, poison: bool = True, q_scale: float = 1.0) -> DecodeBatch:
+    """Prefill / extend batch: request b has prefix_lens[b] cached tokens and
+    q_lens[b] new ones, whose K/V are already in the pool (seq_len = prefix +
+    q_len); its q_lens[b] query rows are stored flattened in ``q_rows`` with
+    offsets ``qo_indptr``.  Draw order: pool layout and contents as in
+    make_batch, then the query rows."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    ql = np.asarray(q_lens, dtype=np.int64)
+    pl = np.asarray(prefix_lens, dtype=np.int64)
+    batch = make_batch(name=name, seed=seed, B=ql.size, Hq=Hq, Hkv=Hkv, D=D, P=P,
+                       lengths=pl + ql, poison=poison, rng=rng)
+    offsets = np.zeros(ql.size + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(ql)
+    batch.qo_indptr = offsets
+    batch.q_rows = normal_bf16(rng, (int(offsets[-1]), Hq, D), q_scale)
     return batch
 
 
@@ -398,4 +421,7 @@ def to_device(batch: DecodeBatch, device="cuda:0") -> dict:
     if batch.append:
         d["k_new"] = bits(batch.k_new)
         d["v_new"] = bits(batch.v_new)
+    if batch.q_rows is not None:
+        d["q_rows"] = bits(batch.q_rows)
+        d["qo_indptr"] = torch.from_numpy(batch.qo_indptr.astype(np.int32)).to(device)
     return d
