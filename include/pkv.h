@@ -236,6 +236,31 @@ int pkv_decode_masked(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                       int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
                       void* out, void* stream);
 
+/* Paged prefill / extend attention of one layer (one launch, no workspace).
+ * Request b has n_b = qo_indptr[b+1] - qo_indptr[b] query rows (its newest
+ * tokens) and attends to its L_b = seq_lens[b] cached tokens, the new ones
+ * included, through the same page table as the decode.  With causal != 0,
+ * query row i (0-based) sees keys 0 .. L_b - n_b + i (the mask aligned to the
+ * end of the KV: the pages' causal offset 0, attention_ops.py,
+ * attn_paged_prefill, on the compare page); otherwise every row sees all L_b
+ * keys.  A row that sees no key gets zeros.
+ *  q            device bf16 [total_q][num_q_heads][head_dim], rows of request b
+ *               at qo_indptr[b] ..
+ *  qo_indptr    device int32 [batch + 1], non-decreasing, qo_indptr[0] = 0
+ *  kv_indptr    device int32 [batch + 1] from pkv_build_metadata(seq_lens)
+ *  kv_indices   device int32 [num_indices] (may be NULL when num_indices is 0)
+ *  seq_lens     device int32 [batch] KV lengths
+ *  max_q_len    host int: an upper bound of every n_b; it sizes the grid
+ *               (rows beyond it are not computed)
+ *  out          device bf16 [total_q][num_q_heads][head_dim]
+ * The descriptor gives the shapes (num_workgroups and min_tiles_per_group are
+ * not used).  Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED,
+ * PKV_ERR_CAPACITY (batch above max_batch or 65535), PKV_ERR_LAUNCH. */
+int pkv_prefill(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                int32_t num_indices, const int32_t* seq_lens, int32_t batch, int32_t max_q_len,
+                int32_t causal, float sm_scale, void* out, void* stream);
+
 /* Debug only (synchronises the stream; not capturable).  Checks device
  * metadata and copies the plan to host memory.
  *  groups_out   host int32 or NULL: workgroups the plan uses (W above)

@@ -36,6 +36,7 @@ __all__ = [
     "pkv_decode",
     "pkv_decode_append",
     "pkv_decode_masked",
+    "pkv_prefill",
     "pkv_debug_validate",
     "WAVES_PER_GROUP",
     "PKV_OK",
@@ -113,6 +114,8 @@ _SIGNATURES = {
     "pkv_decode_masked": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp,
                                          _i32, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
                                          ctypes.c_size_t, _vp, _vp]),
+    "pkv_prefill": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp, _vp,
+                                   _vp, _i32, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp]),
     "pkv_debug_validate": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _vp, _vp, _i32, _i32, _i32,
                                           _vp, ctypes.c_size_t, _i32p, _i32p, _vp]),
 }
@@ -304,6 +307,22 @@ def pkv_decode_masked(pool: Pool, desc: Desc, q: torch.Tensor, mask: torch.Tenso
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(out, "out", _BF16, n), _stream(stream))
     _check("pkv_decode_masked", st)
+
+
+def pkv_prefill(pool: Pool, desc: Desc, q: torch.Tensor, qo_indptr: torch.Tensor,
+                kv_indptr: torch.Tensor, kv_indices: torch.Tensor, seq_lens: torch.Tensor,
+                max_q_len: int, causal: bool, sm_scale: float, out: torch.Tensor,
+                stream=None) -> None:
+    """Paged prefill / extend: q and out are [total_q, Hq, D]."""
+    B = seq_lens.numel()
+    n = q.numel()
+    st = load_library().pkv_prefill(
+        ctypes.byref(pool.c()), ctypes.byref(desc.c()), _ptr(q, "q", _BF16),
+        _ptr(qo_indptr, "qo_indptr", _I32, B + 1), _ptr(kv_indptr, "kv_indptr", _I32, B + 1),
+        _ptr(kv_indices, "kv_indices", _I32), kv_indices.numel(),
+        _ptr(seq_lens, "seq_lens", _I32), B, int(max_q_len), int(bool(causal)), float(sm_scale),
+        _ptr(out, "out", _BF16, n), _stream(stream))
+    _check("pkv_prefill", st)
 
 
 def pkv_debug_validate(desc: Desc, seq_lens: torch.Tensor, kv_indptr: torch.Tensor,

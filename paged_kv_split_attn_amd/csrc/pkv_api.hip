@@ -109,7 +109,7 @@ const char* pkv_status_str(int status) {
   }
 }
 
-int32_t pkv_version(void) { return (2 << 16) | 2; }
+int32_t pkv_version(void) { return (2 << 16) | 3; }
 
 size_t pkv_workspace_bytes(const pkv_desc* desc) {
   WsLayout L;
@@ -262,6 +262,43 @@ int pkv_decode_append(const pkv_pool* pool, const pkv_desc* desc, const void* q,
   if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
   return decode_impl(pool, desc, q, k_new, v_new, nullptr, 0, kv_indptr, kv_indices, num_indices,
                      seq_lens, batch, sm_scale, workspace, workspace_bytes, out, stream);
+}
+
+int pkv_prefill(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                int32_t num_indices, const int32_t* seq_lens, int32_t batch, int32_t max_q_len,
+                int32_t causal, float sm_scale, void* out, void* stream) {
+  WsLayout L;
+  int st = check_desc(desc, &L);
+  if (st != PKV_OK) return st;
+  st = check_pool(pool, desc);
+  if (st != PKV_OK) return st;
+  if (!q || !qo_indptr || !kv_indptr || (num_indices > 0 && !kv_indices) || !seq_lens || !out ||
+      batch < 0 || num_indices < 0 || max_q_len < 0 || !(sm_scale == sm_scale))
+    return PKV_ERR_INVALID_ARG;
+  if (batch > desc->max_batch || batch > 65535) return PKV_ERR_CAPACITY;
+  if (batch == 0 || max_q_len == 0) return PKV_OK;
+  PrefillArgs a;
+  a.k = static_cast<const uint16_t*>(pool->k);
+  a.v = static_cast<const uint16_t*>(pool->v);
+  a.q = static_cast<const uint16_t*>(q);
+  a.qo_indptr = qo_indptr;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.num_indices = num_indices;
+  a.num_pages = pool->num_pages;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.page_size = desc->page_size;
+  a.batch = batch;
+  a.causal = causal != 0;
+  a.log2_steps = log2i(desc->page_size / 16);
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  const int hg = heads_per_group(desc->num_q_heads / desc->num_kv_heads);
+  return launch_status(launch_prefill(a, desc->head_dim, hg, max_q_len,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int32_t* kv_indptr,

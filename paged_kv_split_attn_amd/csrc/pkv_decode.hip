@@ -40,38 +40,17 @@
 // (sm_scale * log2 e folded into one multiply-add) so every exponential is a
 // single v_exp_f32.
 
-#include <math.h>
-
-#include "pkv_internal.h"
+#include "pkv_mfma.h"
 
 namespace pkv {
 namespace {
 
-constexpr float kRescaleSlack = 8.0f;  // log2 of the largest un-rescaled weight
-constexpr float kMinusInf = -INFINITY;
-constexpr float kFloorMax = -1.0e30f;  // initial running max (finite: exp2 never sees inf - inf)
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
-}
 
 // Wait until every earlier store of the wave has been acknowledged (for the
 // device-coherent partial stores of the epilogue: is visible to every XCD).
 // s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Re-reads a kernel argument from the argument segment where it is used, so
-// that pointers needed only after the streaming loop do not hold scalar
-// registers through it.
 // A pointer that every lane holds the same value of, moved to scalar
 // registers (readfirstlane works on 32 bits: both halves are read).
 template <class T>
@@ -91,114 +70,11 @@ struct EpiloguePtrs {
   float* opart;
 };
 
-// MFMA operand vectors.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-
-// One step's operands: 16 tokens of one (page, head) tile.
-template <int D>
-struct Step {
-  uint4 k[D / 32];  // K of token r, channels 8*(4kk + g) .. +8 (A of q.K, block kk)
-  uint2 v[D / 16];  // V^T: channel 16*nb + r, tokens 4g .. 4g+3 (B of p.V)
-  uint32_t keep;    // masked decode: keep bytes of tokens 4g .. 4g+3
-};
 
 // Kernel variants: plain decode, KV append fused into the decode, decode with
 // a per-token keep mask.
 enum Kind : int { kPlain = 0, kAppend = 1, kMasked = 2 };
 
-template <int D, int HG>
-struct MfmaWave {
-  static constexpr int KB = D / 32;  // q.K MFMAs per step
-  static constexpr int VB = D / 16;  // p.V channel blocks
-  floatx4_t o[VB];                   // O[head 4g+i][channel 16*nb + r]
-  bf16x8_t qb[KB];                   // q^T operand (zero for heads >= HG)
-  float m, l;                        // head r: running max (log2 domain), partial sum
-
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int nb = 0; nb < VB; ++nb) o[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    m = kFloorMax;
-    l = 0.f;
-  }
-
-  // Consume one step.  `live` = tokens of the step that count (uniform, 0..16);
-  // `g` = lane / 16; `bias` = 0 for heads < HG, -inf otherwise.
-  template <class S>
-  __device__ __forceinline__ void step(const S& st, int live, int g, float scale_log2,
-                                       float bias, uint32_t keep = 0x01010101u) {
-    floatx4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, st.k[kk]),
-                                                   qb[kk], sc, 0, 0, 0);
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = fmaf(sc[i], scale_log2, bias);
-    uint2 vv[VB];
-#pragma unroll
-    for (int nb = 0; nb < VB; ++nb) vv[nb] = st.v[nb];
-    if (live < 16) {
-      // Tokens past the sequence end (or in a skipped page) may hold anything,
-      // NaN included: drop their scores and zero their V so that a zero weight
-      // contributes exactly zero.
-      const int t = 4 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (t + i >= live) s[i] = kMinusInf;
-      const uint32_t m0 = (t + 0 < live ? 0x0000ffffu : 0u) | (t + 1 < live ? 0xffff0000u : 0u);
-      const uint32_t m1 = (t + 2 < live ? 0x0000ffffu : 0u) | (t + 3 < live ? 0xffff0000u : 0u);
-#pragma unroll
-      for (int nb = 0; nb < VB; ++nb) {
-        vv[nb].x &= m0;
-        vv[nb].y &= m1;
-      }
-    }
-    // Keep mask: byte i of `keep` is zero for a dropped token 4g + i (its V is
-    // real data, so a zero weight suffices).
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (((keep >> (8 * i)) & 0xffu) == 0) s[i] = kMinusInf;
-    // Step max of head r over its 16 tokens (4 per lane, 4 lanes).
-    float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    pm = fmaxf(pm, __shfl_xor(pm, 16, kWave));
-    pm = fmaxf(pm, __shfl_xor(pm, 32, kWave));
-    if (__builtin_amdgcn_ballot_w64(pm > m + kRescaleSlack) != 0) {
-      const float mn = fmaxf(m, pm);
-      const float alpha = fast_exp2(m - mn);
-      l *= alpha;
-      m = mn;
-      // Lane (0, i) holds head i's factor; O rows of head i sit in register i.
-#pragma unroll
-      for (int i = 0; i < HG; ++i) {
-        const float ai = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
-#pragma unroll
-        for (int nb = 0; nb < VB; ++nb) o[nb][i] *= ai;
-      }
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - m);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    // p = hi + lo, both bf16: the product keeps ~16 mantissa bits of p.
-    short4_t phi, plo;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 h = (__bf16)p[i];
-      const float hf = (float)h;
-      const __bf16 lo = (__bf16)(p[i] - hf);
-      phi[i] = __builtin_bit_cast(short, h);
-      plo[i] = __builtin_bit_cast(short, lo);
-    }
-#pragma unroll
-    for (int nb = 0; nb < VB; ++nb) {
-      const short4_t vb = __builtin_bit_cast(short4_t, vv[nb]);
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, o[nb], 0, 0, 0);
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, o[nb], 0, 0, 0);
-    }
-  }
-};
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned u4v __attribute__((ext_vector_type(4)));

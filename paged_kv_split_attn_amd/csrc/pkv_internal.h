@@ -118,9 +118,26 @@ struct DecodeArgs {
   float scale_log2;     // sm_scale * log2(e)
 };
 
+struct PrefillArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* q;          // [total_q][Hq][D] bf16
+  const int32_t* qo_indptr;   // [batch + 1] query-row offsets
+  const int32_t* kv_indptr;   // [batch + 1] page prefix sums
+  const int32_t* kv_indices;
+  const int32_t* seq_lens;    // KV tokens per request (new tokens included)
+  uint16_t* out;              // [total_q][Hq][D] bf16
+  int32_t num_indices, num_pages, num_q_heads, num_kv_heads, page_size, batch;
+  int32_t causal;
+  int32_t log2_steps;
+  float scale_log2;
+};
+
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, int groups,
                          hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int heads_per_group, int max_q_len,
+                          hipStream_t s);
 
 }  // namespace pkv

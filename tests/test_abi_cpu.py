@@ -25,7 +25,7 @@ def test_header_declares_expected_entry_points():
     assert set(names) == {
         "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
         "pkv_append_kv", "pkv_decode", "pkv_decode_append", "pkv_decode_masked",
-        "pkv_debug_validate"}
+        "pkv_prefill", "pkv_debug_validate"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -117,6 +117,13 @@ def test_host_checks_reject_before_launch(lib):
                 0.1, fake, ws_bytes, fake, None) == 1
     assert _raw(lib, "pkv_decode_masked", B(pool), B(d), fake, fake, 18, fake, fake, 10, fake, 4,
                 0.1, fake, ws_bytes, fake, None) == 1
+    # prefill: null query offsets, negative max_q_len, batch above capacity
+    assert _raw(lib, "pkv_prefill", B(pool), B(d), fake, None, fake, fake, 10, fake, 4, 8, 1, 0.1,
+                fake, None) == 1
+    assert _raw(lib, "pkv_prefill", B(pool), B(d), fake, fake, fake, fake, 10, fake, 4, -1, 1, 0.1,
+                fake, None) == 1
+    assert _raw(lib, "pkv_prefill", B(pool), B(d), fake, fake, fake, fake, 10, fake, 17, 8, 1, 0.1,
+                fake, None) == 4
     # NaN scale
     assert _raw(lib, "pkv_decode", B(pool), B(d), fake, fake, fake, 10, fake, 4, float("nan"),
                 fake, ws_bytes, fake, None) == 1

@@ -1,0 +1,73 @@
+"""Parity of the HIP paged prefill / extend kernel with the fp64 oracle.
+
+Query rows of ragged lengths attend to each request's paged KV (prefix plus the
+new tokens), with and without the causal mask, for G = 1, 2, 3, 4, 8, head dims
+64 and 128 and pages of 16, 32 and 64 tokens.  The metadata comes from
+pkv_build_metadata, as in a serving step.  Outputs start as NaN, so a row the
+kernel skips shows up.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_split_attn_amd as pkv
+import workloads as W
+from gpu_util import compare, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny_g4": dict(Hq=8, Hkv=2, D=64, P=16, q_lens=[3, 1, 17, 40], prefix_lens=[5, 0, 30, 100]),
+    "g1_d128": dict(Hq=4, Hkv=4, D=128, P=16, q_lens=[16, 33, 7], prefix_lens=[0, 64, 200]),
+    "g2_p32": dict(Hq=8, Hkv=4, D=128, P=32, q_lens=[9, 40], prefix_lens=[31, 0]),
+    "g3": dict(Hq=24, Hkv=8, D=64, P=16, q_lens=[11, 6], prefix_lens=[4, 20]),
+    "g8_p64": dict(Hq=32, Hkv=4, D=128, P=64, q_lens=[50, 3], prefix_lens=[77, 128]),
+    "square_512": dict(Hq=32, Hkv=8, D=128, P=16, q_lens=[512, 300], prefix_lens=[0, 0]),
+}
+
+
+def run_prefill(batch, causal, max_q_len=None):
+    dev = "cuda:0"
+    t = W.to_device(batch, dev)
+    desc = pkv.Desc(max_batch=batch.B, num_q_heads=batch.Hq, num_kv_heads=batch.Hkv,
+                    head_dim=batch.D, page_size=batch.P)
+    ws = torch.empty(pkv.pkv_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    kv_indptr = torch.empty(batch.B + 1, dtype=torch.int32, device=dev)
+    pkv.pkv_build_metadata(desc, t["seq_lens"], 0, kv_indptr, ws)
+    out = torch.full(tuple(batch.q_rows.shape), 0x7FC0, dtype=torch.int16, device=dev)
+    q_lens = np.diff(batch.qo_indptr)
+    pkv.pkv_prefill(pkv.Pool(t["k_pool"], t["v_pool"]), desc, t["q_rows"], t["qo_indptr"],
+                    kv_indptr, t["kv_indices"], t["seq_lens"],
+                    int(q_lens.max()) if max_q_len is None else max_q_len, causal,
+                    batch.sm_scale, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+def oracle_prefill(batch, causal):
+    ip = oracle.kv_indptr(batch.seq_lens, batch.P)
+    return oracle.prefill(batch.q_rows, batch.k_pool, batch.v_pool, ip, batch.kv_indices,
+                          batch.seq_lens, batch.qo_indptr, batch.sm_scale, batch.P, causal)
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("case", list(CASES))
+def test_prefill_parity(case, causal):
+    say(f"prefill {case} causal={causal}")
+    batch = W.make_prefill(name=case, seed=sum(map(ord, case)), **CASES[case])
+    got = run_prefill(batch, causal)
+    compare(got, oracle_prefill(batch, causal), f"prefill {case} causal={causal}")
+
+
+def test_prefill_single_rows_match_decode_semantics():
+    # one new token per request: the causal prefill is the decode of that token
+    say("prefill one row per request")
+    batch = W.make_prefill(name="one", seed=5, Hq=32, Hkv=8, D=128, P=16, q_lens=[1, 1, 1, 1],
+                           prefix_lens=[0, 15, 16, 4000])
+    got = run_prefill(batch, True)
+    ip = oracle.kv_indptr(batch.seq_lens, batch.P)
+    dec = oracle.decode(batch.q_rows, batch.k_pool, batch.v_pool, ip, batch.kv_indices,
+                        batch.seq_lens, batch.sm_scale, batch.P)
+    compare(got, dec, "prefill q_len 1 vs decode oracle")
