@@ -55,6 +55,9 @@ def parse():
                     help="replay each step from a captured hipGraph (one graph per pool copy)")
     ap.add_argument("--mask-keep", type=float, default=None, metavar="P",
                     help="also time pkv_decode_masked with a random keep mask of density P")
+    ap.add_argument("--prefill", action="store_true",
+                    help="also time pkv_prefill on a causal prefill batch (4 x 1024 new tokens, "
+                         "no prefix, Hq=32, Hkv=8, D=128, P=16)")
     ap.add_argument("--no-kernel-loop", action="store_true",
                     help="time only whole steps (skip the decode-only loop)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -123,6 +126,38 @@ def calibrate_copy(mib, reps=5):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": reps}), flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def bench_prefill(pkv, W, torch, dev, stream, K):
+    """Causal prefill of 4 x 1024 new tokens (no prefix); rotating pool copies."""
+    pb = W.make_prefill(name="prefill_b4_q1024", seed=7, Hq=32, Hkv=8, D=128, P=16,
+                        q_lens=[1024] * 4, prefix_lens=[0] * 4, poison=False)
+    t = W.to_device(pb, dev)
+    desc = pkv.Desc(max_batch=pb.B, num_q_heads=pb.Hq, num_kv_heads=pb.Hkv, head_dim=pb.D,
+                    page_size=pb.P)
+    ws = torch.zeros(pkv.pkv_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    ip = torch.zeros(pb.B + 1, dtype=torch.int32, device=dev)
+    pkv.pkv_build_metadata(desc, t["seq_lens"], 0, ip, ws, stream)
+    out = torch.empty(tuple(pb.q_rows.shape), dtype=torch.int16, device=dev)
+    pools = [pkv.Pool(t["k_pool"], t["v_pool"])]
+    pools += [pkv.Pool(t["k_pool"].clone(), t["v_pool"].clone()) for _ in range(3)]
+
+    def call(i):
+        pkv.pkv_prefill(pools[i % len(pools)], desc, t["q_rows"], t["qo_indptr"], ip,
+                        t["kv_indices"], t["seq_lens"], 1024, True, pb.sm_scale, out, stream)
+    for i in range(3):
+        call(i)
+    ms = timed(stream, K, call)
+    # causal: row i of a request sees i + 1 keys; 4 * D flop per key per query head
+    keys = sum(int(n) * (int(n) + 1) // 2 for n in np.diff(pb.qo_indptr))
+    flop = keys * pb.Hq * 4 * pb.D
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"workload": pb.name, "us_per_call": round(ms * 1e3, 2), "flop": int(flop),
+            "TFLOPs": round(tf, 1), "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def timed(stream, K, fn):
@@ -272,6 +307,8 @@ def main():
                          "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
         })
+    if args.prefill:
+        res["prefill"] = bench_prefill(pkv, W, torch, dev, stream, K)
     if args.mask_keep is not None:
         S = -(-int(batch.seq_lens.max()) // 4) * 4
         rng = np.random.default_rng(np.random.PCG64(2000 + args.config))
