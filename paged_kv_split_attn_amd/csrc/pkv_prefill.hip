@@ -1,5 +1,7 @@
 // Paged prefill / extend attention for gfx950: ragged query rows per request
 // attend to the request's paged KV (prefix + new tokens), causal or not.
+// The eight waves of a workgroup share one KV head: each 64-token chunk of its
+// K and V is fetched once into LDS (double buffered) and read by all of them.
 //
 // The pages' paged prefill takes query rows flattened over the batch with
 // per-request offsets, per-request KV lengths and a causal flag with offset 0
@@ -21,23 +23,43 @@ template <int D, int HG>
 __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   constexpr int QT = 16 / HG;     // query tokens per wave block
   constexpr int ROWS = QT * HG;   // score rows in use (15 for HG = 3)
-  constexpr int kStages = 2;      // register ring: steps in flight per wave
-  __shared__ __align__(16) float s_out[kWavesPerGroup][16][D];  // per-wave transpose of rows
+  constexpr int kCh = 4;          // 16-token steps per LDS chunk
+  constexpr int kPieces = D * 16 * 2 / 16;  // 16-byte pieces of one step's K (same for V)
+  static_assert(2 * kPieces * kCh % kGroupThreads == 0 && kPieces % kWave == 0,
+                "whole, wave-uniform loads per thread");
+  constexpr int kLoads = 2 * kPieces * kCh / kGroupThreads;  // per thread and chunk
+  // Two chunks (double buffer) of K as [step][D/8][16][8] and V as
+  // [step][D][16] (the layouts of a 16-token tile); after the last chunk the
+  // same bytes hold the per-wave output rows [wave][16][D] in fp32.
+  constexpr int kKBytes = kCh * D * 16 * 2;
+  constexpr int kBufBytes = 2 * kKBytes;  // K + V of one chunk
+  constexpr int kOutBytes = kWavesPerGroup * 16 * D * 4;
+  __shared__ __align__(16) char smem[2 * kBufBytes > kOutBytes ? 2 * kBufBytes : kOutBytes];
+  auto k_at = [&](int buf, int st, int cb, int t) {  // 16 bytes: K channels 8cb.. of token t
+    return smem + buf * kBufBytes + ((st * (D / 8) + cb) * 16 + t) * 16;
+  };
+  auto v_at = [&](int buf, int st, int ch, int t) {  // V channel ch from token t on
+    return smem + buf * kBufBytes + kKBytes + ((st * D + ch) * 16 + t) * 2;
+  };
+  float* s_out = reinterpret_cast<float*>(smem);
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int b = blockIdx.z;
   const int u = blockIdx.y;
-  const int tok0 = (blockIdx.x * kWavesPerGroup + w) * QT;  // first query token of the block
+  const int wg_tok0 = blockIdx.x * kWavesPerGroup * QT;  // first query token of the workgroup
+  const int tok0 = wg_tok0 + w * QT;                      // first query token of this wave
   const int q0 = a.qo_indptr[b];
   const int n = a.qo_indptr[b + 1] - q0;
-  if (tok0 >= n) return;  // uniform per wave; the kernel has no workgroup barrier
+  if (wg_tok0 >= n) return;  // uniform over the workgroup
   const int L = max(a.seq_lens[b], 0);
   const int ip0 = a.kv_indptr[b];
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
   const int hq0 = u * HG;
   const int g = hq0 / G;  // KV head of the head group
+  const bool active = tok0 < n;  // this wave has query rows
 
   const int g4 = lane >> 4;
   const int r16 = lane & 15;
@@ -46,8 +68,13 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   const bool rvalid = r16 < ROWS && rt < n;
   const int lim = a.causal ? L - n + rt : L - 1;  // last key row r16 sees
   const float bias = rvalid ? 0.f : kMinusInf;
-  const int last_tok = min(tok0 + QT, n) - 1;
-  const int kv_end = a.causal ? max(0, min(L, L - n + last_tok + 1)) : L;  // keys the block reads
+  // Keys this wave reads, and keys the workgroup reads (its last wave's limit).
+  auto block_end = [&](int t0) {
+    const int last = min(t0 + QT, n) - 1;
+    return a.causal ? max(0, min(L, L - n + last + 1)) : L;
+  };
+  const int kv_end = active ? block_end(tok0) : 0;
+  const int wg_end = block_end(min(wg_tok0 + (kWavesPerGroup - 1) * QT, n - 1));
 
   MfmaWave<D, 16> st;
   st.init();
@@ -66,61 +93,96 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   const int log2_s = a.log2_steps;
   const size_t tile_b = (size_t)P * D * 2;
   const size_t head_b = (size_t)g * tile_b;
-  const uint32_t k_boff = (uint32_t)(g4 * P + r16) * 16;
-  const uint32_t v_boff = (uint32_t)(r16 * P + 4 * g4) * 2;
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
-  const int pages = (kv_end + P - 1) / P;
+  const int steps = (wg_end + 15) / 16;
+  const int chunks = (steps + kCh - 1) / kCh;
 
-  for (int jb = 0; jb < pages; jb += kWave) {
-    const int nb = min(kWave, pages - jb);
-    // Page ids of the next (up to) 64 pages, one per lane; -1 if unusable.
-    int vpage = -1;
-    {
-      const int pos = ip0 + jb + lane;
-      const bool ok = lane < nb && pos >= 0 && pos < a.num_indices;
-      const int pid = ok ? a.kv_indices[pos] : -1;
-      if (pid >= 0 && pid < a.num_pages) vpage = pid;
+  // Page of a step, -1 for an index outside kv_indices or the pool (its
+  // tokens are skipped).  Wave-uniform.
+  auto page_of = [&](int step) {
+    const int pos = ip0 + (step >> log2_s);
+    int pid = pos >= 0 && pos < a.num_indices ? a.kv_indices[pos] : -1;
+    if (pid >= a.num_pages) pid = -1;
+    return __builtin_amdgcn_readfirstlane(pid);
+  };
+  // Global -> registers: the workgroup's threads fetch 16-byte pieces
+  // tid, tid + 512, ... of a chunk, step by step, K pieces before V pieces.
+  // Piece y of a step's K is (channel block y / 16, token y % 16); piece y of
+  // its V is (channel y / 2, tokens 8 (y % 2) .. +7).  A wave's 64 pieces lie in
+  // one step and one operand, so page lookup and K/V choice are wave-uniform.
+  uint4 stage[kLoads];
+  auto piece = [&](int i, int& st, int& y, bool& is_v) {
+    const int xw = w * kWave + i * kGroupThreads;  // the wave's first piece
+    st = xw / (2 * kPieces);
+    const int yw = xw - st * 2 * kPieces;
+    is_v = yw >= kPieces;
+    y = yw - (is_v ? kPieces : 0) + lane;
+  };
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      int st, y;
+      bool is_v;
+      piece(i, st, y, is_v);
+      const int step = c * kCh + st;
+      const int pid = step < steps ? page_of(step) : -1;
+      if (pid < 0) {
+        stage[i] = make_uint4(0, 0, 0, 0);
+        continue;
+      }
+      const int sub = step & ((1 << log2_s) - 1);
+      const char* tile = (is_v ? vbase : kbase) + (size_t)pid * a.num_kv_heads * tile_b + head_b;
+      const int off = is_v ? ((y >> 1) * P + sub * 16 + 8 * (y & 1)) * 2
+                           : ((y >> 4) * P + sub * 16 + (y & 15)) * 16;
+      stage[i] = *reinterpret_cast<const uint4*>(tile + off);
     }
-    const int ns = nb << log2_s;
-    auto issue = [&](int j, Step<D>& sd) {
-      const int jc = j < ns ? j : ns - 1;
-      const int pg = jc >> log2_s;
-      const int sub = jc & ((1 << log2_s) - 1);
-      const int pid = __builtin_amdgcn_readlane(vpage, pg);
-      const size_t base = (size_t)(pid < 0 ? 0 : pid) * a.num_kv_heads * tile_b + head_b;
-      const char* kp = kbase + base + (size_t)sub * 16 * 16 + k_boff;
-      const char* vp = vbase + base + (size_t)sub * 16 * 2 + v_boff;
+  };
+  auto publish = [&](int buf) {
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)
-        sd.k[kk] = *reinterpret_cast<const uint4*>(kp + (size_t)kk * 4 * P * 16);
+    for (int i = 0; i < kLoads; ++i) {
+      int st, y;
+      bool is_v;
+      piece(i, st, y, is_v);
+      char* dst = is_v ? v_at(buf, st, y >> 1, 8 * (y & 1)) : k_at(buf, st, y >> 4, y & 15);
+      *reinterpret_cast<uint4*>(dst) = stage[i];
+    }
+  };
+
+  if (chunks > 0) {
+    fetch(0);
+    publish(0);
+  }
+  __syncthreads();
+  for (int c = 0; c < chunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < chunks) fetch(c + 1);  // in flight while this chunk is consumed
 #pragma unroll
-      for (int vb = 0; vb < D / 16; ++vb)
-        sd.v[vb] = *reinterpret_cast<const uint2*>(vp + (size_t)vb * 16 * P * 2);
-    };
-    auto consume = [&](int j, const Step<D>& sd) {
-      const int pg = j >> log2_s;
-      const int sub = j & ((1 << log2_s) - 1);
-      const int pid = __builtin_amdgcn_readlane(vpage, pg);
-      const int t0 = (jb + pg) * P + sub * 16;
-      const int live = pid < 0 ? 0 : min(16, max(0, kv_end - t0));
-      // Causal: key t0 + 4 g4 + i is visible to row r16 iff it is <= lim.
-      const int k0 = t0 + 4 * g4;
-      const uint32_t keep = (k0 + 0 <= lim ? 0x1u : 0u) | (k0 + 1 <= lim ? 0x100u : 0u) |
-                            (k0 + 2 <= lim ? 0x10000u : 0u) | (k0 + 3 <= lim ? 0x1000000u : 0u);
-      st.step(sd, live, g4, a.scale_log2, bias, keep);
-    };
-    Step<D> ring[kStages];
+    for (int s = 0; s < kCh; ++s) {
+      const int t0 = (c * kCh + s) * 16;
+      if (t0 < kv_end) {  // uniform per wave
+        Step<D> sd;
 #pragma unroll
-    for (int i = 0; i < kStages - 1; ++i) issue(i, ring[i]);
-    for (int j = 0; j < ns; j += kStages) {
+        for (int kk = 0; kk < D / 32; ++kk)
+          sd.k[kk] = *reinterpret_cast<const uint4*>(k_at(buf, s, 4 * kk + g4, r16));
 #pragma unroll
-      for (int i = 0; i < kStages; ++i) {
-        issue(j + i + kStages - 1, ring[(i + kStages - 1) % kStages]);
-        if (j + i < ns) consume(j + i, ring[i]);
+        for (int vb = 0; vb < D / 16; ++vb)
+          sd.v[vb] = *reinterpret_cast<const uint2*>(v_at(buf, s, 16 * vb + r16, 4 * g4));
+        const int live = page_of(c * kCh + s) < 0 ? 0 : min(16, kv_end - t0);
+        const int k0 = t0 + 4 * g4;
+        const uint32_t keep = (k0 + 0 <= lim ? 0x1u : 0u) | (k0 + 1 <= lim ? 0x100u : 0u) |
+                              (k0 + 2 <= lim ? 0x10000u : 0u) | (k0 + 3 <= lim ? 0x1000000u : 0u);
+        st.step(sd, live, g4, a.scale_log2, bias, keep);
       }
     }
+    // The other buffer held chunk c - 1, which every wave finished before the
+    // barrier that closed the previous iteration.
+    if (c + 1 < chunks) publish(buf ^ 1);
+    __syncthreads();
   }
+  // Every wave has passed the barrier after the last chunk: the K/V buffers
+  // are free for the output rows.
+  if (!active) return;
 
   // Normalise: the four lanes of row r hold its partial sums; register i of
   // lane group g holds row 4g + i.  Rows go through LDS so that every lane
@@ -133,7 +195,7 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
     const float inv = li > 0.f ? 1.0f / li : 0.f;
 #pragma unroll
     for (int vb = 0; vb < MfmaWave<D, 16>::VB; ++vb)
-      s_out[w][4 * g4 + i][16 * vb + r16] = st.o[vb][i] * inv;
+      s_out[(w * 16 + 4 * g4 + i) * D + 16 * vb + r16] = st.o[vb][i] * inv;
   }
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes land first
   constexpr int kChunks = ROWS * (D / 8);
@@ -143,8 +205,8 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
     const int c8 = (c - rr * (D / 8)) * 8;
     const int tok = tok0 + rr / HG;
     if (tok < n) {
-      const float4 x0 = *reinterpret_cast<const float4*>(&s_out[w][rr][c8]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&s_out[w][rr][c8 + 4]);
+      const float4 x0 = *reinterpret_cast<const float4*>(&s_out[(w * 16 + rr) * D + c8]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&s_out[(w * 16 + rr) * D + c8 + 4]);
       *reinterpret_cast<uint4*>(a.out + ((size_t)(q0 + tok) * Hq + hq0 + rr % HG) * D + c8) =
           make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
                      pack_bf16x2(x1.z, x1.w));
