@@ -255,7 +255,9 @@ int pkv_decode_masked(const pkv_pool* pool, const pkv_desc* desc, const void* q,
  *  out          device bf16 [total_q][num_q_heads][head_dim]
  * The descriptor gives the shapes (num_workgroups and min_tiles_per_group are
  * not used).  Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED,
- * PKV_ERR_CAPACITY (batch above max_batch or 65535), PKV_ERR_LAUNCH. */
+ * PKV_ERR_CAPACITY (batch above max_batch or 65535, or a grid of 2^31 or
+ * more workgroups: ceil(max_q_len / (8 * 16 / hg)) * (num_q_heads / hg) *
+ * batch, hg = query heads per workgroup row block, min(G, 4)), PKV_ERR_LAUNCH. */
 int pkv_prefill(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                 const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                 int32_t num_indices, const int32_t* seq_lens, int32_t batch, int32_t max_q_len,

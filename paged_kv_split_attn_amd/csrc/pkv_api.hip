@@ -278,6 +278,10 @@ int pkv_prefill(const pkv_pool* pool, const pkv_desc* desc, const void* q,
     return PKV_ERR_INVALID_ARG;
   if (batch > desc->max_batch || batch > 65535) return PKV_ERR_CAPACITY;
   if (batch == 0 || max_q_len == 0) return PKV_OK;
+  const int hg = heads_per_group(desc->num_q_heads / desc->num_kv_heads);
+  const long long per_group = 16 / hg * kWavesPerGroup;  // query tokens of one workgroup
+  if ((max_q_len + per_group - 1) / per_group * (desc->num_q_heads / hg) * batch > INT32_MAX)
+    return PKV_ERR_CAPACITY;
   PrefillArgs a;
   a.k = static_cast<const uint16_t*>(pool->k);
   a.v = static_cast<const uint16_t*>(pool->v);
@@ -296,7 +300,6 @@ int pkv_prefill(const pkv_pool* pool, const pkv_desc* desc, const void* q,
   a.causal = causal != 0;
   a.log2_steps = log2i(desc->page_size / 16);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  const int hg = heads_per_group(desc->num_q_heads / desc->num_kv_heads);
   return launch_status(launch_prefill(a, desc->head_dim, hg, max_q_len,
                                       static_cast<hipStream_t>(stream)));
 }

@@ -343,8 +343,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
 
     // Close the piece: total sum of each head over its four lanes; lane (0, i)
     // then holds head i's max and sum, and lanes 0..15 hold its output rows.
-    float lt = st.l + __shfl_xor(st.l, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
+    const float lt = sum_over_groups(st.l);
     const int seg = b * U + u;
     if (p == 0 && len == n) {
       // The whole segment lies in this wave: normalise its rows, transpose
@@ -601,17 +600,15 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     Combine4 x = mc[k];
 #pragma unroll
     for (int off = 16; off <= 32; off <<= 1) {
-      Combine4 y;
-      y.m = __shfl_xor(x.m, off, kWave);
-      y.den = __shfl_xor(x.den, off, kWave);
-      y.num.x = __shfl_xor(x.num.x, off, kWave);
-      y.num.y = __shfl_xor(x.num.y, off, kWave);
-      y.num.z = __shfl_xor(x.num.z, off, kWave);
-      y.num.w = __shfl_xor(x.num.w, off, kWave);
-      const bool lower = (lane & off) == 0;
-      Combine4 r = lower ? x : y;
-      const Combine4& other = lower ? y : x;
-      r.add(other.m, other.den, other.num);
+      // Both lanes of the pair get (lower, upper) and add the upper to the lower.
+      auto pr = [&](float v) { return off == 16 ? pair16(v) : pair32(v); };
+      const LanePair m = pr(x.m), den = pr(x.den), nx = pr(x.num.x), ny = pr(x.num.y),
+                     nz = pr(x.num.z), nw = pr(x.num.w);
+      Combine4 r;
+      r.m = m.lo;
+      r.den = den.lo;
+      r.num = f4{nx.lo, ny.lo, nz.lo, nw.lo};
+      r.add(m.hi, den.hi, f4{nx.hi, ny.hi, nz.hi, nw.hi});
       x = r;
     }
     if (q == 0 && tact) {

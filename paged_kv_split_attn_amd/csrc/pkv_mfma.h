@@ -36,6 +36,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
+// Cross-row exchange with the gfx950 row-swap permutes (VALU, no LDS round
+// trip): every lane of a pair (l, l ^ 16) or (l, l ^ 32) receives both values,
+// the lower lane's first, so a reduction over the pair gives the same bits in
+// both lanes.  Called with the whole wave active.
+struct LanePair {
+  float lo, hi;
+};
+__device__ __forceinline__ LanePair pair16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// Max / sum over the four lanes l % 16 + 16 k (the four lane groups).
+__device__ __forceinline__ float max_over_groups(float x) {
+  const LanePair a = pair16(x);
+  const LanePair b = pair32(fmaxf(a.lo, a.hi));
+  return fmaxf(b.lo, b.hi);
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  const LanePair a = pair16(x);
+  const LanePair b = pair32(a.lo + a.hi);
+  return b.lo + b.hi;
+}
+
 // MFMA operand vectors.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -104,9 +133,7 @@ struct MfmaWave {
     for (int i = 0; i < 4; ++i)
       if (((keep >> (8 * i)) & 0xffu) == 0) s[i] = kMinusInf;
     // Step max of row r over its 16 tokens (4 per lane, 4 lanes).
-    float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    pm = fmaxf(pm, __shfl_xor(pm, 16, kWave));
-    pm = fmaxf(pm, __shfl_xor(pm, 32, kWave));
+    const float pm = max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
     if (__builtin_amdgcn_ballot_w64(pm > m + kRescaleSlack) != 0) {
       const float mn = fmaxf(m, pm);
       const float alpha = fast_exp2(m - mn);

@@ -10,7 +10,7 @@
 // block, head group, request): every wave owns one block of 16 score rows --
 // 16 / HG query tokens times the HG query heads of a head group that share one
 // KV head -- and streams that KV head's pages up to the block's causal limit,
-// with the decode kernel's matrix-core step (pkv_mfma.h).  Query row i of a
+// 32 keys per matrix-core step.  Query row i of a
 // request with n rows and L keys sees keys 0 .. L - n + i when causal (the
 // mask aligned to the end of the KV, so n = 1 is decode).  Rows are
 // independent: no partials, no merge, no workspace.
@@ -19,37 +19,167 @@
 namespace pkv {
 namespace {
 
+// One wave's online softmax over 16 score rows, 32 keys per step.  Scores of
+// the step's two 16-key halves come from v_mfma_f32_16x16x32_bf16 as in the
+// decode step (K rows the A operand, q^T the B operand), leaving lane (g, r)
+// row r's scores of keys 4g .. 4g+3 of each half.  P . V then takes one
+// v_mfma_f32_16x16x32_bf16 per 16 channels and part of P, whose reduction
+// index runs over the eight keys lane group g holds (4g .. 4g+3 of half 0,
+// then of half 1): the weights never move between lanes, and the
+// double-rate instruction does twice the work of the 16-key one in the same
+// time.  P enters as bf16 hi + lo parts.  Output: lane (g, r) register i of
+// block vb holds O[row 4g+i][channel 16 vb + r].
+// Bits 4h + j (h, j < 2, 4) of the keys 16h + j <= d of a lane group's eight.
+__device__ __forceinline__ uint32_t keys_upto(int d) {
+  auto four = [](int x) { return x < 0 ? 0u : x >= 3 ? 15u : (2u << x) - 1u; };
+  return four(d) | (four(d - 16) << 4);
+}
+
+template <int D>
+struct Wave32 {
+  static constexpr int KB = D / 32;  // q.K MFMAs per half
+  static constexpr int VB = D / 16;  // p.V channel blocks
+  floatx4_t o[VB];
+  bf16x8_t qb[KB];  // q^T operand (zero for unused rows)
+  float m, l;       // row r: running max (log2 domain), partial sum
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) o[vb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m = kFloorMax;
+    l = 0.f;
+  }
+
+  // k[h][kk]: K of token r of half h, channels 8 (4kk + g) .. +8.
+  // load_v(vv) fills vv[vb] with channel 16 vb + r, keys 4g .. 4g+3 of half 0
+  // then of half 1; it runs once the scores are issued, so that K and V
+  // operands are not live at the same time.  keep: bit 4h + j set when key
+  // 16h + 4g + j counts for this lane's row.  vlive: keys from this one on
+  // hold no data (their V is zeroed); 32 when all do.
+  template <class LoadV>
+  __device__ __forceinline__ void step(const uint4 (&k)[2][KB], LoadV&& load_v, uint32_t keep,
+                                       int vlive, int g, float scale_log2, float bias) {
+    floatx4_t sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[0][kk]), qb[kk],
+                                                    sc0, 0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[1][kk]), qb[kk],
+                                                    sc1, 0, 0, 0);
+    }
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = fmaf(sc0[i], scale_log2, bias);
+      s[4 + i] = fmaf(sc1[i], scale_log2, bias);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (((keep >> i) & 1u) == 0) s[i] = kMinusInf;
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 vv[VB];
+    load_v(vv);
+    if (vlive < 32) {
+      // Keys past the sequence end may hold anything, NaN included: a zero
+      // weight times their V must give exactly zero.
+      const uint32_t lv = keys_upto(vlive - 1 - 4 * g);
+      uint32_t msk[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        msk[j] = ((lv >> (2 * j)) & 1u ? 0x0000ffffu : 0u) | ((lv >> (2 * j + 1)) & 1u ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        vv[vb].x &= msk[0];
+        vv[vb].y &= msk[1];
+        vv[vb].z &= msk[2];
+        vv[vb].w &= msk[3];
+      }
+    }
+    float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    pm = max_over_groups(fmaxf(pm, fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
+    if (__builtin_amdgcn_ballot_w64(pm > m + kRescaleSlack) != 0) {
+      const float mn = fmaxf(m, pm);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+      m = mn;
+      // Register i of lane group g holds row 4g + i, whose factor lane 4g + i has.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) o[vb][i] *= ai;
+      }
+    }
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[i] - m);
+    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    bf16x8_t phi, plo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = (__bf16)p[i];
+      phi[i] = h;
+      plo[i] = (__bf16)(p[i] - (float)h);
+    }
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+      const bf16x8_t vt = __builtin_bit_cast(bf16x8_t, vv[vb]);
+      o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vt, o[vb], 0, 0, 0);
+      o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vt, o[vb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the next step's K loads start after this one's V
+  }
+};
+
 template <int D, int HG>
 __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   constexpr int QT = 16 / HG;     // query tokens per wave block
   constexpr int ROWS = QT * HG;   // score rows in use (15 for HG = 3)
-  constexpr int kCh = 4;          // 16-token steps per LDS chunk
-  constexpr int kPieces = D * 16 * 2 / 16;  // 16-byte pieces of one step's K (same for V)
-  static_assert(2 * kPieces * kCh % kGroupThreads == 0 && kPieces % kWave == 0,
+  constexpr int kSteps = 2;       // 32-key steps per LDS chunk
+  constexpr int kHalves = 2 * kSteps;  // 16-key pieces per chunk (one page each at P = 16)
+  constexpr int kPieces = D * 16 * 2 / 16;  // 16-byte pieces of 16 keys' K (same for V)
+  static_assert(2 * kPieces * kHalves % kGroupThreads == 0 && kPieces % kWave == 0,
                 "whole, wave-uniform loads per thread");
-  constexpr int kLoads = 2 * kPieces * kCh / kGroupThreads;  // per thread and chunk
-  // Two chunks (double buffer) of K as [step][D/8][16][8] and V as
-  // [step][D][16] (the layouts of a 16-token tile); after the last chunk the
-  // same bytes hold the per-wave output rows [wave][16][D] in fp32.
-  constexpr int kKBytes = kCh * D * 16 * 2;
+  constexpr int kLoads = 2 * kPieces * kHalves / kGroupThreads;  // per thread and chunk
+  // Two chunks (double buffer) of K as [16 keys][D/8][16 keys][8 channels]
+  // and V as [32 keys][D/16][4][16 channels][2][4 keys]: the operand of lane
+  // (g, r) -- K channel block 4kk + g of key r, V keys 4g .. 4g+3 of both
+  // halves of channel 16 vb + r -- is 16 contiguous bytes, and the 16 lanes of
+  // a lane group read one contiguous run (no bank conflicts).  After the last
+  // chunk the same bytes hold the per-wave output rows [wave][16][D] in fp32.
+  constexpr int kKBytes = kHalves * D * 16 * 2;
   constexpr int kBufBytes = 2 * kKBytes;  // K + V of one chunk
   constexpr int kOutBytes = kWavesPerGroup * 16 * D * 4;
   __shared__ __align__(16) char smem[2 * kBufBytes > kOutBytes ? 2 * kBufBytes : kOutBytes];
-  auto k_at = [&](int buf, int st, int cb, int t) {  // 16 bytes: K channels 8cb.. of token t
-    return smem + buf * kBufBytes + ((st * (D / 8) + cb) * 16 + t) * 16;
+  auto k_at = [&](int buf, int hf, int cb, int t) {  // 16 bytes: K channels 8cb.. of key t
+    return smem + buf * kBufBytes + ((hf * (D / 8) + cb) * 16 + t) * 16;
   };
-  auto v_at = [&](int buf, int st, int ch, int t) {  // V channel ch from token t on
-    return smem + buf * kBufBytes + kKBytes + ((st * D + ch) * 16 + t) * 2;
+  auto v_at = [&](int buf, int st, int ch, int g, int hf) {  // 8 bytes: keys 4g.. of half hf
+    return smem + buf * kBufBytes + kKBytes +
+           ((((st * (D / 16) + (ch >> 4)) * 4 + g) * 16 + (ch & 15)) * 2 + hf) * 8;
   };
   float* s_out = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int b = blockIdx.z;
-  const int u = blockIdx.y;
-  const int wg_tok0 = blockIdx.x * kWavesPerGroup * QT;  // first query token of the workgroup
-  const int tok0 = wg_tok0 + w * QT;                      // first query token of this wave
+  // Tile order.  Workgroups go to the XCDs round robin by linear id; the
+  // order below gives each XCD whole runs of query blocks of one (request,
+  // head group), so that their K/V chunks stay in that XCD's L2, and puts
+  // the blocks with the longest causal range first in each run.
+  int b, u, bx;
+  {
+    const uint32_t gx = gridDim.x, gy = gridDim.y;
+    const uint32_t n_wg = gx * gy * gridDim.z;  // below 2^31 (checked on the host)
+    uint32_t t = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const uint32_t full = n_wg & ~(uint32_t)(kXcds - 1);
+    if (t < full) t = (t % kXcds) * (full / kXcds) + t / kXcds;
+    bx = (int)(gx - 1 - t % gx);
+    u = (int)((t / gx) % gy);
+    b = (int)(t / (gx * gy));
+  }
+  const int wg_tok0 = bx * kWavesPerGroup * QT;  // first query token of the workgroup
+  const int tok0 = wg_tok0 + w * QT;              // first query token of this wave
   const int q0 = a.qo_indptr[b];
   const int n = a.qo_indptr[b + 1] - q0;
   if (wg_tok0 >= n) return;  // uniform over the workgroup
@@ -76,17 +206,20 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   const int kv_end = active ? block_end(tok0) : 0;
   const int wg_end = block_end(min(wg_tok0 + (kWavesPerGroup - 1) * QT, n - 1));
 
-  MfmaWave<D, 16> st;
+  Wave32<D> st;
   st.init();
   {
     // q^T operand: lane (g4, r16) supplies row r16, channels 8*(4kk + g4) .. +8.
     const uint4* qp = reinterpret_cast<const uint4*>(
         a.q + ((size_t)(q0 + (rvalid ? rt : 0)) * Hq + hq0 + r16 % HG) * D + g4 * 8);
 #pragma unroll
-    for (int kk = 0; kk < MfmaWave<D, 16>::KB; ++kk) {
+    for (int kk = 0; kk < Wave32<D>::KB; ++kk) {
       const uint4 w4 = rvalid ? qp[4 * kk] : make_uint4(0, 0, 0, 0);
       st.qb[kk] = __builtin_bit_cast(bf16x8_t, w4);
     }
+    // Wait for q here: left to the first matrix-core step, the wait would sit
+    // inside the KV loop and drain the next chunk's loads with it every step.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
 
   const int P = a.page_size;
@@ -95,43 +228,54 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   const size_t head_b = (size_t)g * tile_b;
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
-  const int steps = (wg_end + 15) / 16;
-  const int chunks = (steps + kCh - 1) / kCh;
+  const int halves = (wg_end + 15) / 16;  // 16-key pieces the workgroup reads
+  const int chunks = (halves + kHalves - 1) / kHalves;
 
-  // Page of a step, -1 for an index outside kv_indices or the pool (its
-  // tokens are skipped).  Wave-uniform.
-  auto page_of = [&](int step) {
-    const int pos = ip0 + (step >> log2_s);
-    int pid = pos >= 0 && pos < a.num_indices ? a.kv_indices[pos] : -1;
-    if (pid >= a.num_pages) pid = -1;
-    return __builtin_amdgcn_readfirstlane(pid);
+  // Page ids are read 64 at a time, one per lane, and taken out with a
+  // uniform readlane (a vector load of a uniform address would need a wait
+  // that also drains the K/V loads in flight).  Page of a 16-key piece: -1 for
+  // an index outside kv_indices or the pool (its keys are skipped).
+  int vblk = -1, vpage = -1;
+  auto page_of = [&](int hf) {
+    const int pg = hf >> log2_s;
+    if ((pg >> 6) != vblk) {  // uniform; once per 64 pages
+      vblk = pg >> 6;
+      const int pos = ip0 + (vblk << 6) + lane;
+      vpage = pos >= 0 && pos < a.num_indices ? a.kv_indices[pos] : -1;
+      if (vpage >= a.num_pages) vpage = -1;
+    }
+    return __builtin_amdgcn_readlane(vpage, pg & 63);
   };
   // Global -> registers: the workgroup's threads fetch 16-byte pieces
-  // tid, tid + 512, ... of a chunk, step by step, K pieces before V pieces.
-  // Piece y of a step's K is (channel block y / 16, token y % 16); piece y of
-  // its V is (channel y / 2, tokens 8 (y % 2) .. +7).  A wave's 64 pieces lie in
-  // one step and one operand, so page lookup and K/V choice are wave-uniform.
+  // tid, tid + 512, ... of a chunk, 16 keys at a time, K pieces before V
+  // pieces.  Piece y of 16 keys' K is (channel block y / 16, key y % 16);
+  // piece y of their V is (channel y / 2, keys 8 (y % 2) .. +7).  A wave's 64
+  // pieces lie in one 16-key piece and one operand, so page lookup and K/V
+  // choice are wave-uniform.
   uint4 stage[kLoads];
-  auto piece = [&](int i, int& st, int& y, bool& is_v) {
+  int pids[kHalves];  // pages of the 16-key pieces of the chunk being fetched
+  auto piece = [&](int i, int& hf, int& y, bool& is_v) {
     const int xw = w * kWave + i * kGroupThreads;  // the wave's first piece
-    st = xw / (2 * kPieces);
-    const int yw = xw - st * 2 * kPieces;
+    hf = xw / (2 * kPieces);
+    const int yw = xw - hf * 2 * kPieces;
     is_v = yw >= kPieces;
     y = yw - (is_v ? kPieces : 0) + lane;
   };
   auto fetch = [&](int c) {
 #pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf)
+      pids[hf] = c * kHalves + hf < halves ? page_of(c * kHalves + hf) : -1;
+#pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      int st, y;
+      int hf, y;
       bool is_v;
-      piece(i, st, y, is_v);
-      const int step = c * kCh + st;
-      const int pid = step < steps ? page_of(step) : -1;
+      piece(i, hf, y, is_v);
+      const int pid = pids[hf];
       if (pid < 0) {
         stage[i] = make_uint4(0, 0, 0, 0);
         continue;
       }
-      const int sub = step & ((1 << log2_s) - 1);
+      const int sub = (c * kHalves + hf) & ((1 << log2_s) - 1);
       const char* tile = (is_v ? vbase : kbase) + (size_t)pid * a.num_kv_heads * tile_b + head_b;
       const int off = is_v ? ((y >> 1) * P + sub * 16 + 8 * (y & 1)) * 2
                            : ((y >> 4) * P + sub * 16 + (y & 15)) * 16;
@@ -141,11 +285,18 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   auto publish = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      int st, y;
+      int hf, y;
       bool is_v;
-      piece(i, st, y, is_v);
-      char* dst = is_v ? v_at(buf, st, y >> 1, 8 * (y & 1)) : k_at(buf, st, y >> 4, y & 15);
-      *reinterpret_cast<uint4*>(dst) = stage[i];
+      piece(i, hf, y, is_v);
+      if (is_v) {  // keys 8h .. 8h+7 of one channel: two 4-key pieces
+        const int ch = y >> 1, h = y & 1;
+        *reinterpret_cast<uint2*>(v_at(buf, hf >> 1, ch, 2 * h, hf & 1)) =
+            make_uint2(stage[i].x, stage[i].y);
+        *reinterpret_cast<uint2*>(v_at(buf, hf >> 1, ch, 2 * h + 1, hf & 1)) =
+            make_uint2(stage[i].z, stage[i].w);
+      } else {
+        *reinterpret_cast<uint4*>(k_at(buf, hf, y >> 4, y & 15)) = stage[i];
+      }
     }
   };
 
@@ -156,23 +307,32 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   __syncthreads();
   for (int c = 0; c < chunks; ++c) {
     const int buf = c & 1;
+    int live_pids[kHalves];
+#pragma unroll
+    for (int hf = 0; hf < kHalves; ++hf) live_pids[hf] = pids[hf];
     if (c + 1 < chunks) fetch(c + 1);  // in flight while this chunk is consumed
 #pragma unroll
-    for (int s = 0; s < kCh; ++s) {
-      const int t0 = (c * kCh + s) * 16;
+    for (int s = 0; s < kSteps; ++s) {
+      const int t0 = (c * kSteps + s) * 32;
       if (t0 < kv_end) {  // uniform per wave
-        Step<D> sd;
+        uint4 kop[2][Wave32<D>::KB];
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-          sd.k[kk] = *reinterpret_cast<const uint4*>(k_at(buf, s, 4 * kk + g4, r16));
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int vb = 0; vb < D / 16; ++vb)
-          sd.v[vb] = *reinterpret_cast<const uint2*>(v_at(buf, s, 16 * vb + r16, 4 * g4));
-        const int live = page_of(c * kCh + s) < 0 ? 0 : min(16, kv_end - t0);
-        const int k0 = t0 + 4 * g4;
-        const uint32_t keep = (k0 + 0 <= lim ? 0x1u : 0u) | (k0 + 1 <= lim ? 0x100u : 0u) |
-                              (k0 + 2 <= lim ? 0x10000u : 0u) | (k0 + 3 <= lim ? 0x1000000u : 0u);
-        st.step(sd, live, g4, a.scale_log2, bias, keep);
+          for (int kk = 0; kk < Wave32<D>::KB; ++kk)
+            kop[h][kk] = *reinterpret_cast<const uint4*>(k_at(buf, 2 * s + h, 4 * kk + g4, r16));
+        auto load_v = [&](uint4 (&vv)[Wave32<D>::VB]) {
+#pragma unroll
+          for (int vb = 0; vb < Wave32<D>::VB; ++vb)
+            vv[vb] = *reinterpret_cast<const uint4*>(v_at(buf, s, 16 * vb + r16, g4, 0));
+        };
+        const int vlive = min(32, kv_end - t0);
+        // Key t0 + 16h + 4 g4 + j counts when it is at most min(lim, kv_end - 1)
+        // and its page exists.
+        uint32_t keep = keys_upto(min(lim, kv_end - 1) - t0 - 4 * g4);
+        if (live_pids[2 * s] < 0) keep &= 0xf0u;
+        if (live_pids[2 * s + 1] < 0) keep &= 0x0fu;
+        st.step(kop, load_v, keep, vlive, g4, a.scale_log2, bias);
       }
     }
     // The other buffer held chunk c - 1, which every wave finished before the
@@ -187,14 +347,13 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   // Normalise: the four lanes of row r hold its partial sums; register i of
   // lane group g holds row 4g + i.  Rows go through LDS so that every lane
   // writes 8 channels (16 bytes) of one row.
-  float lt = st.l + __shfl_xor(st.l, 16, kWave);
-  lt += __shfl_xor(lt, 32, kWave);
+  const float lt = sum_over_groups(st.l);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float li = __shfl(lt, 4 * g4 + i, kWave);
     const float inv = li > 0.f ? 1.0f / li : 0.f;
 #pragma unroll
-    for (int vb = 0; vb < MfmaWave<D, 16>::VB; ++vb)
+    for (int vb = 0; vb < Wave32<D>::VB; ++vb)
       s_out[(w * 16 + 4 * g4 + i) * D + 16 * vb + r16] = st.o[vb][i] * inv;
   }
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes land first
@@ -235,6 +394,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int hg, int max_q_
   const int per_group = qt * kWavesPerGroup;  // query tokens one workgroup covers
   const dim3 grid((max_q_len + per_group - 1) / per_group, a.num_q_heads / hg, a.batch);
   if (grid.x == 0 || grid.z == 0) return hipSuccess;
+  if ((long long)grid.x * grid.y * grid.z > INT32_MAX) return hipErrorInvalidConfiguration;
   if (head_dim == 128) return launch_p<128>(a, hg, grid, s);
   if (head_dim == 64) return launch_p<64>(a, hg, grid, s);
   return hipErrorInvalidValue;
