@@ -34,6 +34,9 @@ the hunk or bullet, as the pages have no section numbers):
   by exp(lse_s - max lse).
 * KV append: the token written this step goes to position seq_len - 1
   (cache.py, bind_tasks: write_pos = seq_lens - 1).
+* Token-major K/V (decode_tokens): one [Hkv, D] row per token slot, found
+  through a request-to-token table (page size 1) or at b * stride + t in the
+  contiguous [batch, seq, kv_heads, head_dim] layout of the non-paged decode.
 
 Readings taken where the pages are silent:
 kv_indptr in pages; KV head of query head hq is hq // G; seq_len includes
@@ -64,6 +67,7 @@ __all__ = [
     "softmax_attend",
     "decode",
     "decode_masked",
+    "decode_tokens",
     "prefill",
     "chunk_partial",
     "merge_partials",
@@ -164,6 +168,40 @@ def decode_masked(q_bits, k_pool, v_pool, indptr, indices, seq_lens, sm_scale: f
         keep = keep_all[b, :L]
         Kd = gather_request(k_pool, indptr, indices, b, L, P)[keep]
         Vd = gather_request(v_pool, indptr, indices, b, L, P)[keep]
+        for hq in range(Hq):
+            h = kv_head_of(hq, G)
+            out[b, hq] = softmax_attend(q[b, hq], Kd[:, h, :], Vd[:, h, :], sm_scale)
+    return out
+
+
+def decode_tokens(q_bits, k_cache, v_cache, seq_lens, sm_scale: float, slot_table=None,
+                  stride: int = 0) -> np.ndarray:
+    """Decode attention over token-major K/V -> float64 [B, Hq, D].
+
+    ``k_cache`` / ``v_cache`` hold one row [Hkv, D] per token slot.  Token t of
+    request b is slot ``slot_table[b, t]``: the token-level mode in which the
+    request-to-token table serves as the page table with page size 1 (commits
+    by ViperEkura: the bullet on the CUDA backend's decode).  Without a table it
+    is slot b * stride + t: the contiguous K/V of the non-paged decode wrapper,
+    laid out [batch, seq_len, kv_heads, head_dim] (AstrAI compare
+    v1.3.12..6f09b1d, attention_ops.py: attn_decode and the BLHD TensorLayout),
+    here with a per-request length.  That wrapper's causal flag puts the
+    causal offset at the last key, so every key of a decode query counts.
+    """
+    q = bf16_to_f64(q_bits)
+    B, Hq, D = q.shape
+    k_all = np.asarray(k_cache)
+    Hkv = k_all.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if slot_table is None:
+            slots = b * int(stride) + np.arange(L)
+        else:
+            slots = np.asarray(slot_table)[b, :L].astype(np.int64)
+        Kd = bf16_to_f64(k_all[slots])
+        Vd = bf16_to_f64(np.asarray(v_cache)[slots])
         for hq in range(Hq):
             h = kv_head_of(hq, G)
             out[b, hq] = softmax_attend(q[b, hq], Kd[:, h, :], Vd[:, h, :], sm_scale)

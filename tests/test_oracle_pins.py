@@ -25,7 +25,11 @@ mathematics of softmax attention and from invariants the method must keep:
     decode bit for bit, causal row i is the decode of the first L - n + i + 1
     tokens, the non-causal rows all see L tokens, and with an identity page
     table and no prefix the causal result is torch's scaled_dot_product_attention
-    (is_causal) in float64.
+    (is_causal) in float64;
+12. token-major K/V: brute force over each request's slots (table and
+    contiguous), the paged batches stored token-major give the paged decode
+    bit for bit, the contiguous layout equals the table b * stride + t, and a
+    one-token request returns that slot's V row.
 
 ``test_planted_mistakes`` plants plausible mistakes in the oracle (on the CPU)
 and checks that at least one pin fails for each.
@@ -502,9 +506,71 @@ def pin_prefill(mod):
     assert np.max(np.abs(got - ref.permute(1, 0, 2).numpy())) < 1e-12
 
 
+# ------------------------------------------------------ token-major (pin 12)
+
+def token_batches():
+    lens = np.array([7, 0, 1, 12])
+    return (W.make_tokens(name="tok", seed=41, B=4, Hq=4, Hkv=2, D=8, lengths=lens),
+            W.make_tokens(name="contig", seed=42, B=4, Hq=8, Hkv=2, D=8, lengths=lens,
+                          table=False, stride=13))
+
+
+def run_tokens(mod, tb):
+    return mod.decode_tokens(tb.q, tb.k_cache, tb.v_cache, tb.seq_lens, tb.sm_scale,
+                             tb.slot_table, tb.stride)
+
+
+def brute_force_tokens(tb):
+    out = np.zeros((tb.B, tb.Hq, tb.D))
+    for b in range(tb.B):
+        L = int(tb.seq_lens[b])
+        slots = [int(tb.slot_table[b][t]) if tb.slot_table is not None else b * tb.stride + t
+                 for t in range(L)]
+        if not slots:
+            continue
+        for hq in range(tb.Hq):
+            h = (hq * tb.Hkv) // tb.Hq
+            qv = [_bf16_py(tb.q[b, hq, d]) for d in range(tb.D)]
+            xs = [tb.sm_scale * math.fsum(a * _bf16_py(tb.k_cache[sl, h, d])
+                                          for d, a in enumerate(qv)) for sl in slots]
+            m = max(xs)
+            ws = [math.exp(x - m) for x in xs]
+            den = math.fsum(ws)
+            for d in range(tb.D):
+                out[b, hq, d] = math.fsum(w * _bf16_py(tb.v_cache[sl, h, d])
+                                          for w, sl in zip(ws, slots)) / den
+    return out
+
+
+def pin_tokens(mod):
+    for tb in token_batches():
+        got = run_tokens(mod, tb)
+        assert np.isfinite(got).all()
+        assert np.max(np.abs(got - brute_force_tokens(tb))) < 1e-12
+    # the paged batches stored token-major: the paged decode, bit for bit
+    for batch in (W.config(1), tiny_batch(), gqa8_batch()):
+        assert np.array_equal(run_tokens(mod, W.tokens_from_pages(batch)), run_decode(mod, batch))
+    # the contiguous layout is the table b * stride + t
+    _, contig = token_batches()
+    ident = np.full((contig.B, contig.stride), -1, np.int32)
+    for b in range(contig.B):
+        L = int(contig.seq_lens[b])
+        ident[b, :L] = b * contig.stride + np.arange(L)
+    with_table = mod.decode_tokens(contig.q, contig.k_cache, contig.v_cache, contig.seq_lens,
+                                   contig.sm_scale, ident, 0)
+    assert np.array_equal(with_table, run_tokens(mod, contig))
+    # one token: its V row
+    one = W.make_tokens(name="one", seed=43, B=2, Hq=4, Hkv=2, D=8, lengths=np.array([1, 1]))
+    got = run_tokens(mod, one)
+    for b in range(2):
+        for hq in range(4):
+            row = W.bf16_bits_to_f32(one.v_cache[one.slot_table[b, 0], hq // 2]).astype(np.float64)
+            assert np.array_equal(got[b, hq], row)
+
+
 PINS = [pin_brute_force, pin_seq_len_one, pin_permutation, pin_split_invariance, pin_q_zero,
         pin_constant_v, pin_dominant_key, pin_sdpa, pin_kv_indptr, pin_plan, pin_stream_pieces,
-        pin_append, pin_poison, pin_mask, pin_prefill]
+        pin_append, pin_poison, pin_mask, pin_prefill, pin_tokens]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -645,6 +711,27 @@ def _mutants():
                     out[int(qo[b]) + i] = OA.decode(qi, k, v, ip, idx, sl_b, sc, P)[b]
         return out
     m["prefill_causal_one_short"] = {"prefill": prefill_causal_one_short}
+
+    def tokens_next_slot(q, k, v, sl, sc, table=None, stride=0):
+        # a slip in the table walk: every token read from the slot after its own
+        if table is None:
+            return OA.__dict__["_orig_decode_tokens"](q, k[1:], v[1:], sl, sc, None, stride)
+        return OA.__dict__["_orig_decode_tokens"](q, k, v, sl, sc,
+                                                  np.where(np.asarray(table) >= 0,
+                                                           (np.asarray(table) + 1) % len(k), -1),
+                                                  stride)
+    m["tokens_next_slot"] = {"decode_tokens": tokens_next_slot}
+
+    def tokens_packed_rows(q, k, v, sl, sc, table=None, stride=0):
+        # contiguous rows read back to back, ignoring the row stride
+        if table is not None:
+            return OA.__dict__["_orig_decode_tokens"](q, k, v, sl, sc, table, stride)
+        starts = np.concatenate([[0], np.cumsum(np.asarray(sl, np.int64))[:-1]])
+        packed = np.full((len(sl), max(1, stride)), -1, np.int64)
+        for b in range(len(sl)):
+            packed[b, : int(sl[b])] = starts[b] + np.arange(int(sl[b]))
+        return OA.__dict__["_orig_decode_tokens"](q, k, v, sl, sc, packed, 0)
+    m["tokens_packed_rows"] = {"decode_tokens": tokens_packed_rows}
     return m
 
 
@@ -654,7 +741,7 @@ MUTANTS = _mutants()
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistakes(name, monkeypatch):
     for fn in ("softmax_attend", "chunk_partial", "plan_stream", "decode_pieces", "append_kv",
-               "decode_masked", "prefill"):
+               "decode_masked", "prefill", "decode_tokens"):
         monkeypatch.setitem(OA.__dict__, "_orig_" + fn, getattr(OA, fn))
     for attr, repl in MUTANTS[name].items():
         monkeypatch.setattr(OA, attr, repl)

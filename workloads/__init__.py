@@ -49,6 +49,10 @@ __all__ = [
     "v_pool_token_major",
     "k_pool_blocked",
     "k_pool_token_major",
+    "TokenBatch",
+    "make_tokens",
+    "tokens_from_pages",
+    "tokens_to_device",
 ]
 
 
@@ -424,4 +428,118 @@ def to_device(batch: DecodeBatch, device="cuda:0") -> dict:
     if batch.q_rows is not None:
         d["q_rows"] = bits(batch.q_rows)
         d["qo_indptr"] = torch.from_numpy(batch.qo_indptr.astype(np.int32)).to(device)
+    return d
+
+
+# ------------------------------------------------------------ token-major K/V
+
+@dataclass
+class TokenBatch:
+    """Decode inputs over token-major K/V: one row [Hkv][D] per token slot.
+
+    Token t of request b is slot ``slot_table[b, t]`` (the token-level mode:
+    a request-to-token table used as a page table with page size 1) or, when
+    ``slot_table`` is None, slot ``b * stride + t`` (the contiguous layout
+    [batch, seq, kv_heads, head_dim], flattened over batch and seq).  Table
+    entries at t >= seq_lens[b] are -1 and are not read.
+    """
+
+    name: str
+    seed: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    seq_lens: np.ndarray  # int32 [B]
+    stride: int  # table row length / tokens per request row of the contiguous layout
+    slot_table: Optional[np.ndarray]  # int32 [B, stride] or None (contiguous)
+    num_slots: int
+    q: np.ndarray  # uint16 [B, Hq, D]
+    k_cache: np.ndarray  # uint16 [num_slots, Hkv, D]
+    v_cache: np.ndarray  # uint16 [num_slots, Hkv, D]
+    sm_scale: float
+    poisoned: bool = False
+
+
+def make_tokens(*, name: str, seed: int, B: int, Hq: int, Hkv: int, D: int, lengths,
+                table: bool = True, stride: Optional[int] = None, slot_slack: float = 0.10,
+                poison: bool = True) -> TokenBatch:
+    """Token-major batch.  With ``table`` the tokens of all requests sit at
+    random slots of a shuffled cache of ceil((1 + slot_slack) * tokens) slots;
+    without it the cache is the contiguous [B, stride, Hkv, D] array.  Unwritten
+    slots hold bf16 NaN when ``poison``.  Draw order: lengths, slot permutation
+    (table mode), q, K cache, V cache."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    seq = lengths(rng) if callable(lengths) else lengths
+    seq = np.asarray(seq, dtype=np.int64).reshape(B)
+    S = int(stride) if stride is not None else max(1, int(seq.max(initial=0)))
+    if int(seq.max(initial=0)) > S:
+        raise ValueError("stride below the longest request")
+    total = int(seq.sum())
+    slot_table = None
+    written = None
+    if table:
+        num_slots = max(1, math.ceil((1.0 + slot_slack) * total))
+        perm = rng.permutation(num_slots).astype(np.int32)
+        slot_table = np.full((B, S), -1, dtype=np.int32)
+        cur = 0
+        for b in range(B):
+            L = int(seq[b])
+            slot_table[b, :L] = perm[cur : cur + L]
+            cur += L
+        written = np.zeros(num_slots, dtype=bool)
+        written[perm[:total]] = True
+    else:
+        num_slots = B * S
+        written = np.zeros((B, S), dtype=bool)
+        for b in range(B):
+            written[b, : int(seq[b])] = True
+        written = written.reshape(-1)
+    q = normal_bf16(rng, (B, Hq, D))
+    k = normal_bf16(rng, (num_slots, Hkv, D))
+    v = normal_bf16(rng, (num_slots, Hkv, D))
+    if poison:
+        k[~written] = BF16_QNAN
+        v[~written] = BF16_QNAN
+    return TokenBatch(name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, D=D,
+                      seq_lens=seq.astype(np.int32), stride=S, slot_table=slot_table,
+                      num_slots=num_slots, q=q, k_cache=k, v_cache=v,
+                      sm_scale=1.0 / math.sqrt(D), poisoned=poison)
+
+
+def tokens_from_pages(batch: DecodeBatch) -> TokenBatch:
+    """The same K/V as a paged batch, stored token-major: slot p * P + o holds
+    offset o of page p, and the table lists each request's token slots."""
+    P = batch.P
+    k = np.ascontiguousarray(np.swapaxes(batch.k_pool, 1, 2)).reshape(-1, batch.Hkv, batch.D)
+    v = np.ascontiguousarray(np.swapaxes(batch.v_pool, 1, 2)).reshape(-1, batch.Hkv, batch.D)
+    S = max(1, int(np.max(batch.seq_lens, initial=0)))
+    table = np.full((batch.B, S), -1, dtype=np.int32)
+    for b in range(batch.B):
+        L = int(batch.seq_lens[b])
+        t = np.arange(L)
+        table[b, :L] = batch.page_lists[b][t // P] * P + t % P
+    return TokenBatch(name=batch.name + "_tokens", seed=batch.seed, B=batch.B, Hq=batch.Hq,
+                      Hkv=batch.Hkv, D=batch.D, seq_lens=batch.seq_lens.copy(), stride=S,
+                      slot_table=table, num_slots=k.shape[0], q=batch.q, k_cache=k,
+                      v_cache=v, sm_scale=batch.sm_scale, poisoned=batch.poisoned)
+
+
+def tokens_to_device(tb: TokenBatch, device="cuda:0") -> dict:
+    """Device copies of a token batch (bf16 bits as int16; the slot table, if
+    any, as int32).  Data movement only."""
+    import torch
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+    d = {
+        "q": bits(tb.q),
+        "k_cache": bits(tb.k_cache),
+        "v_cache": bits(tb.v_cache),
+        "seq_lens": torch.from_numpy(tb.seq_lens.astype(np.int32)).to(device),
+        "slot_table": None,
+    }
+    if tb.slot_table is not None:
+        d["slot_table"] = torch.from_numpy(np.ascontiguousarray(tb.slot_table, np.int32)).to(device)
     return d
