@@ -236,6 +236,37 @@ int pkv_decode_masked(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                       int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
                       void* out, void* stream);
 
+/* Decode attention over token-major K/V (one launch): one [num_kv_heads]
+ * [head_dim] row per token slot instead of pages.  Covers the token-level mode
+ * in which the request-to-token table is the page table with page size 1
+ * (commits by ViperEkura, the bullet on the CUDA backend's decode) and, with no
+ * table, the contiguous K/V of the non-paged decode wrapper, laid out [batch,
+ * seq_len, kv_heads, head_dim] (attention_ops.py, attn_decode and the BLHD
+ * layout, on the compare page), here with per-request lengths.
+ *  desc         as for pkv_decode, with page_size 16: the plan cuts each request
+ *               into 16-token blocks
+ *  k_cache, v_cache  device bf16 [num_slots][num_kv_heads][head_dim]
+ *  num_slots    slots in the caches, >= 1
+ *  slot_table   device int32 [batch][table_stride]: slot of token t of request
+ *               b at slot_table[b * table_stride + t] (entries at t >=
+ *               seq_lens[b] are not read), or NULL: slot b * table_stride + t,
+ *               which needs batch * table_stride <= num_slots
+ *  table_stride tokens per table row (request row of the contiguous layout);
+ *               batch * table_stride < 2^31
+ *  kv_indptr    device int32 [batch + 1] from pkv_build_metadata(desc, seq_lens)
+ *               (the plan of the same call)
+ * q, seq_lens, batch, sm_scale, the workspace and out are as for pkv_decode.
+ * A token at t >= table_stride or with a slot outside [0, num_slots) is
+ * dropped and sets a bit in the workspace error word.  Errors: those of
+ * pkv_decode; PKV_ERR_INVALID_ARG for page_size other than 16, NULL caches or a
+ * contiguous layout larger than the caches; PKV_ERR_CAPACITY for
+ * batch * table_stride >= 2^31. */
+int pkv_decode_tokens(const pkv_desc* desc, const void* k_cache, const void* v_cache,
+                      int32_t num_slots, const int32_t* slot_table, int32_t table_stride,
+                      const void* q, const int32_t* kv_indptr, const int32_t* seq_lens,
+                      int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
+                      void* out, void* stream);
+
 /* Paged prefill / extend attention of one layer (one launch, no workspace).
  * Request b has n_b = qo_indptr[b+1] - qo_indptr[b] query rows (its newest
  * tokens) and attends to its L_b = seq_lens[b] cached tokens, the new ones

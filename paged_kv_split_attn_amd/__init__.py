@@ -36,6 +36,7 @@ __all__ = [
     "pkv_decode",
     "pkv_decode_append",
     "pkv_decode_masked",
+    "pkv_decode_tokens",
     "pkv_prefill",
     "pkv_debug_validate",
     "WAVES_PER_GROUP",
@@ -114,6 +115,9 @@ _SIGNATURES = {
     "pkv_decode_masked": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp,
                                          _i32, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
                                          ctypes.c_size_t, _vp, _vp]),
+    "pkv_decode_tokens": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _vp, _i32, _vp, _i32, _vp,
+                                         _vp, _vp, _i32, ctypes.c_float, _vp, ctypes.c_size_t,
+                                         _vp, _vp]),
     "pkv_prefill": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp, _vp,
                                    _vp, _i32, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp]),
     "pkv_debug_validate": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _vp, _vp, _i32, _i32, _i32,
@@ -307,6 +311,30 @@ def pkv_decode_masked(pool: Pool, desc: Desc, q: torch.Tensor, mask: torch.Tenso
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(out, "out", _BF16, n), _stream(stream))
     _check("pkv_decode_masked", st)
+
+
+def pkv_decode_tokens(desc: Desc, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      slot_table: Optional[torch.Tensor], table_stride: int, q: torch.Tensor,
+                      kv_indptr: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float,
+                      workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """Decode over token-major K/V [num_slots, Hkv, D]: through slot_table
+    [batch, table_stride] (int32), or contiguous (slot b * table_stride + t)
+    when slot_table is None.  desc.page_size must be 16."""
+    B = seq_lens.numel()
+    n = B * desc.num_q_heads * desc.head_dim
+    row = desc.num_kv_heads * desc.head_dim
+    if k_cache.numel() % row or v_cache.numel() != k_cache.numel():
+        raise ValueError("k_cache and v_cache must be [num_slots, num_kv_heads, head_dim]")
+    table = 0
+    if slot_table is not None:
+        table = _ptr(slot_table, "slot_table", _I32, B * int(table_stride))
+    st = load_library().pkv_decode_tokens(
+        ctypes.byref(desc.c()), _ptr(k_cache, "k_cache", _BF16), _ptr(v_cache, "v_cache", _BF16),
+        k_cache.numel() // row, table or None, int(table_stride), _ptr(q, "q", _BF16, n),
+        _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(seq_lens, "seq_lens", _I32), B,
+        float(sm_scale), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(out, "out", _BF16, n), _stream(stream))
+    _check("pkv_decode_tokens", st)
 
 
 def pkv_prefill(pool: Pool, desc: Desc, q: torch.Tensor, qo_indptr: torch.Tensor,

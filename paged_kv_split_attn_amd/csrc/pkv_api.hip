@@ -109,7 +109,7 @@ const char* pkv_status_str(int status) {
   }
 }
 
-int32_t pkv_version(void) { return (2 << 16) | 3; }
+int32_t pkv_version(void) { return (2 << 16) | 4; }
 
 size_t pkv_workspace_bytes(const pkv_desc* desc) {
   WsLayout L;
@@ -226,6 +226,10 @@ int decode_impl(const pkv_pool* pool, const pkv_desc* desc, const void* q, const
   d.units = desc->num_q_heads / hg;
   d.log2_steps = log2i(desc->page_size / 16);
   d.scale_log2 = sm_scale * 1.4426950408889634f;
+  d.token_major = 0;
+  d.slot_table = nullptr;
+  d.table_stride = 0;
+  d.num_slots = 0;
   return launch_status(
       launch_decode(d, desc->head_dim, hg, L.groups, static_cast<hipStream_t>(stream)));
 }
@@ -262,6 +266,52 @@ int pkv_decode_append(const pkv_pool* pool, const pkv_desc* desc, const void* q,
   if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
   return decode_impl(pool, desc, q, k_new, v_new, nullptr, 0, kv_indptr, kv_indices, num_indices,
                      seq_lens, batch, sm_scale, workspace, workspace_bytes, out, stream);
+}
+
+int pkv_decode_tokens(const pkv_desc* desc, const void* k_cache, const void* v_cache,
+                      int32_t num_slots, const int32_t* slot_table, int32_t table_stride,
+                      const void* q, const int32_t* kv_indptr, const int32_t* seq_lens,
+                      int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
+                      void* out, void* stream) {
+  WsLayout L;
+  int st = check_desc(desc, &L);
+  if (st != PKV_OK) return st;
+  if (desc->page_size != 16) return PKV_ERR_INVALID_ARG;
+  if (!k_cache || !v_cache || !q || !kv_indptr || !seq_lens || !workspace || !out || batch < 0 ||
+      num_slots < 1 || table_stride < 0 || !(sm_scale == sm_scale))
+    return PKV_ERR_INVALID_ARG;
+  if (batch > desc->max_batch) return PKV_ERR_CAPACITY;
+  if ((long long)batch * table_stride > INT32_MAX) return PKV_ERR_CAPACITY;
+  if (!slot_table && (long long)batch * table_stride > num_slots) return PKV_ERR_INVALID_ARG;
+  if (workspace_bytes < L.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (batch == 0) return PKV_OK;
+  DecodeArgs d{};
+  d.k = static_cast<uint16_t*>(const_cast<void*>(k_cache));  // read only: no append here
+  d.v = static_cast<uint16_t*>(const_cast<void*>(v_cache));
+  d.q = static_cast<const uint16_t*>(q);
+  d.kv_indptr = kv_indptr;
+  d.seq_lens = seq_lens;
+  d.hdr = at<int32_t>(workspace, L.hdr);
+  d.waves = at<WaveRange>(workspace, L.waves);
+  d.ginfo = at<GroupInfo>(workspace, L.ginfo);
+  d.counters = at<int32_t>(workspace, L.counters);
+  d.lse = at<float>(workspace, L.lse);
+  d.opart = at<float>(workspace, L.opart);
+  d.out = static_cast<uint16_t*>(out);
+  d.num_q_heads = desc->num_q_heads;
+  d.num_kv_heads = desc->num_kv_heads;
+  d.page_size = 16;
+  d.batch = batch;
+  const int hg = heads_per_group(desc->num_q_heads / desc->num_kv_heads);
+  d.units = desc->num_q_heads / hg;
+  d.log2_steps = 0;
+  d.scale_log2 = sm_scale * 1.4426950408889634f;
+  d.token_major = 1;
+  d.slot_table = slot_table;
+  d.table_stride = table_stride;
+  d.num_slots = num_slots;
+  return launch_status(
+      launch_decode(d, desc->head_dim, hg, L.groups, static_cast<hipStream_t>(stream)));
 }
 
 int pkv_prefill(const pkv_pool* pool, const pkv_desc* desc, const void* q,

@@ -73,7 +73,7 @@ struct EpiloguePtrs {
 
 // Kernel variants: plain decode, KV append fused into the decode, decode with
 // a per-token keep mask.
-enum Kind : int { kPlain = 0, kAppend = 1, kMasked = 2 };
+enum Kind : int { kPlain = 0, kAppend = 1, kMasked = 2, kTokens = 3 };
 
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -105,6 +105,7 @@ template <int D, int HG, int KIND>
 __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   constexpr bool APPEND = KIND == kAppend;
   constexpr bool MASKED = KIND == kMasked;
+  constexpr bool TOKENS = KIND == kTokens;  // token-major K/V, 16-token blocks as pages
   constexpr int kStages = 2;  // register ring: steps in flight per wave
   constexpr int kOut = (HG * D + kGroupThreads - 1) / kGroupThreads;  // outputs per thread
 
@@ -174,6 +175,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const uint32_t v_boff = (uint32_t)(r16 * P + 4 * g4) * 2;
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
+  const size_t slot_b = (size_t)a.num_kv_heads * D * 2;  // bytes of one token slot (TOKENS)
   // Fused KV append (k_new / v_new given): the step that holds token seq_len - 1
   // takes that token's K and V from k_new / v_new instead of the pool, and the
   // wave of the KV head's first head group writes them into the pool.
@@ -219,12 +221,29 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       if (p + len == n && lane < D / 2) vnew2 = reinterpret_cast<const uint32_t*>(vnew_row)[lane];
     }
 
-    for (int jb = 0; jb < len; jb += kWave) {
-      const int nb = min(kWave, len - jb);
-      // One vector load fetches the page ids of the next (up to) 64 pages: lane i
-      // holds the id of page p + jb + i, or -1 if it is unusable.
+    // Token-major K/V: blocks of 4 steps, lane i holding the slot of token
+    // 16 (p + jb) + i of the block (its K row for lane r16 = i, its V element
+    // for the lanes whose four tokens include it, both fetched by a lane
+    // shuffle), or -1 past the sequence or for an unusable slot.
+    constexpr int kBlock = TOKENS ? 4 : kWave;
+    for (int jb = 0; jb < len; jb += kBlock) {
+      const int nb = min(kBlock, len - jb);
       int vpage = -1;
-      {
+      if constexpr (TOKENS) {
+        const int tk = (p + jb) * 16 + lane;
+        if (lane < nb * 16 && tk < L) {
+          if (tk >= a.table_stride) {
+            err |= kErrBadIndexPos;
+          } else {
+            const int pos = b * a.table_stride + tk;  // below 2^31 (checked on the host)
+            const int slot = a.slot_table ? a.slot_table[pos] : pos;
+            if (slot < 0 || slot >= a.num_slots) err |= kErrBadPageId;
+            else vpage = slot;
+          }
+        }
+      } else {
+        // One vector load fetches the page ids of the next (up to) 64 pages:
+        // lane i holds the id of page p + jb + i, or -1 if it is unusable.
         const int pos = ip0 + p + jb + lane;
         const bool pos_ok = pos >= 0 && pos < a.num_indices;
         const int pid = pos_ok ? a.kv_indices[pos] : -1;
@@ -234,7 +253,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
           else vpage = pid;
         }
       }
-      const int ns = nb << log2_s;  // steps in this block, >= 1
+      const int ns = TOKENS ? nb : nb << log2_s;  // steps in this block, >= 1
 
       // Step j of the block: page id (uniform) and loads.  Steps past the block
       // re-read its last step (a cache hit) and are never consumed, so the
@@ -245,7 +264,42 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         const int tok = L - 1 - t0;
         return fuse_append && j < ns && tok >= 0 && tok < 16 ? tok : -1;
       };
+      auto issue_tokens = [&](int j, Step<D>& sd) {
+        const int jc = j < ns ? j : ns - 1;
+        const char* khead = kbase + (size_t)g * D * 2;
+        const char* vhead = vbase + (size_t)g * D * 2;
+        // K: lane (g4, r16) reads channels 8 (4kk + g4) .. +8 of token r16.
+        const int sk = __shfl(vpage, 16 * jc + r16, kWave);
+        const char* kq = khead + (size_t)(sk < 0 ? 0 : sk) * slot_b + g4 * 16;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) sd.k[kk] = *reinterpret_cast<const uint4*>(kq + kk * 64);
+        // V^T: channel 16 vb + r16 of tokens 4 g4 .. 4 g4 + 3, one element each;
+        // an unusable slot reads slot 0 and contributes zero (keep byte 0, V 0).
+        int sv[4];
+        uint32_t keep = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = __shfl(vpage, 16 * jc + 4 * g4 + i, kWave);
+          keep |= (sv[i] >= 0 ? 1u : 0u) << (8 * i);
+        }
+#pragma unroll
+        for (int vb = 0; vb < D / 16; ++vb) {
+          uint32_t e[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint16_t x = *reinterpret_cast<const uint16_t*>(
+                vhead + (size_t)(sv[i] < 0 ? 0 : sv[i]) * slot_b + (16 * vb + r16) * 2);
+            e[i] = sv[i] < 0 ? 0u : (uint32_t)x;
+          }
+          sd.v[vb] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        }
+        sd.keep = keep;
+      };
       auto issue = [&](int j, Step<D>& sd) {
+        if constexpr (TOKENS) {
+          issue_tokens(j, sd);
+          return;
+        }
         const int jc = j < ns ? j : ns - 1;
         const int pg = jc >> log2_s;
         const int sub = jc & ((1 << log2_s) - 1);
@@ -272,6 +326,11 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         }
       };
       auto consume = [&](int j, Step<D>& sd) {
+        if constexpr (TOKENS) {
+          const int t0 = (p + jb + j) * 16;
+          st.step(sd, min(16, max(0, L - t0)), g4, a.scale_log2, bias, sd.keep);
+          return;
+        }
         const int pg = j >> log2_s;
         const int sub = j & ((1 << log2_s) - 1);
         const int pid = __builtin_amdgcn_readlane(vpage, pg);
@@ -639,13 +698,17 @@ hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int hg, int groups, hipStream_t s) {
   if (groups <= 0) return hipSuccess;
-  const int kind = a.k_new != nullptr ? kAppend : (a.mask != nullptr ? kMasked : kPlain);
+  const int kind = a.token_major ? kTokens
+                   : a.k_new != nullptr ? kAppend
+                                        : (a.mask != nullptr ? kMasked : kPlain);
   if (head_dim == 128) {
+    if (kind == kTokens) return launch_d<128, kTokens>(a, hg, groups, s);
     if (kind == kAppend) return launch_d<128, kAppend>(a, hg, groups, s);
     if (kind == kMasked) return launch_d<128, kMasked>(a, hg, groups, s);
     return launch_d<128, kPlain>(a, hg, groups, s);
   }
   if (head_dim == 64) {
+    if (kind == kTokens) return launch_d<64, kTokens>(a, hg, groups, s);
     if (kind == kAppend) return launch_d<64, kAppend>(a, hg, groups, s);
     if (kind == kMasked) return launch_d<64, kMasked>(a, hg, groups, s);
     return launch_d<64, kPlain>(a, hg, groups, s);

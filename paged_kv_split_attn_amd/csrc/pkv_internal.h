@@ -117,6 +117,13 @@ struct DecodeArgs {
   int32_t units;        // head groups per request
   int32_t log2_steps;   // log2(page_size / 16): steps of 16 tokens per page
   float scale_log2;     // sm_scale * log2(e)
+  // Token-major K/V (k, v are [num_slots][Hkv][D]; the plan's pages are
+  // 16-token blocks): slot of token t of request b = slot_table[b * stride + t],
+  // or b * stride + t without a table.
+  int32_t token_major;
+  const int32_t* slot_table;
+  int32_t table_stride;
+  int32_t num_slots;
 };
 
 struct PrefillArgs {

@@ -25,7 +25,7 @@ def test_header_declares_expected_entry_points():
     assert set(names) == {
         "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
         "pkv_append_kv", "pkv_decode", "pkv_decode_append", "pkv_decode_masked",
-        "pkv_prefill", "pkv_debug_validate"}
+        "pkv_decode_tokens", "pkv_prefill", "pkv_debug_validate"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -124,6 +124,19 @@ def test_host_checks_reject_before_launch(lib):
                 fake, None) == 1
     assert _raw(lib, "pkv_prefill", B(pool), B(d), fake, fake, fake, fake, 10, fake, 17, 8, 1, 0.1,
                 fake, None) == 4
+    # token-major decode: page size other than 16, no slots, a contiguous layout
+    # larger than the caches, a table of 2^31 entries or more, a small workspace
+    d32 = _desc(page_size=32).c()
+    assert _raw(lib, "pkv_decode_tokens", B(d32), fake, fake, 100, fake, 8, fake, fake, fake, 4,
+                0.1, fake, ws_bytes, fake, None) == 1
+    assert _raw(lib, "pkv_decode_tokens", B(d), fake, fake, 0, fake, 8, fake, fake, fake, 4, 0.1,
+                fake, ws_bytes, fake, None) == 1
+    assert _raw(lib, "pkv_decode_tokens", B(d), fake, fake, 31, None, 8, fake, fake, fake, 4, 0.1,
+                fake, ws_bytes, fake, None) == 1
+    assert _raw(lib, "pkv_decode_tokens", B(d), fake, fake, 100, fake, 1 << 30, fake, fake, fake,
+                4, 0.1, fake, ws_bytes, fake, None) == 4
+    assert _raw(lib, "pkv_decode_tokens", B(d), fake, fake, 100, fake, 8, fake, fake, fake, 4, 0.1,
+                fake, 16, fake, None) == 3
     # NaN scale
     assert _raw(lib, "pkv_decode", B(pool), B(d), fake, fake, fake, 10, fake, 4, float("nan"),
                 fake, ws_bytes, fake, None) == 1
