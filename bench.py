@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--prefill", action="store_true",
                     help="also time pkv_prefill on a causal prefill batch (4 x 1024 new tokens, "
                          "no prefix, Hq=32, Hkv=8, D=128, P=16)")
+    ap.add_argument("--tokens", action="store_true",
+                    help="also time pkv_decode_tokens (token-major K/V): the ragged batch through "
+                         "a page-size-1 token table, and one contiguous 32k-token request")
     ap.add_argument("--no-kernel-loop", action="store_true",
                     help="time only whole steps (skip the decode-only loop)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -158,6 +161,45 @@ def bench_prefill(pkv, W, torch, dev, stream, K):
     return {"workload": pb.name, "us_per_call": round(ms * 1e3, 2), "flop": int(flop),
             "TFLOPs": round(tf, 1), "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
             "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_tokens(pkv, W, torch, dev, stream, K):
+    """Token-major decode at full size: the ragged batch stored token-major
+    (table mode) and one 32,768-token request in the contiguous layout.  K/V
+    copies rotate so that every call streams from HBM."""
+    cases = [W.tokens_from_pages(W.config(3, poison=False)),
+             W.make_tokens(name="contig_b1_32k", seed=4, B=1, Hq=32, Hkv=8, D=128,
+                           lengths=np.array([32768]), table=False, poison=False)]
+    res = []
+    for tb in cases:
+        t = W.tokens_to_device(tb, dev)
+        desc = pkv.Desc(max_batch=tb.B, num_q_heads=tb.Hq, num_kv_heads=tb.Hkv, head_dim=tb.D,
+                        page_size=16)
+        ws = torch.zeros(pkv.pkv_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        ip = torch.zeros(tb.B + 1, dtype=torch.int32, device=dev)
+        pkv.pkv_build_metadata(desc, t["seq_lens"], 0, ip, ws, stream)
+        out = torch.empty((tb.B, tb.Hq, tb.D), dtype=torch.int16, device=dev)
+        cache_bytes = 2 * t["k_cache"].numel() * 2
+        n = max(1, -(-(768 << 20) // cache_bytes))
+        caches = [(t["k_cache"], t["v_cache"])]
+        caches += [(t["k_cache"].clone(), t["v_cache"].clone()) for _ in range(n - 1)]
+
+        def call(i):
+            k, v = caches[i % n]
+            pkv.pkv_decode_tokens(desc, k, v, t["slot_table"], tb.stride, t["q"], ip,
+                                  t["seq_lens"], tb.sm_scale, ws, out, stream)
+        for i in range(3):
+            call(i)
+        ms = timed(stream, K, call)
+        tokens = int(tb.seq_lens.astype(np.int64).sum())
+        byts = (tokens * tb.Hkv * tb.D * 2 * 2 + 2 * tb.B * tb.Hq * tb.D * 2 + 4 * tb.B
+                + (4 * tokens if tb.slot_table is not None else 0))
+        gbps = byts / (ms * 1e-3) / 1e9
+        res.append({"workload": tb.name, "layout": "table" if tb.slot_table is not None
+                    else "contiguous", "kv_tokens": tokens, "us_per_call": round(ms * 1e3, 2),
+                    "bytes": int(byts), "GBps": round(gbps, 1),
+                    "frac": round(gbps / PEAK_HBM_GBPS, 4), "copies": n})
+    return res
 
 
 def timed(stream, K, fn):
@@ -309,6 +351,8 @@ def main():
         })
     if args.prefill:
         res["prefill"] = bench_prefill(pkv, W, torch, dev, stream, K)
+    if args.tokens:
+        res["tokens"] = bench_tokens(pkv, W, torch, dev, stream, K)
     if args.mask_keep is not None:
         S = -(-int(batch.seq_lens.max()) // 4) * 4
         rng = np.random.default_rng(np.random.PCG64(2000 + args.config))
