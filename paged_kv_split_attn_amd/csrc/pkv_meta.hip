@@ -9,6 +9,8 @@
 // compute_num_splits bullets); here every wave gets the same number of pages
 // whatever the length mix, and the plan is computed on the device, so the host
 // never reads seq_lens.
+#include <algorithm>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -47,26 +49,60 @@ __device__ int block_inclusive_scan(int x, int* smem, int* total) {
 
 __device__ __forceinline__ int pages_of(int len, int P) { return len > 0 ? (len + P - 1) / P : 0; }
 
+// Integer arithmetic of the plan, in I = uint32_t when the step has fewer than
+// 2^31 tiles (every division a 32-bit one) and uint64_t otherwise.  All
+// results are the exact floors the plan defines, whatever I is.
+template <typename I>
+struct PlanMath {
+  I T;         // tiles
+  uint32_t W;  // workgroups, 1 <= W <= min(T, 65536)
+  I q, r;      // T = q W + r
+  __device__ PlanMath(I tiles, uint32_t groups) : T(tiles), W(groups), q(tiles / groups),
+                                                  r(tiles % groups) {}
+  // First tile of workgroup i (i <= W): floor(i T / W) = i q + floor(i r / W),
+  // where i r <= 65536 * 65535 fits 32 bits.
+  __device__ I start(uint32_t i) const { return (I)i * q + (I)(i * (uint32_t)r / W); }
+  // floor(w len / 8) without forming w len.
+  __device__ static I part(I len, int w) {
+    return (I)w * (len >> 3) + (I)(((uint32_t)w * (uint32_t)(len & 7)) >> 3);
+  }
+  // Workgroup that owns tile t: floor(((t + 1) W - 1) / T), the largest i with
+  // start(i) <= t.  In 32-bit plans the dividend is below 2^47, so a double
+  // division is within one of the floor, and one integer check fixes it.
+  __device__ uint32_t owner(I t) const {
+    const uint64_t num = ((uint64_t)t + 1) * W - 1;
+    if constexpr (sizeof(I) == 4) {
+      uint64_t q = (uint64_t)((double)num / (double)T);
+      if (q * T > num) --q;
+      else if ((q + 1) * T <= num) ++q;
+      return (uint32_t)q;
+    } else {
+      return (uint32_t)(num / T);
+    }
+  }
+};
+
 struct Locator {
   const int32_t* ip;  // page prefix sums (LDS copy or global)
-  const int32_t* seq_lens;
+  const int32_t* seq_lens;  // (LDS copy or global)
   int batch, units;
   // (request, head group, page) of tile t < T: the request is the largest b
   // with ip[b] * U <= t (requests without pages have empty ranges).
-  __device__ WaveRange at(long long t, int count) const {
+  template <typename I>
+  __device__ WaveRange at(I t, int count) const {
     int lo = 0, hi = batch;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if ((long long)ip[mid] * units <= t) lo = mid;
+      if ((I)ip[mid] * (I)units <= t) lo = mid;
       else hi = mid - 1;
     }
     const int n = ip[lo + 1] - ip[lo];
-    const long long r = t - (long long)ip[lo] * units;
-    const int u = (int)(r / n);
+    const I rr = t - (I)ip[lo] * (I)units;
+    const int u = (int)(rr / (I)n);
     WaveRange w;
     w.b = lo;
     w.u = u;
-    w.p = (int)(r - (long long)u * n);
+    w.p = (int)(rr - (I)u * (I)n);
     w.count = count;
     w.ip0 = ip[lo];
     w.pages = n;
@@ -76,19 +112,76 @@ struct Locator {
   }
 };
 
+// Phases 2 and 3 of the metadata kernel (see there), in integer type I.  The
+// work items -- one per wave of the grid, then two per workgroup record -- are
+// dealt to the threads of all metadata workgroups.
+template <typename I>
+__device__ void build_plan(const MetaArgs& a, const Locator& loc, I T, int W) {
+  const int U = a.units;
+  const PlanMath<I> pm(T, (uint32_t)max(W, 1));
+  const int nw = a.groups * kWavesPerGroup;
+  for (int x = blockIdx.x * kMetaThreads + threadIdx.x; x < nw + 2 * a.groups;
+       x += gridDim.x * kMetaThreads) {
+    if (x < nw) {
+      // Phase 2: the range of wave w of group i.  Group i covers
+      // [start(i), start(i + 1)); its wave w the w-th of kWavesPerGroup equal
+      // parts.
+      const int i = x / kWavesPerGroup;
+      const int w = x - i * kWavesPerGroup;
+      WaveRange r{0, 0, 0, 0, 0, 0, 0, 0};
+      if (i < W) {
+        const I g0 = pm.start(i), len = pm.start(i + 1) - g0;
+        const I t0 = g0 + PlanMath<I>::part(len, w);
+        const I t1 = g0 + PlanMath<I>::part(len, w + 1);
+        if (t1 > t0) r = loc.at(t0, (int)(t1 - t0));
+      }
+      a.waves[x] = r;
+    } else {
+      // Phase 3: half k of the merge record of group i (two threads per
+      // group): its first (k = 0) or last (k = 1) segment (b * U + u), and the
+      // workgroups that segment's tiles span.  A segment is the first segment
+      // of a workgroup exactly when that workgroup's range starts inside it.
+      const int i = (x - nw) >> 1, k = (x - nw) & 1;
+      int seg = -1, lo = 0, hi = -1, slot = 0;
+      const I g0 = i < W ? pm.start(i) : 0;
+      const I g1 = i < W ? pm.start(i + 1) : 0;
+      if (g1 > g0) {
+        const WaveRange e = loc.at(k == 0 ? g0 : g1 - 1, 0);
+        const I t0 = (I)e.ip0 * (I)U + (I)e.u * (I)e.pages;
+        const I t1 = t0 + (I)(e.pages - 1);
+        const uint32_t l = pm.owner(t0);
+        seg = e.b * U + e.u;
+        lo = (int)l;
+        hi = (int)pm.owner(t1);
+        slot = pm.start(l) >= t0 ? 0 : 1;
+      }
+      GroupInfo& gi = a.ginfo[i];
+      gi.seg[k] = seg;
+      gi.lo[k] = lo;
+      gi.hi[k] = hi;
+      gi.slot_lo[k] = slot;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
   __shared__ int smem[kMetaWaves];
   __shared__ int s_err;
   __shared__ int s_empty;
   __shared__ int32_t s_ip[kMetaLdsRequests + 1];
+  __shared__ int32_t s_len[kMetaLdsRequests];
   const int tid = threadIdx.x;
   const bool in_lds = a.batch <= kMetaLdsRequests;
   int err = 0;
+  // Every workgroup builds the prefix sums for its own searches; workgroup 0
+  // also writes kv_indptr, the counters and the header.  (With more requests
+  // than LDS holds the launch has one workgroup, which searches kv_indptr.)
+  const bool lead = blockIdx.x == 0;
   if (tid == 0) {
     s_err = 0;
     s_empty = 0;
     s_ip[0] = 0;
-    a.kv_indptr[0] = 0;
+    if (lead) a.kv_indptr[0] = 0;
   }
 
   // Phase 1: kv_indptr = exclusive prefix sum of page counts.
@@ -98,6 +191,7 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
     int n = 0;
     if (b < a.batch) {
       const int L = a.seq_lens[b];
+      if (in_lds) s_len[b] = L;
       if (L < 0) err |= kErrNegativeLength;
       n = pages_of(L, a.page_size);
       empty += n == 0;
@@ -105,7 +199,7 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
     int total;
     const int incl = block_inclusive_scan(n, smem, &total);
     if (b < a.batch) {
-      a.kv_indptr[b + 1] = carry + incl;
+      if (lead) a.kv_indptr[b + 1] = carry + incl;
       if (in_lds) s_ip[b + 1] = carry + incl;
     }
     carry += total;
@@ -124,49 +218,20 @@ __global__ void __launch_bounds__(kMetaThreads) metadata_kernel(MetaArgs a) {
       W = (int)(want < a.groups ? want : a.groups);
     }
   }
-  Locator loc{in_lds ? s_ip : a.kv_indptr, a.seq_lens, a.batch, U};
-
-  // Phase 2: every wave's range.  Group i covers [i*T/W, (i+1)*T/W); its wave
-  // w covers the w-th of kWavesPerGroup equal parts.
-  for (int gw = tid; gw < a.groups * kWavesPerGroup; gw += kMetaThreads) {
-    const int i = gw / kWavesPerGroup;
-    const int w = gw - i * kWavesPerGroup;
-    WaveRange r{0, 0, 0, 0, 0, 0, 0, 0};
-    if (i < W) {
-      const long long g0 = (long long)i * T / W, g1 = (long long)(i + 1) * T / W;
-      const long long len = g1 - g0;
-      const long long t0 = g0 + (long long)w * len / kWavesPerGroup;
-      const long long t1 = g0 + (long long)(w + 1) * len / kWavesPerGroup;
-      if (t1 > t0) r = loc.at(t0, (int)(t1 - t0));
-    }
-    a.waves[gw] = r;
+  // The searches read the prefix sums from LDS when they fit there (a
+  // separate instantiation, so that they compile to LDS loads).
+  const bool small = T < 0x80000000LL;
+  if (in_lds) {
+    const Locator loc{s_ip, s_len, a.batch, U};
+    if (small) build_plan<uint32_t>(a, loc, (uint32_t)T, W);
+    else build_plan<uint64_t>(a, loc, (uint64_t)T, W);
+  } else {
+    const Locator loc{a.kv_indptr, a.seq_lens, a.batch, U};
+    if (small) build_plan<uint32_t>(a, loc, (uint32_t)T, W);
+    else build_plan<uint64_t>(a, loc, (uint64_t)T, W);
   }
 
-  // Phase 3: the merge record of every workgroup.  Its first and last segment
-  // (b * U + u), and for each the workgroups its tiles span: tile t belongs to
-  // workgroup floor(((t + 1) * W - 1) / T).  A segment is the first segment of
-  // a workgroup exactly when that workgroup's range starts inside it.
-  for (int i = tid; i < a.groups; i += kMetaThreads) {
-    GroupInfo gi{{-1, -1}, {0, 0}, {-1, -1}, {0, 0}};
-    const long long g0 = i < W ? (long long)i * T / W : 0;
-    const long long g1 = i < W ? (long long)(i + 1) * T / W : 0;
-    if (g1 > g0) {
-      const WaveRange ends[2] = {loc.at(g0, 0), loc.at(g1 - 1, 0)};
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const WaveRange& e = ends[k];
-        const long long t0 = (long long)e.ip0 * U + (long long)e.u * e.pages;
-        const long long t1 = t0 + e.pages - 1;
-        const int lo = (int)(((t0 + 1) * W - 1) / T);
-        gi.seg[k] = e.b * U + e.u;
-        gi.lo[k] = lo;
-        gi.hi[k] = (int)(((t1 + 1) * W - 1) / T);
-        gi.slot_lo[k] = (long long)lo * T / W >= t0 ? 0 : 1;
-      }
-    }
-    a.ginfo[i] = gi;
-  }
-
+  if (!lead) return;
   // Phase 4: arrival counters of the cross-workgroup merge.
   for (int sgi = tid; sgi < a.batch * U; sgi += kMetaThreads) a.counters[sgi] = 0;
 
@@ -228,7 +293,13 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
 }  // namespace
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(kMetaThreads), 0, s, a);
+  // Plan items (one per wave of the decode grid, two per workgroup record)
+  // spread over several workgroups when the prefix sums fit in LDS.
+  const long long items = (long long)a.groups * (kWavesPerGroup + 2);
+  const int parts = a.batch <= kMetaLdsRequests
+                        ? (int)std::max(1LL, (items + kMetaThreads - 1) / kMetaThreads)
+                        : 1;
+  hipLaunchKernelGGL(metadata_kernel, dim3(parts), dim3(kMetaThreads), 0, s, a);
   return hipGetLastError();
 }
 
