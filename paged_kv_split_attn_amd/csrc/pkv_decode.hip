@@ -39,6 +39,11 @@
 // branch (wave-uniform) is rarely taken.  Scores are kept in the log2 domain
 // (sm_scale * log2 e folded into one multiply-add) so every exponential is a
 // single v_exp_f32.
+//
+// Variants (template KIND): the plain decode; the KV append fused into the
+// decode; a per-token keep mask; and token-major K/V ([slot][Hkv][D] rows, the
+// contiguous layout or a page-size-1 token table), where the plan's pages are
+// 16-token blocks and V^T operands are gathered element by element.
 
 #include "pkv_mfma.h"
 
@@ -72,7 +77,7 @@ struct EpiloguePtrs {
 
 
 // Kernel variants: plain decode, KV append fused into the decode, decode with
-// a per-token keep mask.
+// a per-token keep mask, decode over token-major K/V.
 enum Kind : int { kPlain = 0, kAppend = 1, kMasked = 2, kTokens = 3 };
 
 

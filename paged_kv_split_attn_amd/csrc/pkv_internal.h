@@ -14,6 +14,7 @@ constexpr int kWave = 64;
 constexpr int kWavesPerGroup = PKV_WAVES_PER_WORKGROUP;  // waves of one decode workgroup (two per SIMD)
 constexpr int kGroupThreads = kWavesPerGroup * kWave;  // 512
 constexpr int kXcds = 8;  // accelerator dies of the chip, each with its own L2
+constexpr int kPrefillTiles = 1;  // 16-row tiles per prefill wave (2 measured slower: fewer, longer workgroups)
 constexpr int kDefaultMinTiles = 8;
 constexpr int kMaxBatch = 65536;
 constexpr int kMaxGroups = 65536;

@@ -19,63 +19,74 @@
 namespace pkv {
 namespace {
 
-// One wave's online softmax over 16 score rows, 32 keys per step.  Scores of
-// the step's two 16-key halves come from v_mfma_f32_16x16x32_bf16 as in the
-// decode step (K rows the A operand, q^T the B operand), leaving lane (g, r)
-// row r's scores of keys 4g .. 4g+3 of each half.  P . V then takes one
-// v_mfma_f32_16x16x32_bf16 per 16 channels and part of P, whose reduction
-// index runs over the eight keys lane group g holds (4g .. 4g+3 of half 0,
-// then of half 1): the weights never move between lanes, and the
-// double-rate instruction does twice the work of the 16-key one in the same
-// time.  P enters as bf16 hi + lo parts.  Output: lane (g, r) register i of
-// block vb holds O[row 4g+i][channel 16 vb + r].
 // Bits 4h + j (h, j < 2, 4) of the keys 16h + j <= d of a lane group's eight.
 __device__ __forceinline__ uint32_t keys_upto(int d) {
   auto four = [](int x) { return x < 0 ? 0u : x >= 3 ? 15u : (2u << x) - 1u; };
   return four(d) | (four(d - 16) << 4);
 }
 
-template <int D>
+// One wave's online softmax over NT tiles of 16 score rows, 32 keys per step;
+// the tiles share every K and V operand the wave reads.  Scores of the
+// step's two 16-key halves come from v_mfma_f32_16x16x32_bf16 as in the decode
+// step (K rows the A operand, q^T the B operand), leaving lane (g, r) row r's
+// scores of keys 4g .. 4g+3 of each half.  P . V then takes one
+// v_mfma_f32_16x16x32_bf16 per tile, 16 channels and part of P, whose
+// reduction index runs over the eight keys lane group g holds (4g .. 4g+3 of
+// half 0, then of half 1): the weights never move between lanes, and the
+// double-rate instruction does twice the work of the 16-key one in the same
+// time.  P enters as bf16 hi + lo parts.  Output: lane (g, r) register i of
+// block vb of tile t holds O[row 4g+i of t][channel 16 vb + r].
+template <int D, int NT>
 struct Wave32 {
-  static constexpr int KB = D / 32;  // q.K MFMAs per half
+  static constexpr int KB = D / 32;  // q.K MFMAs per half and tile
   static constexpr int VB = D / 16;  // p.V channel blocks
-  floatx4_t o[VB];
-  bf16x8_t qb[KB];  // q^T operand (zero for unused rows)
-  float m, l;       // row r: running max (log2 domain), partial sum
+  floatx4_t o[NT][VB];
+  bf16x8_t qb[NT][KB];  // q^T operands (zero for unused rows)
+  float m[NT], l[NT];   // row r of tile t: running max (log2 domain), partial sum
 
   __device__ __forceinline__ void init() {
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb) o[vb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    m = kFloorMax;
-    l = 0.f;
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) o[t][vb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      m[t] = kFloorMax;
+      l[t] = 0.f;
+    }
   }
 
   // k[h][kk]: K of token r of half h, channels 8 (4kk + g) .. +8.
   // load_v(vv) fills vv[vb] with channel 16 vb + r, keys 4g .. 4g+3 of half 0
   // then of half 1; it runs once the scores are issued, so that K and V
-  // operands are not live at the same time.  keep: bit 4h + j set when key
-  // 16h + 4g + j counts for this lane's row.  vlive: keys from this one on
-  // hold no data (their V is zeroed); 32 when all do.
+  // operands are not live at the same time.  keep[t]: bit 4h + j set when key
+  // 16h + 4g + j counts for this lane's row of tile t.  vlive: keys from this
+  // one on hold no data (their V is zeroed); 32 when all do.
   template <class LoadV>
-  __device__ __forceinline__ void step(const uint4 (&k)[2][KB], LoadV&& load_v, uint32_t keep,
-                                       int vlive, int g, float scale_log2, float bias) {
-    floatx4_t sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ void step(const uint4 (&k)[2][KB], LoadV&& load_v,
+                                       const uint32_t (&keep)[NT], int vlive, int g,
+                                       float scale_log2, const float (&bias)[NT]) {
+    floatx4_t sc[NT][2];
 #pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[0][kk]), qb[kk],
-                                                    sc0, 0, 0, 0);
-      sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[1][kk]), qb[kk],
-                                                    sc1, 0, 0, 0);
+    for (int t = 0; t < NT; ++t) sc[t][0] = sc[t][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          sc[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, k[h][kk]), qb[t][kk], sc[t][h], 0, 0, 0);
+    float s[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[t][i] = fmaf(sc[t][0][i], scale_log2, bias[t]);
+        s[t][4 + i] = fmaf(sc[t][1][i], scale_log2, bias[t]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (((keep[t] >> i) & 1u) == 0) s[t][i] = kMinusInf;
     }
-    float s[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = fmaf(sc0[i], scale_log2, bias);
-      s[4 + i] = fmaf(sc1[i], scale_log2, bias);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (((keep >> i) & 1u) == 0) s[i] = kMinusInf;
     __builtin_amdgcn_sched_barrier(0);
     uint4 vv[VB];
     load_v(vv);
@@ -95,37 +106,43 @@ struct Wave32 {
         vv[vb].w &= msk[3];
       }
     }
-    float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    pm = max_over_groups(fmaxf(pm, fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
-    if (__builtin_amdgcn_ballot_w64(pm > m + kRescaleSlack) != 0) {
-      const float mn = fmaxf(m, pm);
-      const float alpha = fast_exp2(m - mn);
-      l *= alpha;
-      m = mn;
-      // Register i of lane group g holds row 4g + i, whose factor lane 4g + i has.
+    bf16x8_t phi[NT], plo[NT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * g + i, kWave);
+    for (int t = 0; t < NT; ++t) {
+      float pm = fmaxf(fmaxf(s[t][0], s[t][1]), fmaxf(s[t][2], s[t][3]));
+      pm = max_over_groups(fmaxf(pm, fmaxf(fmaxf(s[t][4], s[t][5]), fmaxf(s[t][6], s[t][7]))));
+      if (__builtin_amdgcn_ballot_w64(pm > m[t] + kRescaleSlack) != 0) {
+        const float mn = fmaxf(m[t], pm);
+        const float alpha = fast_exp2(m[t] - mn);
+        l[t] *= alpha;
+        m[t] = mn;
+        // Register i of lane group g holds row 4g + i, whose factor lane 4g + i has.
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb) o[vb][i] *= ai;
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb) o[t][vb][i] *= ai;
+        }
       }
-    }
-    float p[8];
+      float p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[i] - m);
-    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    bf16x8_t phi, plo;
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[t][i] - m[t]);
+      l[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = (__bf16)p[i];
-      phi[i] = h;
-      plo[i] = (__bf16)(p[i] - (float)h);
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)p[i];
+        phi[t][i] = h;
+        plo[t][i] = (__bf16)(p[i] - (float)h);
+      }
     }
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) {
       const bf16x8_t vt = __builtin_bit_cast(bf16x8_t, vv[vb]);
-      o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vt, o[vb], 0, 0, 0);
-      o[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vt, o[vb], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        o[t][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[t], vt, o[t][vb], 0, 0, 0);
+        o[t][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[t], vt, o[t][vb], 0, 0, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);  // the next step's K loads start after this one's V
   }
@@ -133,8 +150,9 @@ struct Wave32 {
 
 template <int D, int HG>
 __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
-  constexpr int QT = 16 / HG;     // query tokens per wave block
-  constexpr int ROWS = QT * HG;   // score rows in use (15 for HG = 3)
+  constexpr int QT = 16 / HG;     // query tokens per row tile
+  constexpr int ROWS = QT * HG;   // score rows in use per tile (15 for HG = 3)
+  constexpr int NT = kPrefillTiles;  // row tiles per wave
   constexpr int kSteps = 2;       // 32-key steps per LDS chunk
   constexpr int kHalves = 2 * kSteps;  // 16-key pieces per chunk (one page each at P = 16)
   constexpr int kPieces = D * 16 * 2 / 16;  // 16-byte pieces of 16 keys' K (same for V)
@@ -178,8 +196,8 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
     u = (int)((t / gx) % gy);
     b = (int)(t / (gx * gy));
   }
-  const int wg_tok0 = bx * kWavesPerGroup * QT;  // first query token of the workgroup
-  const int tok0 = wg_tok0 + w * QT;              // first query token of this wave
+  const int wg_tok0 = bx * kWavesPerGroup * NT * QT;  // first query token of the workgroup
+  const int tok0 = wg_tok0 + w * NT * QT;              // first query token of this wave
   const int q0 = a.qo_indptr[b];
   const int n = a.qo_indptr[b + 1] - q0;
   if (wg_tok0 >= n) return;  // uniform over the workgroup
@@ -193,29 +211,39 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
 
   const int g4 = lane >> 4;
   const int r16 = lane & 15;
-  // Row r16 = (token tok0 + r16 / HG, head r16 % HG).
-  const int rt = tok0 + r16 / HG;
-  const bool rvalid = r16 < ROWS && rt < n;
-  const int lim = a.causal ? L - n + rt : L - 1;  // last key row r16 sees
-  const float bias = rvalid ? 0.f : kMinusInf;
+  // Row r16 of tile t = (token tok0 + t QT + r16 / HG, head r16 % HG).
+  int rt[NT], lim[NT];
+  bool rvalid[NT];
+  float bias[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    rt[t] = tok0 + t * QT + r16 / HG;
+    rvalid[t] = r16 < ROWS && rt[t] < n;
+    lim[t] = a.causal ? L - n + rt[t] : L - 1;  // last key the row sees
+    bias[t] = rvalid[t] ? 0.f : kMinusInf;
+  }
   // Keys this wave reads, and keys the workgroup reads (its last wave's limit).
   auto block_end = [&](int t0) {
-    const int last = min(t0 + QT, n) - 1;
+    const int last = min(t0 + NT * QT, n) - 1;
     return a.causal ? max(0, min(L, L - n + last + 1)) : L;
   };
   const int kv_end = active ? block_end(tok0) : 0;
-  const int wg_end = block_end(min(wg_tok0 + (kWavesPerGroup - 1) * QT, n - 1));
+  const int wg_end = block_end(min(wg_tok0 + (kWavesPerGroup - 1) * NT * QT, n - 1));
 
-  Wave32<D> st;
+  Wave32<D, NT> st;
   st.init();
   {
-    // q^T operand: lane (g4, r16) supplies row r16, channels 8*(4kk + g4) .. +8.
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        a.q + ((size_t)(q0 + (rvalid ? rt : 0)) * Hq + hq0 + r16 % HG) * D + g4 * 8);
+    // q^T operands: lane (g4, r16) supplies row r16 of each tile, channels
+    // 8*(4kk + g4) .. +8.
 #pragma unroll
-    for (int kk = 0; kk < Wave32<D>::KB; ++kk) {
-      const uint4 w4 = rvalid ? qp[4 * kk] : make_uint4(0, 0, 0, 0);
-      st.qb[kk] = __builtin_bit_cast(bf16x8_t, w4);
+    for (int t = 0; t < NT; ++t) {
+      const uint4* qp = reinterpret_cast<const uint4*>(
+          a.q + ((size_t)(q0 + (rvalid[t] ? rt[t] : 0)) * Hq + hq0 + r16 % HG) * D + g4 * 8);
+#pragma unroll
+      for (int kk = 0; kk < Wave32<D, NT>::KB; ++kk) {
+        const uint4 w4 = rvalid[t] ? qp[4 * kk] : make_uint4(0, 0, 0, 0);
+        st.qb[t][kk] = __builtin_bit_cast(bf16x8_t, w4);
+      }
     }
     // Wait for q here: left to the first matrix-core step, the wait would sit
     // inside the KV loop and drain the next chunk's loads with it every step.
@@ -315,23 +343,26 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
     for (int s = 0; s < kSteps; ++s) {
       const int t0 = (c * kSteps + s) * 32;
       if (t0 < kv_end) {  // uniform per wave
-        uint4 kop[2][Wave32<D>::KB];
+        uint4 kop[2][Wave32<D, NT>::KB];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int kk = 0; kk < Wave32<D>::KB; ++kk)
+          for (int kk = 0; kk < Wave32<D, NT>::KB; ++kk)
             kop[h][kk] = *reinterpret_cast<const uint4*>(k_at(buf, 2 * s + h, 4 * kk + g4, r16));
-        auto load_v = [&](uint4 (&vv)[Wave32<D>::VB]) {
+        auto load_v = [&](uint4 (&vv)[Wave32<D, NT>::VB]) {
 #pragma unroll
-          for (int vb = 0; vb < Wave32<D>::VB; ++vb)
+          for (int vb = 0; vb < Wave32<D, NT>::VB; ++vb)
             vv[vb] = *reinterpret_cast<const uint4*>(v_at(buf, s, 16 * vb + r16, g4, 0));
         };
         const int vlive = min(32, kv_end - t0);
-        // Key t0 + 16h + 4 g4 + j counts when it is at most min(lim, kv_end - 1)
-        // and its page exists.
-        uint32_t keep = keys_upto(min(lim, kv_end - 1) - t0 - 4 * g4);
-        if (live_pids[2 * s] < 0) keep &= 0xf0u;
-        if (live_pids[2 * s + 1] < 0) keep &= 0x0fu;
+        // Key t0 + 16h + 4 g4 + j counts for a row when it is at most
+        // min(lim, kv_end - 1) and its page exists.
+        const uint32_t pages_ok = (live_pids[2 * s] < 0 ? 0u : 0x0fu) |
+                                  (live_pids[2 * s + 1] < 0 ? 0u : 0xf0u);
+        uint32_t keep[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          keep[t] = keys_upto(min(lim[t], kv_end - 1) - t0 - 4 * g4) & pages_ok;
         st.step(kop, load_v, keep, vlive, g4, a.scale_log2, bias);
       }
     }
@@ -344,32 +375,38 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   // are free for the output rows.
   if (!active) return;
 
-  // Normalise: the four lanes of row r hold its partial sums; register i of
-  // lane group g holds row 4g + i.  Rows go through LDS so that every lane
-  // writes 8 channels (16 bytes) of one row.
-  const float lt = sum_over_groups(st.l);
+  // Normalise, one tile at a time: the four lanes of row r hold its partial
+  // sums; register i of lane group g holds row 4g + i.  Rows go through LDS
+  // so that every lane writes 8 channels (16 bytes) of one row.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float li = __shfl(lt, 4 * g4 + i, kWave);
-    const float inv = li > 0.f ? 1.0f / li : 0.f;
+  for (int t = 0; t < NT; ++t) {
+    const float lt = sum_over_groups(st.l[t]);
 #pragma unroll
-    for (int vb = 0; vb < Wave32<D>::VB; ++vb)
-      s_out[(w * 16 + 4 * g4 + i) * D + 16 * vb + r16] = st.o[vb][i] * inv;
-  }
-  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes land first
-  constexpr int kChunks = ROWS * (D / 8);
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(lt, 4 * g4 + i, kWave);
+      const float inv = li > 0.f ? 1.0f / li : 0.f;
 #pragma unroll
-  for (int c = lane; c < kChunks; c += kWave) {
-    const int rr = c / (D / 8);
-    const int c8 = (c - rr * (D / 8)) * 8;
-    const int tok = tok0 + rr / HG;
-    if (tok < n) {
-      const float4 x0 = *reinterpret_cast<const float4*>(&s_out[(w * 16 + rr) * D + c8]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&s_out[(w * 16 + rr) * D + c8 + 4]);
-      *reinterpret_cast<uint4*>(a.out + ((size_t)(q0 + tok) * Hq + hq0 + rr % HG) * D + c8) =
-          make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
-                     pack_bf16x2(x1.z, x1.w));
+      for (int vb = 0; vb < Wave32<D, NT>::VB; ++vb)
+        s_out[(w * 16 + 4 * g4 + i) * D + 16 * vb + r16] = st.o[t][vb][i] * inv;
     }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes land first
+    constexpr int kChunks = ROWS * (D / 8);
+    const int tt0 = tok0 + t * QT;  // first token of the tile
+#pragma unroll
+    for (int c = lane; c < kChunks; c += kWave) {
+      const int rr = c / (D / 8);
+      const int c8 = (c - rr * (D / 8)) * 8;
+      const int tok = tt0 + rr / HG;
+      if (tok < n) {
+        const float4 x0 = *reinterpret_cast<const float4*>(&s_out[(w * 16 + rr) * D + c8]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&s_out[(w * 16 + rr) * D + c8 + 4]);
+        *reinterpret_cast<uint4*>(a.out + ((size_t)(q0 + tok) * Hq + hq0 + rr % HG) * D + c8) =
+            make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
+                       pack_bf16x2(x1.z, x1.w));
+      }
+    }
+    // The next tile's rows reuse the wave's LDS rows: the reads above come
+    // first (LDS operations of a wave complete in order).
   }
 }
 
@@ -391,7 +428,7 @@ hipError_t launch_p(const PrefillArgs& a, int hg, dim3 grid, hipStream_t s) {
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int hg, int max_q_len,
                           hipStream_t s) {
   const int qt = 16 / hg;
-  const int per_group = qt * kWavesPerGroup;  // query tokens one workgroup covers
+  const int per_group = qt * kPrefillTiles * kWavesPerGroup;  // query tokens one workgroup covers
   const dim3 grid((max_q_len + per_group - 1) / per_group, a.num_q_heads / hg, a.batch);
   if (grid.x == 0 || grid.z == 0) return hipSuccess;
   if ((long long)grid.x * grid.y * grid.z > INT32_MAX) return hipErrorInvalidConfiguration;
