@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--tokens", action="store_true",
                     help="also time pkv_decode_tokens (token-major K/V): the ragged batch through "
                          "a page-size-1 token table, and one contiguous 32k-token request")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time a plain read-only launch over the decode call's byte count "
+                         "(the achievable read rate of one launch of that size)")
     ap.add_argument("--no-kernel-loop", action="store_true",
                     help="time only whole steps (skip the decode-only loop)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -200,6 +203,25 @@ def bench_tokens(pkv, W, torch, dev, stream, K):
                     "bytes": int(byts), "GBps": round(gbps, 1),
                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "copies": n})
     return res
+
+
+def bench_ceiling(pkv, torch, dev, stream, K, nbytes):
+    """pkv_debug_read_ceiling over nbytes, rotating copies so that every call
+    reads from HBM."""
+    n = max(16, nbytes // 16 * 16)
+    copies = max(3, -(-(768 << 20) // n))
+    bufs = [torch.full((n,), i + 1, dtype=torch.uint8, device=dev) for i in range(copies)]
+    sink = torch.empty(pkv.READ_CEILING_GROUPS * 64 * pkv.WAVES_PER_GROUP, dtype=torch.int32,
+                       device=dev)
+
+    def call(i):
+        pkv.pkv_debug_read_ceiling(bufs[i % copies], sink, stream)
+    for i in range(3):
+        call(i)
+    ms = timed(stream, K, call)
+    gbps = n / (ms * 1e-3) / 1e9
+    return {"bytes": n, "us_per_call": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+            "frac": round(gbps / PEAK_HBM_GBPS, 4), "copies": copies}
 
 
 def timed(stream, K, fn):
@@ -353,6 +375,8 @@ def main():
         res["prefill"] = bench_prefill(pkv, W, torch, dev, stream, K)
     if args.tokens:
         res["tokens"] = bench_tokens(pkv, W, torch, dev, stream, K)
+    if args.ceiling:
+        res["read_ceiling"] = bench_ceiling(pkv, torch, dev, stream, K, call_bytes)
     if args.mask_keep is not None:
         S = -(-int(batch.seq_lens.max()) // 4) * 4
         rng = np.random.default_rng(np.random.PCG64(2000 + args.config))

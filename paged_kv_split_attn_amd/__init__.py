@@ -39,6 +39,7 @@ __all__ = [
     "pkv_decode_tokens",
     "pkv_prefill",
     "pkv_debug_validate",
+    "pkv_debug_read_ceiling",
     "WAVES_PER_GROUP",
     "PKV_OK",
     "PKV_ERR_INVALID_ARG",
@@ -120,6 +121,7 @@ _SIGNATURES = {
                                          _vp, _vp]),
     "pkv_prefill": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp, _vp,
                                    _vp, _i32, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp]),
+    "pkv_debug_read_ceiling": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _vp]),
     "pkv_debug_validate": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _vp, _vp, _i32, _i32, _i32,
                                           _vp, ctypes.c_size_t, _i32p, _i32p, _vp]),
 }
@@ -375,3 +377,17 @@ def pkv_debug_validate(desc: Desc, seq_lens: torch.Tensor, kv_indptr: torch.Tens
         _check("pkv_debug_validate", st)
     w = [tuple(waves[4 * i: 4 * i + 4]) for i in range(nw)]
     return {"status": st, "groups": groups.value, "waves": w}
+
+
+READ_CEILING_GROUPS = _header_define("PKV_READ_CEILING_GROUPS")
+
+
+def pkv_debug_read_ceiling(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """One read-only launch over src (a diagnostic of the achievable read rate);
+    sink is uint32/int32 with at least READ_CEILING_GROUPS * 64 * WAVES_PER_GROUP
+    elements."""
+    nbytes = src.numel() * src.element_size()
+    st = load_library().pkv_debug_read_ceiling(
+        _ptr(src, "src"), nbytes, _ptr(sink, "sink", (torch.int32, torch.uint32)), sink.numel(),
+        _stream(stream))
+    _check("pkv_debug_read_ceiling", st)

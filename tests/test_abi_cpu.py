@@ -25,7 +25,7 @@ def test_header_declares_expected_entry_points():
     assert set(names) == {
         "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
         "pkv_append_kv", "pkv_decode", "pkv_decode_append", "pkv_decode_masked",
-        "pkv_decode_tokens", "pkv_prefill", "pkv_debug_validate"}
+        "pkv_decode_tokens", "pkv_prefill", "pkv_debug_validate", "pkv_debug_read_ceiling"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -137,6 +137,9 @@ def test_host_checks_reject_before_launch(lib):
                 4, 0.1, fake, ws_bytes, fake, None) == 4
     assert _raw(lib, "pkv_decode_tokens", B(d), fake, fake, 100, fake, 8, fake, fake, fake, 4, 0.1,
                 fake, 16, fake, None) == 3
+    # read-ceiling probe: size not a multiple of 16, sink too small
+    assert _raw(lib, "pkv_debug_read_ceiling", fake, 100, fake, 1 << 20, None) == 1
+    assert _raw(lib, "pkv_debug_read_ceiling", fake, 1 << 20, fake, 1000, None) == 1
     # NaN scale
     assert _raw(lib, "pkv_decode", B(pool), B(d), fake, fake, fake, 10, fake, 4, float("nan"),
                 fake, ws_bytes, fake, None) == 1

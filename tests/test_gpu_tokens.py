@@ -117,3 +117,20 @@ def test_tokens_match_paged_decode_bitwise():
     paged = run.step()
     tok = run_tokens(W.tokens_from_pages(batch))
     assert np.array_equal(paged, tok)
+
+
+def test_read_ceiling_probe_reads_every_word_once():
+    # The diagnostic read kernel: the xor of all its per-lane folds equals the
+    # xor of every 32-bit word of the buffer (each word read exactly once).
+    g = torch.Generator().manual_seed(5)
+    n_words = (3 << 20) + 4 * 37  # not a multiple of the per-wave span
+    host = torch.randint(-(1 << 31), (1 << 31) - 1, (n_words,), dtype=torch.int64,
+                         generator=g).to(torch.int32)
+    src = host.to("cuda:0")
+    sink = torch.full((pkv.READ_CEILING_GROUPS * 64 * pkv.WAVES_PER_GROUP,), 7, dtype=torch.int32,
+                      device="cuda:0")
+    pkv.pkv_debug_read_ceiling(src, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert got == want
