@@ -1,7 +1,7 @@
 // Paged prefill / extend attention for gfx950: ragged query rows per request
 // attend to the request's paged KV (prefix + new tokens), causal or not.
-// The eight waves of a workgroup share one KV head: each 64-token chunk of its
-// K and V is fetched once into LDS (double buffered) and read by all of them.
+// The waves of a workgroup share one KV head: each chunk of its K and V (32
+// keys) is fetched once into LDS (double buffered) and read by all of them.
 //
 // The pages' paged prefill takes query rows flattened over the batch with
 // per-request offsets, per-request KV lengths and a causal flag with offset 0
@@ -148,17 +148,22 @@ struct Wave32 {
   }
 };
 
+// Two workgroups per CU (four waves per SIMD) need at most 128 VGPRs: the
+// attribute holds the compiler to that (a couple of spilled registers at
+// D = 128); with one workgroup per CU the kernel measured 11% slower.
 template <int D, int HG>
-__global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+prefill_kernel(PrefillArgs a) {
   constexpr int QT = 16 / HG;     // query tokens per row tile
   constexpr int ROWS = QT * HG;   // score rows in use per tile (15 for HG = 3)
   constexpr int NT = kPrefillTiles;  // row tiles per wave
-  constexpr int kSteps = 2;       // 32-key steps per LDS chunk
+  constexpr int kThreads = kPrefillWaves * kWave;
+  constexpr int kSteps = kPrefillSteps;  // 32-key steps per LDS chunk
   constexpr int kHalves = 2 * kSteps;  // 16-key pieces per chunk (one page each at P = 16)
   constexpr int kPieces = D * 16 * 2 / 16;  // 16-byte pieces of 16 keys' K (same for V)
-  static_assert(2 * kPieces * kHalves % kGroupThreads == 0 && kPieces % kWave == 0,
+  static_assert(2 * kPieces * kHalves % kThreads == 0 && kPieces % kWave == 0,
                 "whole, wave-uniform loads per thread");
-  constexpr int kLoads = 2 * kPieces * kHalves / kGroupThreads;  // per thread and chunk
+  constexpr int kLoads = 2 * kPieces * kHalves / kThreads;  // per thread and chunk
   // Two chunks (double buffer) of K as [16 keys][D/8][16 keys][8 channels]
   // and V as [32 keys][D/16][4][16 channels][2][4 keys]: the operand of lane
   // (g, r) -- K channel block 4kk + g of key r, V keys 4g .. 4g+3 of both
@@ -167,7 +172,7 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   // chunk the same bytes hold the per-wave output rows [wave][16][D] in fp32.
   constexpr int kKBytes = kHalves * D * 16 * 2;
   constexpr int kBufBytes = 2 * kKBytes;  // K + V of one chunk
-  constexpr int kOutBytes = kWavesPerGroup * 16 * D * 4;
+  constexpr int kOutBytes = kPrefillWaves * 16 * D * 4;
   __shared__ __align__(16) char smem[2 * kBufBytes > kOutBytes ? 2 * kBufBytes : kOutBytes];
   auto k_at = [&](int buf, int hf, int cb, int t) {  // 16 bytes: K channels 8cb.. of key t
     return smem + buf * kBufBytes + ((hf * (D / 8) + cb) * 16 + t) * 16;
@@ -196,7 +201,7 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
     u = (int)((t / gx) % gy);
     b = (int)(t / (gx * gy));
   }
-  const int wg_tok0 = bx * kWavesPerGroup * NT * QT;  // first query token of the workgroup
+  const int wg_tok0 = bx * kPrefillWaves * NT * QT;  // first query token of the workgroup
   const int tok0 = wg_tok0 + w * NT * QT;              // first query token of this wave
   const int q0 = a.qo_indptr[b];
   const int n = a.qo_indptr[b + 1] - q0;
@@ -228,7 +233,7 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
     return a.causal ? max(0, min(L, L - n + last + 1)) : L;
   };
   const int kv_end = active ? block_end(tok0) : 0;
-  const int wg_end = block_end(min(wg_tok0 + (kWavesPerGroup - 1) * NT * QT, n - 1));
+  const int wg_end = block_end(min(wg_tok0 + (kPrefillWaves - 1) * NT * QT, n - 1));
 
   Wave32<D, NT> st;
   st.init();
@@ -283,7 +288,7 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
   uint4 stage[kLoads];
   int pids[kHalves];  // pages of the 16-key pieces of the chunk being fetched
   auto piece = [&](int i, int& hf, int& y, bool& is_v) {
-    const int xw = w * kWave + i * kGroupThreads;  // the wave's first piece
+    const int xw = w * kWave + i * kThreads;  // the wave's first piece
     hf = xw / (2 * kPieces);
     const int yw = xw - hf * 2 * kPieces;
     is_v = yw >= kPieces;
@@ -412,7 +417,7 @@ __global__ void __launch_bounds__(kGroupThreads) prefill_kernel(PrefillArgs a) {
 
 template <int D>
 hipError_t launch_p(const PrefillArgs& a, int hg, dim3 grid, hipStream_t s) {
-  const dim3 block(kGroupThreads);
+  const dim3 block(kPrefillWaves * kWave);
   switch (hg) {
     case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, block, 0, s, a); break;
@@ -428,7 +433,7 @@ hipError_t launch_p(const PrefillArgs& a, int hg, dim3 grid, hipStream_t s) {
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int hg, int max_q_len,
                           hipStream_t s) {
   const int qt = 16 / hg;
-  const int per_group = qt * kPrefillTiles * kWavesPerGroup;  // query tokens one workgroup covers
+  const int per_group = qt * kPrefillTiles * kPrefillWaves;  // query tokens one workgroup covers
   const dim3 grid((max_q_len + per_group - 1) / per_group, a.num_q_heads / hg, a.batch);
   if (grid.x == 0 || grid.z == 0) return hipSuccess;
   if ((long long)grid.x * grid.y * grid.z > INT32_MAX) return hipErrorInvalidConfiguration;
