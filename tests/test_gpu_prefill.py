@@ -28,9 +28,11 @@ CASES = {
 }
 
 
-def run_prefill(batch, causal, max_q_len=None):
+def run_prefill(batch, causal, max_q_len=None, seq_lens=None):
     dev = "cuda:0"
     t = W.to_device(batch, dev)
+    if seq_lens is not None:  # attend to fewer keys than the pool holds
+        t["seq_lens"] = torch.from_numpy(np.asarray(seq_lens, np.int32)).to(dev)
     desc = pkv.Desc(max_batch=batch.B, num_q_heads=batch.Hq, num_kv_heads=batch.Hkv,
                     head_dim=batch.D, page_size=batch.P)
     ws = torch.empty(pkv.pkv_workspace_bytes(desc), dtype=torch.uint8, device=dev)
@@ -71,3 +73,32 @@ def test_prefill_single_rows_match_decode_semantics():
     dec = oracle.decode(batch.q_rows, batch.k_pool, batch.v_pool, ip, batch.kv_indices,
                         batch.seq_lens, batch.sm_scale, batch.P)
     compare(got, dec, "prefill q_len 1 vs decode oracle")
+
+
+def test_prefill_ragged_extend_batch():
+    # Many requests of a serving step's extend phase: ragged new-token counts
+    # (zero included) over ragged cached prefixes, G = 4, D = 128.
+    rng = np.random.default_rng(np.random.PCG64(61))
+    q_lens = rng.integers(0, 41, size=24)
+    q_lens[[3, 17]] = 0
+    prefix = rng.integers(0, 301, size=24)
+    say(f"prefill ragged extend: {int(q_lens.sum())} rows, {int((q_lens + prefix).sum())} keys")
+    batch = W.make_prefill(name="extend24", seed=61, Hq=32, Hkv=8, D=128, P=16,
+                           q_lens=q_lens, prefix_lens=prefix)
+    for causal in (True, False):
+        got = run_prefill(batch, causal)
+        compare(got, oracle_prefill(batch, causal), f"ragged extend causal={causal}")
+
+
+def test_prefill_rows_without_keys_are_zero():
+    # Fewer keys than query rows (seq_len below q_len): with the causal mask
+    # aligned to the end of the keys, the first rows see none and are zero.
+    batch = W.make_prefill(name="nokeys", seed=62, Hq=8, Hkv=2, D=64, P=16, q_lens=[40],
+                           prefix_lens=[0])
+    short = np.array([25], np.int32)
+    got = run_prefill(batch, True, seq_lens=short)
+    ip = oracle.kv_indptr(short, batch.P)
+    ref = oracle.prefill(batch.q_rows, batch.k_pool, batch.v_pool, ip, batch.kv_indices, short,
+                         batch.qo_indptr, batch.sm_scale, batch.P, True)
+    assert np.array_equal(got[:15], np.zeros_like(got[:15]))
+    compare(got, ref, "rows without keys")
