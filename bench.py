@@ -224,6 +224,19 @@ def bench_ceiling(pkv, torch, dev, stream, K, nbytes):
             "frac": round(gbps / PEAK_HBM_GBPS, 4), "copies": copies}
 
 
+def paced(K, fn):
+    """Mean wall-clock ms of fn(i) over K calls issued by the host one after
+    another, the GPU idle at the start: host launch cost included."""
+    import torch
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / K
+
+
 def timed(stream, K, fn):
     """Mean ms of fn(i) over K calls enqueued behind a bounded spin, events at the ends."""
     import torch
@@ -328,7 +341,16 @@ def main():
             graphs.append(g)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
-        ms_step = timed(stream, K, lambda i: graphs[i % ncopies].replay())
+
+        def replay(i):
+            graphs[i % ncopies].replay()
+        ms_step = timed(stream, K, replay)
+        # The same steps paced by the host (no spin ahead of them): each eager
+        # step pays its launches' host cost, a replay one graph launch.
+        graph_cmp = {"graph_device_us": round(ms_step * 1e3, 2),
+                     "eager_device_us": round(timed(stream, K, step) * 1e3, 2),
+                     "graph_host_paced_us": round(paced(K, replay) * 1e3, 2),
+                     "eager_host_paced_us": round(paced(K, step) * 1e3, 2)}
     else:
         ms_step = timed(stream, K, step)
 
@@ -373,6 +395,8 @@ def main():
         })
     if args.prefill:
         res["prefill"] = bench_prefill(pkv, W, torch, dev, stream, K)
+    if args.graph:
+        res["graph_compare"] = graph_cmp
     if args.tokens:
         res["tokens"] = bench_tokens(pkv, W, torch, dev, stream, K)
     if args.ceiling:
