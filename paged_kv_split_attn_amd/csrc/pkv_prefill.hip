@@ -56,8 +56,7 @@ struct Wave32 {
 
   // k[h][kk]: K of token r of half h, channels 8 (4kk + g) .. +8.
   // load_v(vv) fills vv[vb] with channel 16 vb + r, keys 4g .. 4g+3 of half 0
-  // then of half 1; it runs once the scores are issued, so that K and V
-  // operands are not live at the same time.  keep[t]: bit 4h + j set when key
+  // then of half 1; it is called after the score MFMAs, which need only K.  keep[t]: bit 4h + j set when key
   // 16h + 4g + j counts for this lane's row of tile t.  vlive: keys from this
   // one on hold no data (their V is zeroed); 32 when all do.
   template <class LoadV>
@@ -87,7 +86,6 @@ struct Wave32 {
       for (int i = 0; i < 8; ++i)
         if (((keep[t] >> i) & 1u) == 0) s[t][i] = kMinusInf;
     }
-    __builtin_amdgcn_sched_barrier(0);
     uint4 vv[VB];
     load_v(vv);
     if (vlive < 32) {
@@ -144,7 +142,6 @@ struct Wave32 {
         o[t][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[t], vt, o[t][vb], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);  // the next step's K loads start after this one's V
   }
 };
 
