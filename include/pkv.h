@@ -139,7 +139,10 @@ typedef struct pkv_desc {
  * caller allocates it once (any device allocation, 256-byte aligned) and passes
  * it to every pkv_build_metadata / pkv_decode call of that descriptor.  Its
  * contents need no initialisation: pkv_build_metadata writes everything the
- * decode reads. */
+ * decode reads.  The decode calls of a step reuse the plan and overwrite the
+ * partials and arrival counters, so calls that share a workspace must run one
+ * after another (in one stream, or ordered by events); concurrent calls need
+ * one workspace each. */
 size_t pkv_workspace_bytes(const pkv_desc* desc);
 
 /* Step metadata, once per decode step (before the per-layer calls).
