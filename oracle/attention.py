@@ -34,6 +34,10 @@ the hunk or bullet, as the pages have no section numbers):
   by exp(lse_s - max lse).
 * KV append: the token written this step goes to position seq_len - 1
   (cache.py, bind_tasks: write_pos = seq_lens - 1).
+* Keep mask (decode_masked): token t of request b attends iff t < seq_len and
+  the mask keeps it (the paged decode wrapper's optional 2-D bool mask).
+* Prefill / extend (prefill): n new query rows per request over its L keys,
+  the causal mask aligned to the end of the keys (causal offset 0).
 * Token-major K/V (decode_tokens): one [Hkv, D] row per token slot, found
   through a request-to-token table (page size 1) or at b * stride + t in the
   contiguous [batch, seq, kv_heads, head_dim] layout of the non-paged decode.
