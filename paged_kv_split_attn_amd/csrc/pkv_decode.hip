@@ -600,10 +600,12 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // Merge every segment this workgroup arrived last for.  Wave w merges output
   // groups 16 w .. 16 w + 15; the four 16-lane quarters of the wave take the
   // segment's workgroups in turn (quarter q: contributors q, q + 4, ...).  Every
-  // load of a round is issued before any is used, and addresses are clamped so
-  // the loads need no branches.  The quarters' results are then combined
-  // across lanes (quarter pairs 0+1 and 2+3, then the two pairs, lower first),
-  // so the result depends only on the plan and no barrier is needed.
+  // load of a round is issued before any is used; a quarter issues loads only
+  // for contributors that exist (the loads bypass the caches, so a repeated
+  // load would cost a memory round trip of its own).  The quarters' results
+  // are then combined across lanes (quarter pairs 0+1 and 2+3, then the two
+  // pairs, lower first), so the result depends only on the plan and no
+  // barrier is needed.
   static_assert(kWavesPerGroup * 16 >= kVec, "one output group per lane of a quarter");
   constexpr int kQuarters = 4;
   constexpr int kPer = 8;  // contributors per quarter and segment in one round
@@ -630,12 +632,16 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     for (int k = 0; k < 2; ++k) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const int j = max(min(lo[k] + (rd * kPer + i) * kQuarters + q, hi[k]), 0);
-        const int row = (2 * j + (j == lo[k] ? slot0[k] : 0)) * HG + h;
-        ls[k][i] = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(lse_rs, row * 4, 0, kCoherent));
-        ov[k][i] = __builtin_bit_cast(
-            f4, __builtin_amdgcn_raw_buffer_load_b128(opart_rs, (row * D + c) * 4, 0, kCoherent));
+        const int j = lo[k] + (rd * kPer + i) * kQuarters + q;
+        ls[k][i] = kFloorMax;
+        ov[k][i] = f4{0.f, 0.f, 0.f, 0.f};
+        if (j <= hi[k]) {  // uniform over a quarter
+          const int row = (2 * j + (j == lo[k] ? slot0[k] : 0)) * HG + h;
+          ls[k][i] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(lse_rs, row * 4, 0, kCoherent));
+          ov[k][i] = __builtin_bit_cast(
+              f4, __builtin_amdgcn_raw_buffer_load_b128(opart_rs, (row * D + c) * 4, 0, kCoherent));
+        }
       }
     }
     // This round's contributors: max first, then one exponential each.
