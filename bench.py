@@ -53,6 +53,10 @@ def parse():
                     help="KV append fused into the decode launch, or its own launch")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured hipGraph (one graph per pool copy)")
+    ap.add_argument("--layers", type=int, default=0, metavar="N",
+                    help="also time a model-like decode step: one metadata build, then N layers of "
+                         "fused append + decode (each layer its own pool and q), issued eagerly and "
+                         "replayed from one captured hipGraph, timed on the device and host-paced")
     ap.add_argument("--mask-keep", type=float, default=None, metavar="P",
                     help="also time pkv_decode_masked with a random keep mask of density P")
     ap.add_argument("--prefill", action="store_true",
@@ -222,6 +226,53 @@ def bench_ceiling(pkv, torch, dev, stream, K, nbytes):
     gbps = n / (ms * 1e-3) / 1e9
     return {"bytes": n, "us_per_call": round(ms * 1e3, 2), "GBps": round(gbps, 1),
             "frac": round(gbps / PEAK_HBM_GBPS, 4), "copies": copies}
+
+
+def bench_layers(pkv, torch, stream, K, batch, desc, base, nl):
+    """A decode step of an nl-layer model's attention: pkv_build_metadata once,
+    then pkv_decode_append for every layer (its own pool and q), eager and as
+    one hipGraph replay.  Device-timed (host enqueues ahead) and host-paced
+    (GPU idle at the start, launch cost included)."""
+    layers = [(pkv.Pool(base["k_pool"].clone(), base["v_pool"].clone()), base["q"].clone())
+              for _ in range(nl)]
+    ws = torch.zeros(pkv.pkv_workspace_bytes(desc), dtype=torch.uint8, device=stream.device)
+    kv_indptr = torch.zeros(batch.B + 1, dtype=torch.int32, device=stream.device)
+    out = torch.zeros((batch.B, batch.Hq, batch.D), dtype=torch.int16, device=stream.device)
+    seq, idx = base["seq_lens"], base["kv_indices"]
+
+    def step_on(st):
+        pkv.pkv_build_metadata(desc, seq, 0, kv_indptr, ws, st)
+        for pool, q in layers:
+            pkv.pkv_decode_append(pool, desc, q, base["k_new"], base["v_new"], kv_indptr, idx, seq,
+                                  batch.sm_scale, ws, out, st)
+
+    for _ in range(3):
+        step_on(stream)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step_on(cap)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref):
+        raise RuntimeError("graph replay of the layered step differs from the eager step")
+    eager = lambda i: step_on(stream)  # noqa: E731
+    replay = lambda i: g.replay()  # noqa: E731
+    kl = max(5, K // 4)
+    res = {"layers": nl, "workload": batch.name,
+           "eager_device_us": timed(stream, kl, eager) * 1e3,
+           "graph_device_us": timed(stream, kl, replay) * 1e3,
+           "eager_host_paced_us": paced(kl, eager) * 1e3,
+           "graph_host_paced_us": paced(kl, replay) * 1e3}
+    res = {k: (round(v, 1) if isinstance(v, float) else v) for k, v in res.items()}
+    res["graph_speedup_host_paced"] = round(res["eager_host_paced_us"] / res["graph_host_paced_us"], 3)
+    return res
 
 
 def paced(K, fn):
@@ -401,6 +452,8 @@ def main():
         res["tokens"] = bench_tokens(pkv, W, torch, dev, stream, K)
     if args.ceiling:
         res["read_ceiling"] = bench_ceiling(pkv, torch, dev, stream, K, call_bytes)
+    if args.layers > 0:
+        res["layered_step"] = bench_layers(pkv, torch, stream, K, batch, desc, base, args.layers)
     if args.mask_keep is not None:
         S = -(-int(batch.seq_lens.max()) // 4) * 4
         rng = np.random.default_rng(np.random.PCG64(2000 + args.config))

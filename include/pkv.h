@@ -121,7 +121,7 @@ typedef struct pkv_pool {
  *  num_workgroups       workgroups of the decode grid (0 = one per compute unit
  *                       of the device current at the call; 1 .. 65536)
  *  min_tiles_per_group  fewest tiles a workgroup is given; small batches use
- *                       fewer workgroups (0 = default 8)
+ *                       fewer workgroups (0 = default 16)
  */
 typedef struct pkv_desc {
   int32_t max_batch;

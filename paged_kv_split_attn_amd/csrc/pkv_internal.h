@@ -17,7 +17,7 @@ constexpr int kXcds = 8;  // accelerator dies of the chip, each with its own L2
 constexpr int kPrefillTiles = 1;  // 16-row tiles per prefill wave (2 measured slower: fewer, longer workgroups)
 constexpr int kPrefillWaves = 8;  // waves of a prefill workgroup (they share each K/V chunk)
 constexpr int kPrefillSteps = 1;  // 32-key steps per prefill K/V chunk (two measured slower)
-constexpr int kDefaultMinTiles = 8;
+constexpr int kDefaultMinTiles = 16;  // fewer tiles per workgroup measured slower on small batches
 constexpr int kMaxBatch = 65536;
 constexpr int kMaxGroups = 65536;
 constexpr int kMetaLdsRequests = 8192;  // kv_indptr entries the metadata kernel keeps in LDS

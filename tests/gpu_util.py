@@ -29,7 +29,7 @@ def make_desc(batch, num_workgroups=0, min_tiles=0, max_batch=None):
 def oracle_plan(batch, desc, forced=0):
     _, U = oracle.head_groups(batch.Hq, batch.Hkv)
     return oracle.plan_stream(batch.seq_lens, batch.P, U, desc.groups(),
-                              desc.min_tiles_per_group or 8, forced,
+                              desc.min_tiles_per_group or 16, forced,
                               waves_per_group=pkv.WAVES_PER_GROUP)
 
 
