@@ -58,10 +58,13 @@ struct Wave32 {
   // load_v(vv) fills vv[vb] with channel 16 vb + r, keys 4g .. 4g+3 of half 0
   // then of half 1; it is called after the score MFMAs, which need only K.  keep[t]: bit 4h + j set when key
   // 16h + 4g + j counts for this lane's row of tile t.  vlive: keys from this
-  // one on hold no data (their V is zeroed); 32 when all do.
+  // one on hold no data (their V is zeroed); 32 when all do.  masked (uniform)
+  // false: every key of the step counts for every row of the wave, and keep
+  // and vlive are not read (most steps of a causal block lie below its
+  // diagonal, and the per-key selects are a fifth of a step's vector work).
   template <class LoadV>
   __device__ __forceinline__ void step(const uint4 (&k)[2][KB], LoadV&& load_v,
-                                       const uint32_t (&keep)[NT], int vlive, int g,
+                                       const uint32_t (&keep)[NT], int vlive, bool masked, int g,
                                        float scale_log2, const float (&bias)[NT]) {
     floatx4_t sc[NT][2];
 #pragma unroll
@@ -82,13 +85,17 @@ struct Wave32 {
         s[t][i] = fmaf(sc[t][0][i], scale_log2, bias[t]);
         s[t][4 + i] = fmaf(sc[t][1][i], scale_log2, bias[t]);
       }
+    }
+    if (masked) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (((keep[t] >> i) & 1u) == 0) s[t][i] = kMinusInf;
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (((keep[t] >> i) & 1u) == 0) s[t][i] = kMinusInf;
     }
     uint4 vv[VB];
     load_v(vv);
-    if (vlive < 32) {
+    if (masked && vlive < 32) {
       // Keys past the sequence end may hold anything, NaN included: a zero
       // weight times their V must give exactly zero.
       const uint32_t lv = keys_upto(vlive - 1 - 4 * g);
@@ -230,6 +237,9 @@ prefill_kernel(PrefillArgs a) {
     return a.causal ? max(0, min(L, L - n + last + 1)) : L;
   };
   const int kv_end = active ? block_end(tok0) : 0;
+  // The last key every row of the wave sees (its first token has the
+  // smallest causal limit).
+  const int lim_min = min(a.causal ? L - n + tok0 : L - 1, kv_end - 1);
   const int wg_end = block_end(min(wg_tok0 + (kPrefillWaves - 1) * NT * QT, n - 1));
 
   Wave32<D, NT> st;
@@ -356,16 +366,23 @@ prefill_kernel(PrefillArgs a) {
           for (int vb = 0; vb < Wave32<D, NT>::VB; ++vb)
             vv[vb] = *reinterpret_cast<const uint4*>(v_at(buf, s, 16 * vb + r16, g4, 0));
         };
-        const int vlive = min(32, kv_end - t0);
         // Key t0 + 16h + 4 g4 + j counts for a row when it is at most
-        // min(lim, kv_end - 1) and its page exists.
-        const uint32_t pages_ok = (live_pids[2 * s] < 0 ? 0u : 0x0fu) |
-                                  (live_pids[2 * s + 1] < 0 ? 0u : 0xf0u);
+        // min(lim, kv_end - 1) and its page exists; when that holds for all 32
+        // keys and every row of the wave (uniform), no key is masked.
+        const bool pages_all = (live_pids[2 * s] >= 0) & (live_pids[2 * s + 1] >= 0);
+        const bool masked = !(pages_all && t0 + 31 <= lim_min);
+        const int vlive = min(32, kv_end - t0);
         uint32_t keep[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          keep[t] = keys_upto(min(lim[t], kv_end - 1) - t0 - 4 * g4) & pages_ok;
-        st.step(kop, load_v, keep, vlive, g4, a.scale_log2, bias);
+        for (int t = 0; t < NT; ++t) keep[t] = 0xffu;
+        if (masked) {
+          const uint32_t pages_ok = (live_pids[2 * s] < 0 ? 0u : 0x0fu) |
+                                    (live_pids[2 * s + 1] < 0 ? 0u : 0xf0u);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            keep[t] = keys_upto(min(lim[t], kv_end - 1) - t0 - 4 * g4) & pages_ok;
+        }
+        st.step(kop, load_v, keep, vlive, masked, g4, a.scale_log2, bias);
       }
     }
     // The other buffer held chunk c - 1, which every wave finished before the
