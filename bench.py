@@ -87,6 +87,19 @@ def algorithmic_bytes(batch):
     return call, call + append + 4 * (batch.B + 1)
 
 
+def unique_kv_bytes(batch):
+    """K/V bytes of one decode call with every physical page counted once (a
+    page shared by several requests' prefixes is read by each of them)."""
+    used = {}
+    for b, pages in enumerate(batch.page_lists):
+        L = int(batch.seq_lens[b])
+        for j, p in enumerate(pages):
+            n = min(batch.P, L - j * batch.P)
+            if n > 0:
+                used[int(p)] = max(used.get(int(p), 0), n)
+    return sum(used.values()) * batch.Hkv * batch.D * 2 * 2
+
+
 def cpu_baseline(batch, budget_s):
     import oracle
     from threadpoolctl import threadpool_limits
@@ -436,6 +449,11 @@ def main():
         traffic = None
         if ctr is not None:
             traffic = ctr.get("traffic_bytes_per_launch", {}).get(batch.name)
+        kv_bytes = int(batch.seq_lens.astype(np.int64).sum()) * batch.Hkv * batch.D * 2 * 2
+        uniq = unique_kv_bytes(batch)
+        if uniq < kv_bytes:  # shared prefixes: also the rate over bytes counted once
+            res["unique_call_bytes"] = call_bytes - kv_bytes + uniq
+            res["unique_call_GBps"] = round(res["unique_call_bytes"] / (call_ms * 1e-3) / 1e9, 1)
         res.update({
             "us_per_call": round(call_ms * 1e3, 2),
             "call_GBps": round(achieved, 1),

@@ -69,6 +69,14 @@ struct Wave32 {
     floatx4_t sc[NT][2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) sc[t][0] = sc[t][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // The matrix-core runs of a step (scores here, P.V below) are issued at a
+    // raised wave priority, so that a wave that reaches them goes ahead of the
+    // other waves of its SIMD, which are in their vector (softmax) phase: the
+    // waves of a workgroup move in step between the per-chunk barriers, and
+    // without this their matrix and vector phases line up instead of
+    // overlapping (95 -> 91 us on the 4 x 1024 causal batch).
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
@@ -77,6 +85,8 @@ struct Wave32 {
         for (int h = 0; h < 2; ++h)
           sc[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, k[h][kk]), qb[t][kk], sc[t][h], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     float s[NT][8];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -140,6 +150,8 @@ struct Wave32 {
         plo[t][i] = (__bf16)(p[i] - (float)h);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) {
       const bf16x8_t vt = __builtin_bit_cast(bf16x8_t, vv[vb]);
@@ -149,6 +161,7 @@ struct Wave32 {
         o[t][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[t], vt, o[t][vb], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 };
 
