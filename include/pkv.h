@@ -315,14 +315,15 @@ int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int3
 
 /* Diagnostic, not part of the attention path: one launch that reads `bytes`
  * of device memory at src (16-byte aligned, a multiple of 16) with the decode
- * kernel's load shape -- PKV_READ_CEILING_GROUPS workgroups of
- * PKV_WAVES_PER_WORKGROUP waves, 16-byte loads, eight in flight per wave --
+ * kernel's load shape on MI355X -- PKV_READ_CEILING_GROUPS workgroups (one
+ * per compute unit) of PKV_WAVES_PER_WORKGROUP waves, 16-byte loads, eight in
+ * flight per wave --
  * and writes one xor-fold per lane to sink, so that timing it gives the
  * achievable read rate of a launch of that size on this machine.
  *  sink        device uint32 [sink_words], sink_words >= PKV_READ_CEILING_GROUPS
  *              * 64 * PKV_WAVES_PER_WORKGROUP
  * Errors: PKV_ERR_INVALID_ARG (NULL, misaligned size, small sink), PKV_ERR_LAUNCH. */
-#define PKV_READ_CEILING_GROUPS 512
+#define PKV_READ_CEILING_GROUPS 256
 int pkv_debug_read_ceiling(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
                            void* stream);
 

@@ -1,7 +1,7 @@
 // Read-bandwidth ceiling probe: the achievable HBM read rate of one launch of a
-// given size on this machine, with the decode kernel's load shape (512-thread
-// workgroups, 16-byte loads, 1 KiB per wave instruction, eight loads in
-// flight per wave).  Diagnostic only; not part of the attention path.
+// given size on this machine, with the decode kernel's load shape (one
+// workgroup of eight waves per compute unit, 16-byte loads, 1 KiB per wave
+// instruction, eight loads in flight per wave).  Diagnostic only; not part of the attention path.
 #include "pkv_internal.h"
 
 namespace pkv {
