@@ -28,9 +28,11 @@ CASES = {
 }
 
 
-def run_prefill(batch, causal, max_q_len=None, seq_lens=None):
+def run_prefill(batch, causal, max_q_len=None, seq_lens=None, edit=None):
     dev = "cuda:0"
     t = W.to_device(batch, dev)
+    if edit is not None:  # change the device inputs (e.g. corrupt a page id)
+        edit(t)
     if seq_lens is not None:  # attend to fewer keys than the pool holds
         t["seq_lens"] = torch.from_numpy(np.asarray(seq_lens, np.int32)).to(dev)
     desc = pkv.Desc(max_batch=batch.B, num_q_heads=batch.Hq, num_kv_heads=batch.Hkv,
@@ -102,3 +104,30 @@ def test_prefill_rows_without_keys_are_zero():
                          batch.qo_indptr, batch.sm_scale, batch.P, True)
     assert np.array_equal(got[:15], np.zeros_like(got[:15]))
     compare(got, ref, "rows without keys")
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_prefill_bad_page_id_drops_its_keys(causal):
+    # Request 1's second page id points one past the pool.  The kernel skips
+    # that page's 16 keys; they lie below every row's causal limit, so the
+    # result is the attention over the request without that page (positions
+    # after it shift down by a page in the reduced problem and every limit
+    # with them).  The other requests are untouched.
+    say(f"prefill bad page id causal={causal}")
+    batch = W.make_prefill(name="badpage", seed=63, Hq=32, Hkv=8, D=128, P=16,
+                           q_lens=[5, 20, 7], prefix_lens=[40, 64, 30])
+    pos = len(batch.page_lists[0]) + 1
+
+    def corrupt(t):
+        t["kv_indices"][pos] = batch.num_pages
+    got = run_prefill(batch, causal, edit=corrupt)
+    ref = oracle_prefill(batch, causal)
+    qo = batch.qo_indptr
+    for b in (0, 2):
+        compare(got[qo[b]:qo[b + 1]], ref[qo[b]:qo[b + 1]], f"untouched request {b}")
+    pages = np.delete(batch.page_lists[1], 1).astype(np.int32)
+    L = np.array([int(batch.seq_lens[1]) - batch.P], np.int32)
+    q1 = batch.q_rows[qo[1]:qo[2]]
+    ref1 = oracle.prefill(q1, batch.k_pool, batch.v_pool, oracle.kv_indptr(L, batch.P), pages, L,
+                          np.array([0, len(q1)], np.int32), batch.sm_scale, batch.P, causal)
+    compare(got[qo[1]:qo[2]], ref1, "request 1 without its skipped page")
