@@ -203,17 +203,30 @@ prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  // Tile order.  Workgroups go to the XCDs round robin by linear id; the
-  // order below gives each XCD whole runs of query blocks of one (request,
-  // head group), so that their K/V chunks stay in that XCD's L2, and puts
-  // the blocks with the longest causal range first in each run.
+  // Tile order.  Workgroups go to the XCDs round robin by linear id, and on
+  // each XCD in that order.  The order below gives each XCD whole runs of
+  // query blocks of a few (request, head group) pairs, so that their K/V
+  // chunks stay in that XCD's L2, and hands out the XCD's blocks longest
+  // causal range first across all of its pairs (longest-processing-time
+  // order: with the pairs taken one after another, the short blocks of the
+  // first pairs ran early and the long blocks of the last pairs formed a tail
+  // that left CUs idle).
   int b, u, bx;
   {
     const uint32_t gx = gridDim.x, gy = gridDim.y;
     const uint32_t n_wg = gx * gy * gridDim.z;  // below 2^31 (checked on the host)
     uint32_t t = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
     const uint32_t full = n_wg & ~(uint32_t)(kXcds - 1);
-    if (t < full) t = (t % kXcds) * (full / kXcds) + t / kXcds;
+    if (t < full) {
+      const uint32_t per = full / kXcds;  // workgroups of one XCD
+      const uint32_t x = t % kXcds, j = t / kXcds;  // XCD, place in its order
+      if (per % gx == 0) {
+        const uint32_t pairs = per / gx;  // whole (request, head group) runs
+        t = x * per + (j % pairs) * gx + j / pairs;
+      } else {
+        t = x * per + j;
+      }
+    }
     bx = (int)(gx - 1 - t % gx);
     u = (int)((t / gx) % gy);
     b = (int)(t / (gx * gy));
