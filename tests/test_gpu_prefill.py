@@ -131,3 +131,34 @@ def test_prefill_bad_page_id_drops_its_keys(causal):
     ref1 = oracle.prefill(q1, batch.k_pool, batch.v_pool, oracle.kv_indptr(L, batch.P), pages, L,
                           np.array([0, len(q1)], np.int32), batch.sm_scale, batch.P, causal)
     compare(got[qo[1]:qo[2]], ref1, "request 1 without its skipped page")
+
+
+def test_prefill_bench_batch_sampled_rows():
+    # The benchmark's prefill batch and launch (4 requests x 1024 new tokens,
+    # no prefix, causal, Hq 32, Hkv 8, D 128, max_q_len 1024), checked on
+    # sampled query rows (every head of each), which the oracle computes one
+    # by one: first and last rows of each request plus random ones.
+    say("prefill benchmark batch, sampled rows")
+    batch = W.make_prefill(name="prefill_b4_q1024", seed=7, Hq=32, Hkv=8, D=128, P=16,
+                           q_lens=[1024] * 4, prefix_lens=[0] * 4, poison=False)
+    got = run_prefill(batch, True, max_q_len=1024)
+    ip = oracle.kv_indptr(batch.seq_lens, batch.P)
+    rng = np.random.default_rng(np.random.PCG64(71))
+    rows = sorted(set(rng.integers(0, 4096, size=40).tolist())
+                  | {0, 1, 1023, 1024, 2047, 3071, 3072, 4095})
+    q = oracle.bf16_to_f64(batch.q_rows)
+    G = batch.Hq // batch.Hkv
+    kv = {}
+    ref = np.zeros((len(rows), batch.Hq, batch.D))
+    for j, r in enumerate(rows):
+        b, i = divmod(r, 1024)
+        if b not in kv:
+            L = int(batch.seq_lens[b])
+            kv[b] = (oracle.gather_request(batch.k_pool, ip, batch.kv_indices, b, L, batch.P),
+                     oracle.gather_request(batch.v_pool, ip, batch.kv_indices, b, L, batch.P))
+        Kd, Vd = kv[b]
+        for hq in range(batch.Hq):
+            h = oracle.kv_head_of(hq, G)
+            ref[j, hq] = oracle.softmax_attend(q[r, hq], Kd[:i + 1, h, :], Vd[:i + 1, h, :],
+                                               batch.sm_scale)
+    compare(got[rows], ref, f"benchmark prefill batch, {len(rows)} sampled rows")
