@@ -162,3 +162,50 @@ def test_prefill_bench_batch_sampled_rows():
             ref[j, hq] = oracle.softmax_attend(q[r, hq], Kd[:i + 1, h, :], Vd[:i + 1, h, :],
                                                batch.sm_scale)
     compare(got[rows], ref, f"benchmark prefill batch, {len(rows)} sampled rows")
+
+
+def test_prefill_graph_replay_matches_eager():
+    # One prefill launch captured in a hipGraph and replayed with new query
+    # rows written in place between replays (the caller's buffers stay put):
+    # every replay is bitwise the eager launch on the same inputs, and both
+    # match the oracle.
+    say("prefill graph replay")
+    batch = W.make_prefill(name="graph_pf", seed=64, Hq=32, Hkv=8, D=128, P=16,
+                           q_lens=[40, 7, 64], prefix_lens=[100, 0, 33])
+    dev = "cuda:0"
+    t = W.to_device(batch, dev)
+    desc = pkv.Desc(max_batch=batch.B, num_q_heads=batch.Hq, num_kv_heads=batch.Hkv,
+                    head_dim=batch.D, page_size=batch.P)
+    ws = torch.empty(pkv.pkv_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    kv_indptr = torch.empty(batch.B + 1, dtype=torch.int32, device=dev)
+    pkv.pkv_build_metadata(desc, t["seq_lens"], 0, kv_indptr, ws)
+    out = torch.full(tuple(batch.q_rows.shape), 0x7FC0, dtype=torch.int16, device=dev)
+    pool = pkv.Pool(t["k_pool"], t["v_pool"])
+
+    def launch():
+        pkv.pkv_prefill(pool, desc, t["q_rows"], t["qo_indptr"], kv_indptr, t["kv_indices"],
+                        t["seq_lens"], 64, True, batch.sm_scale, out)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch()  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    rng = np.random.default_rng(np.random.PCG64(65))
+    for rep in range(3):
+        batch.q_rows = W.normal_bf16(rng, batch.q_rows.shape)
+        t["q_rows"].copy_(torch.from_numpy(batch.q_rows.view(np.int16)))
+        out.fill_(0x7FC0)
+        g.replay()
+        torch.cuda.synchronize()
+        replay_bits = out.cpu().numpy().view(np.uint16).copy()
+        out.fill_(0x7FC0)
+        launch()
+        torch.cuda.synchronize()
+        eager = out.cpu().numpy().view(np.uint16).copy()
+        assert np.array_equal(replay_bits, eager), f"replay {rep} differs from eager"
+        compare(eager, oracle_prefill(batch, True), f"graph replay {rep}")
