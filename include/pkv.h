@@ -151,7 +151,8 @@ size_t pkv_workspace_bytes(const pkv_desc* desc);
  * step, the token appended this step included) it writes
  *   kv_indptr   device int32 [batch + 1], page prefix sums as defined above,
  * and the work plan into the workspace.  Plan, with U = num_q_heads / H query
- * head groups per request (H = G for G <= 4, else 4) and T = kv_indptr[batch] * U
+ * head groups per request (H = G for G <= 4, 8 for a multiple of 8, else 4) and
+ * T = kv_indptr[batch] * U
  * tiles:
  *   groups   W = min(num_workgroups, max(1, ceil(T / min_tiles_per_group))),
  *            or min(forced_groups, num_workgroups, T) when forced_groups > 0;

@@ -328,7 +328,7 @@ int pkv_prefill(const pkv_pool* pool, const pkv_desc* desc, const void* q,
     return PKV_ERR_INVALID_ARG;
   if (batch > desc->max_batch || batch > 65535) return PKV_ERR_CAPACITY;
   if (batch == 0 || max_q_len == 0) return PKV_OK;
-  const int hg = heads_per_group(desc->num_q_heads / desc->num_kv_heads);
+  const int hg = prefill_heads_per_group(desc->num_q_heads / desc->num_kv_heads);
   const long long per_group = 16 / hg * kPrefillTiles * kPrefillWaves;  // query tokens of one workgroup
   if ((max_q_len + per_group - 1) / per_group * (desc->num_q_heads / hg) * batch > INT32_MAX)
     return PKV_ERR_CAPACITY;

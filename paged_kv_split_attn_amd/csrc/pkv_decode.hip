@@ -416,29 +416,34 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       for (int i = 0; i < HG; ++i) {
         const float li = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt), i));
         const float inv = li > 0.f ? 1.0f / li : 0.f;
-        if (g4 == 0) {
+        if (g4 == (i >> 2)) {  // head i: register i % 4 of lane group i / 4
 #pragma unroll
-          for (int vb = 0; vb < MfmaWave<D, HG>::VB; ++vb) s_out[w][i][16 * vb + r16] = st.o[vb][i] * inv;
+          for (int vb = 0; vb < MfmaWave<D, HG>::VB; ++vb)
+            s_out[w][i][16 * vb + r16] = st.o[vb][i & 3] * inv;
         }
       }
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes land first
-      if (lane < HG * (D / 8)) {
-        const int i = lane / (D / 8);
-        const int c8 = (lane - i * (D / 8)) * 8;
-        const float4 x0 = *reinterpret_cast<const float4*>(&s_out[w][i][c8]);
-        const float4 x1 = *reinterpret_cast<const float4*>(&s_out[w][i][c8 + 4]);
-        *reinterpret_cast<uint4*>(a.out + ((size_t)b * Hq + hq0 + i) * D + c8) =
-            make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
-                       pack_bf16x2(x1.z, x1.w));
+#pragma unroll
+      for (int e8 = 0; e8 < HG * (D / 8); e8 += kWave) {  // one pass when HG * D <= 512
+        if (e8 + lane < HG * (D / 8)) {
+          const int i = (e8 + lane) / (D / 8);
+          const int c8 = (e8 + lane - i * (D / 8)) * 8;
+          const float4 x0 = *reinterpret_cast<const float4*>(&s_out[w][i][c8]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&s_out[w][i][c8 + 4]);
+          *reinterpret_cast<uint4*>(a.out + ((size_t)b * Hq + hq0 + i) * D + c8) =
+              make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
+                         pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
+        }
       }
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before s_out is reused
     } else {
       const int slot = piece == 0 ? 0 : 1;
 #pragma unroll
       for (int i = 0; i < HG; ++i) {
-        if (g4 == 0) {
+        if (g4 == (i >> 2)) {
 #pragma unroll
-          for (int vb = 0; vb < MfmaWave<D, HG>::VB; ++vb) s_acc[w][slot][i][16 * vb + r16] = st.o[vb][i];
+          for (int vb = 0; vb < MfmaWave<D, HG>::VB; ++vb)
+            s_acc[w][slot][i][16 * vb + r16] = st.o[vb][i & 3];
         }
         if (lane == i) {
           s_m[w][slot][i] = st.m;
@@ -475,7 +480,9 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // Epilogue.  Outputs are handled as groups of four channels: thread t < kVec
   // owns channels 4 (t % (D / 4)) .. +3 of head t / (D / 4) of a segment.
   constexpr int kVec = HG * D / 4;
-  static_assert(kVec <= 128 && kGroupThreads % 128 == 0, "thread quarters of 128");
+  constexpr int kVecPass = kWavesPerGroup * 16;  // output groups one merge pass covers
+  constexpr int kVecPasses = (kVec + kVecPass - 1) / kVecPass;
+  static_assert(kGroupThreads % 128 == 0, "thread quarters of 128");
   // Buffer resources of the partials (built where used: they occupy scalar
   // registers).
   auto lse_rsrc = [&]() {
@@ -544,9 +551,13 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  if (tid < HG * D) {
-    const int h = tid / D;
-    const int c = tid - h * D;
+  constexpr int kP2 = (HG * D + kGroupThreads - 1) / kGroupThreads;  // passes over the outputs
+#pragma unroll
+  for (int r2 = 0; r2 < kP2; ++r2) {
+  const int e2 = tid + r2 * kGroupThreads;
+  if (e2 < HG * D) {
+    const int h = e2 / D;
+    const int c = e2 - h * D;
     const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
     float acc = 0.f;
 #pragma unroll
@@ -567,6 +578,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       }
       acc = 0.f;
     }
+  }
   }
 
   // Cross-workgroup merge: publish the partials, count arrivals, and let the
@@ -606,14 +618,9 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // are then combined across lanes (quarter pairs 0+1 and 2+3, then the two
   // pairs, lower first), so the result depends only on the plan and no
   // barrier is needed.
-  static_assert(kWavesPerGroup * 16 >= kVec, "one output group per lane of a quarter");
   constexpr int kQuarters = 4;
   constexpr int kPer = 8;  // contributors per quarter and segment in one round
   const int q = lane >> 4;
-  const int t = w * 16 + (lane & 15);
-  const bool tact = t < kVec;
-  const int h = tact ? t / (D / 4) : 0;
-  const int c = tact ? (t - h * (D / 4)) * 4 : 0;
   // Segment k's contributors are workgroups lo[k] .. hi[k] (none if not merged
   // here).  Workgroup j > lo holds the segment as its first segment (slot 0);
   // the first workgroup holds it in the slot the plan recorded.
@@ -623,6 +630,13 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
   const int span = max(hi[0] - lo[0], hi[1] - lo[1]) + 1;
   const int rounds = (span + kQuarters * kPer - 1) / (kQuarters * kPer);
+  // One pass per 128 output groups (a single pass when HG * D <= 512).
+#pragma unroll
+  for (int og = 0; og < kVecPasses; ++og) {
+  const int t = og * kVecPass + w * 16 + (lane & 15);
+  const bool tact = t < kVec;
+  const int h = tact ? t / (D / 4) : 0;
+  const int c = tact ? (t - h * (D / 4)) * 4 : 0;
   Combine4 mc[2];
 #pragma unroll 1
   for (int rd = 0; rd < rounds; ++rd) {
@@ -690,6 +704,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
           make_uint2(pack_bf16x2(val.x, val.y), pack_bf16x2(val.z, val.w));
     }
   }
+  }
 }
 
 template <int D, int KIND>
@@ -700,6 +715,7 @@ hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
     case 2: hipLaunchKernelGGL((decode_kernel<D, 2, KIND>), grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL((decode_kernel<D, 3, KIND>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((decode_kernel<D, 4, KIND>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, KIND>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

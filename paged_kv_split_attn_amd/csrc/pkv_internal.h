@@ -70,9 +70,13 @@ struct WsLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Query heads one head group covers (the rest of a GQA group of more than four
-// heads goes to sibling head groups that read the same K/V tiles).
-inline int heads_per_group(int G) { return G <= 4 ? G : 4; }
+// Query heads one decode head group covers: the whole GQA group up to four
+// heads, eight for a multiple of eight (one 16-row matrix-core tile holds up to
+// sixteen), else four; the rest of a larger group goes to sibling head groups
+// that read the same K/V tiles again.
+inline int heads_per_group(int G) { return G <= 4 ? G : (G % 8 == 0 ? 8 : 4); }
+// Query heads of one prefill row tile (16 rows = 16 / HG tokens x HG heads).
+inline int prefill_heads_per_group(int G) { return G <= 4 ? G : 4; }
 
 // Returns false for an invalid descriptor; `groups` is the resolved grid size.
 bool ws_layout(const pkv_desc& d, int groups, WsLayout* out);
