@@ -114,7 +114,11 @@ typedef struct pkv_pool {
  * commits by ViperEkura, PagedKV::host_kv_len bullet).
  *
  *  max_batch            requests per call (1 .. 65536)
- *  num_q_heads          Hq; num_kv_heads must divide it
+ *  num_q_heads          Hq; num_kv_heads must divide it, and the group size
+ *                       G = Hq / Hkv must be at most 4 or a multiple of 4
+ *                       (else PKV_ERR_UNSUPPORTED); the decode reads each K/V
+ *                       tile once per head group of min(G, 4) heads, or of 8
+ *                       heads when G is a multiple of 8
  *  num_kv_heads         Hkv
  *  head_dim             D, 64 or 128
  *  page_size            P, a power of two >= 16
