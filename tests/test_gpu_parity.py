@@ -362,3 +362,15 @@ def test_graph_capture_replay_matches_eager(fused):
         hk, hv = oracle.append_kv(hk, hv, batch.k_new, batch.v_new, ip, idx, lens, batch.P)
         expect = oracle.decode(batch.q, hk, hv, ip, idx, lens, batch.sm_scale, batch.P)
         compare(eager, expect, f"replay {rep}")
+
+
+def test_gqa8_ragged_lengths_full_size():
+    # Eight query heads per KV head (Hq 64, Hkv 8): head groups of eight, so
+    # every output pass of the workgroup merge and of the cross-workgroup merge
+    # runs twice; the ragged batch's lengths give merges across many workgroups.
+    say("G = 8 on the ragged lengths")
+    lens = cfg(3).seq_lens.copy()
+    batch = W.make_batch(name="g8_ragged", seed=31, B=16, Hq=64, Hkv=8, D=128, P=16,
+                         lengths=lens)
+    got = GpuRun(batch, make_desc(batch)).step()
+    compare(got, oracle_out(batch), "G=8 ragged lengths")
