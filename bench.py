@@ -66,8 +66,10 @@ def parse():
                     help="also time pkv_decode_tokens (token-major K/V): the ragged batch through "
                          "a page-size-1 token table, and one contiguous 32k-token request")
     ap.add_argument("--ceiling", action="store_true",
-                    help="also time a plain read-only launch over the decode call's byte count "
-                         "(the achievable read rate of one launch of that size)")
+                    help="(the read-only launch is timed by default; kept for old command lines)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the read-only launch over the decode call's byte count (the "
+                         "achievable read rate of one launch of that size), timed by default")
     ap.add_argument("--no-kernel-loop", action="store_true",
                     help="time only whole steps (skip the decode-only loop)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -468,7 +470,7 @@ def main():
         res["graph_compare"] = graph_cmp
     if args.tokens:
         res["tokens"] = bench_tokens(pkv, W, torch, dev, stream, K)
-    if args.ceiling:
+    if not args.no_ceiling and not args.no_kernel_loop:
         res["read_ceiling"] = bench_ceiling(pkv, torch, dev, stream, K, call_bytes)
     if args.layers > 0:
         res["layered_step"] = bench_layers(pkv, torch, stream, K, batch, desc, base, args.layers)
