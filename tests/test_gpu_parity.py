@@ -374,3 +374,32 @@ def test_gqa8_ragged_lengths_full_size():
                          lengths=lens)
     got = GpuRun(batch, make_desc(batch)).step()
     compare(got, oracle_out(batch), "G=8 ragged lengths")
+
+
+def test_two_streams_with_separate_workspaces():
+    # The library keeps no state of its own: two steps issued on two streams,
+    # each with its own workspace, metadata and output, may run concurrently
+    # and give bitwise the results each gives alone.
+    say("two streams, separate workspaces")
+    a = W.make_batch(name="s1", seed=41, B=8, Hq=32, Hkv=8, D=128, P=16,
+                     lengths=np.array([3000, 17, 900, 4096, 1, 640, 2048, 333]))
+    b = W.make_batch(name="s2", seed=42, B=5, Hq=8, Hkv=2, D=64, P=32,
+                     lengths=np.array([700, 64, 65, 1500, 9]))
+    ra, rb = GpuRun(a, make_desc(a)), GpuRun(b, make_desc(b))
+    alone_a, alone_b = ra.step().copy(), rb.step().copy()
+    for run in (ra, rb):
+        run.out.fill_(0x7FC0)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            ra.metadata()
+            ra.decode()
+        with torch.cuda.stream(sb):
+            rb.metadata()
+            rb.decode()
+    torch.cuda.synchronize()
+    assert np.array_equal(ra.out_bits(), alone_a)
+    assert np.array_equal(rb.out_bits(), alone_b)
+    compare(alone_a, oracle_out(a), "stream 1")
+    compare(alone_b, oracle_out(b), "stream 2")
