@@ -89,7 +89,12 @@ typedef enum pkv_status {
   PKV_ERR_DEVICE_DATA = 6           /* pkv_debug_validate found bad device metadata */
 } pkv_status;
 
-/* Static description of one message of pkv_status (never NULL). */
+/* Static description of one message of pkv_status (never NULL).  Errors are
+ * status codes, not exceptions: the pages' kernel wrappers raise a runtime
+ * error when a kernel is missing and a value error for an input they do not
+ * support (AstrAI compare v1.3.12..6f09b1d, attention_ops.py, _check_available;
+ * attention_backend.py, FlashAttnBackend.fwd_prefill); here the Python
+ * binding turns every status other than PKV_OK into an exception. */
 const char* pkv_status_str(int status);
 
 /* Library ABI version: (major << 16) | minor. */
@@ -141,7 +146,12 @@ typedef struct pkv_desc {
 /* Bytes of workspace a descriptor needs (split plan, partial outputs and
  * log-sum-exp values, error word), or 0 if the descriptor is invalid.  The
  * caller allocates it once (any device allocation, 256-byte aligned) and passes
- * it to every pkv_build_metadata / pkv_decode call of that descriptor.  Its
+ * it to every pkv_build_metadata / pkv_decode call of that descriptor: the
+ * pages moved the split partials into a workspace the executor allocates once,
+ * so the decode loop allocates nothing and every kernel address is stable for
+ * graph capture (AstrAI commit 05739629, astrai/inference: the
+ * InferenceWorkspace bullets on decode_o_part / decode_ml_part and zero
+ * allocation in the decode hot loop).  Its
  * contents need no initialisation: pkv_build_metadata writes everything the
  * decode reads.  The decode calls of a step reuse the plan and overwrite the
  * partials and arrival counters, so calls that share a workspace must run one
@@ -189,6 +199,34 @@ int pkv_build_metadata(const pkv_desc* desc, const int32_t* seq_lens, int32_t ba
 int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
                   const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
                   const int32_t* seq_lens, int32_t batch, void* stream);
+
+/* KV append of several new tokens per request (extend / chunked prefill),
+ * one launch: request b's n_b = qo_indptr[b+1] - qo_indptr[b] new tokens are
+ * its newest, positions seq_lens[b] - n_b .. seq_lens[b] - 1, and row
+ * qo_indptr[b] + i of k_new / v_new goes to position seq_lens[b] - n_b + i:
+ *   K[kv_indices[kv_indptr[b] + pos / P]][h][pos % P][:] = k_new[qo_indptr[b] + i][h][:]
+ * in the pool's tile layout, same for V.  On the pages the extend step stores
+ * every new token this way before the paged prefill (attention_backend.py,
+ * CudaBackend.fwd_prefill; cache.py, the KVCache docstring: out_cache_loc
+ * [batch, new_seq_len]; both on the compare page).
+ *  k_new, v_new   device bf16 [rows][num_kv_heads][head_dim], rows = qo_indptr[batch]
+ *  qo_indptr      device int32 [batch + 1], non-decreasing, qo_indptr[0] = 0
+ *                 (the same array pkv_prefill takes)
+ *  kv_indptr      device int32 [batch + 1] (from pkv_build_metadata)
+ *  kv_indices     device int32 [num_indices] (may be NULL when num_indices is 0)
+ *  seq_lens       device int32 [batch], lengths with the new tokens included
+ *  max_new_rows   host int: an upper bound of every n_b; it sizes the grid
+ *                 (rows beyond it are not written)
+ * Rows whose position would be negative (n_b > seq_lens[b]), page ids outside
+ * [0, num_pages) and index positions outside [0, num_indices) are skipped.
+ * Two rows must not target the same slot.  No allocation; capturable.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (head_dim other than 64 or
+ * 128), PKV_ERR_CAPACITY (batch * num_kv_heads * ceil(max_new_rows / 16) of
+ * 2^31 or more), PKV_ERR_LAUNCH. */
+int pkv_append_kv_ragged(const pkv_pool* pool, const void* k_new, const void* v_new,
+                         const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_indices, int32_t num_indices, const int32_t* seq_lens,
+                         int32_t batch, int32_t max_new_rows, void* stream);
 
 /* Decode attention for one layer (one kernel launch).
  *  q            device bf16 [batch][num_q_heads][head_dim], contiguous
@@ -303,7 +341,11 @@ int pkv_prefill(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                 int32_t causal, float sm_scale, void* out, void* stream);
 
 /* Debug only (synchronises the stream; not capturable).  Checks device
- * metadata and copies the plan to host memory.
+ * metadata and copies the plan to host memory.  The launch entry points do not
+ * read device data from the host (the pages keep host reads out of the decode
+ * step: KVCache carries the longest length as a host integer so that decode
+ * needs no device synchronisation, cache.py, the KVCache docstring on the
+ * compare page), so the checks they cannot make live here.
  *  groups_out   host int32 or NULL: workgroups the plan uses (W above)
  *  waves_out    host int32 [num_workgroups * PKV_WAVES_PER_WORKGROUP * 4] or
  *               NULL: for every wave of
@@ -311,8 +353,10 @@ int pkv_prefill(const pkv_pool* pool, const pkv_desc* desc, const void* q,
  *               (tiles = 0 for an idle wave)
  * Returns PKV_ERR_DEVICE_DATA if kv_indptr is not the page prefix sum of
  * seq_lens, any listed page id is outside [0, num_pages), kv_indptr[batch]
- * exceeds num_indices, or a kernel latched the device error word (which it
- * then clears). */
+ * exceeds num_indices, the plan in the workspace was built for another batch
+ * size or head grouping, or a kernel latched the device error word (which it
+ * then clears).  A decode given a workspace whose plan was built for another
+ * batch or head grouping writes no output and latches that word. */
 int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int32_t* kv_indptr,
                        const int32_t* kv_indices, int32_t num_indices, int32_t num_pages,
                        int32_t batch, void* workspace, size_t workspace_bytes,

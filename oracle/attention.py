@@ -33,7 +33,8 @@ the hunk or bullet, as the pages have no section numbers):
   chunk's normalised output and its log-sum-exp; the merge weights each chunk
   by exp(lse_s - max lse).
 * KV append: the token written this step goes to position seq_len - 1
-  (cache.py, bind_tasks: write_pos = seq_lens - 1).
+  (cache.py, bind_tasks: write_pos = seq_lens - 1); an extend step's n new
+  tokens go to positions seq_len - n .. seq_len - 1 (append_kv_rows).
 * Keep mask (decode_masked): token t of request b attends iff t < seq_len and
   the mask keeps it (the paged decode wrapper's optional 2-D bool mask).
 * Prefill / extend (prefill): n new query rows per request over its L keys,
@@ -82,6 +83,7 @@ __all__ = [
     "decode_split",
     "decode_pieces",
     "append_kv",
+    "append_kv_rows",
 ]
 
 
@@ -379,6 +381,35 @@ def append_kv(k_pool, v_pool, k_new, v_new, indptr, indices, seq_lens, P: int):
         page = int(indices[int(indptr[b]) + pos // P])
         k[page, :, pos % P, :] = k_new[b]
         v[page, :, pos % P, :] = v_new[b]
+    return k, v
+
+
+def append_kv_rows(k_pool, v_pool, k_rows, v_rows, qo_indptr, indptr, indices, seq_lens, P: int):
+    """Write every request's new tokens into the pool (returns new copies).
+
+    Request b brings n_b = qo_indptr[b+1] - qo_indptr[b] new tokens, rows
+    qo_indptr[b] .. qo_indptr[b+1] - 1 of k_rows / v_rows ([rows, Hkv, D]);
+    they are its newest tokens, positions seq_len - n_b .. seq_len - 1.  This
+    is the extend step's store of every new token before the paged prefill
+    (AstrAI compare v1.3.12..6f09b1d, attention_backend.py, CudaBackend.
+    fwd_prefill: k_buffer[layer_id, out_cache_loc] = k; cache.py, the KVCache
+    docstring: out_cache_loc [batch, new_seq_len], and bind_tasks, which takes
+    the write slots of positions start_pos .. seq_len - 1).  A row whose
+    position would fall before the request's first token writes nothing.
+    """
+    k = np.array(k_pool, copy=True)
+    v = np.array(v_pool, copy=True)
+    for b in range(len(seq_lens)):
+        L = int(seq_lens[b])
+        r0, r1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        n = r1 - r0
+        for i in range(n):
+            pos = L - n + i
+            if pos < 0:
+                continue
+            page = int(indices[int(indptr[b]) + pos // P])
+            k[page, :, pos % P, :] = k_rows[r0 + i]
+            v[page, :, pos % P, :] = v_rows[r0 + i]
     return k, v
 
 

@@ -33,6 +33,7 @@ __all__ = [
     "pkv_workspace_bytes",
     "pkv_build_metadata",
     "pkv_append_kv",
+    "pkv_append_kv_ragged",
     "pkv_decode",
     "pkv_decode_append",
     "pkv_decode_masked",
@@ -107,6 +108,8 @@ _SIGNATURES = {
                                           ctypes.c_size_t, _vp]),
     "pkv_append_kv": (ctypes.c_int, [ctypes.POINTER(_CPool), _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                      _vp]),
+    "pkv_append_kv_ragged": (ctypes.c_int, [ctypes.POINTER(_CPool), _vp, _vp, _vp, _vp, _vp, _i32,
+                                            _vp, _i32, _i32, _vp]),
     "pkv_decode": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp, _vp,
                                   _i32, _vp, _i32, ctypes.c_float, _vp, ctypes.c_size_t, _vp,
                                   _vp]),
@@ -262,6 +265,25 @@ def pkv_append_kv(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor, kv_indpt
         _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
         kv_indices.numel(), _ptr(seq_lens, "seq_lens", _I32), B, _stream(stream))
     _check("pkv_append_kv", st)
+
+
+def pkv_append_kv_ragged(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor,
+                         qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,
+                         kv_indices: torch.Tensor, seq_lens: torch.Tensor, max_new_rows: int,
+                         stream=None) -> None:
+    """Append each request's new tokens (rows qo_indptr[b] .. qo_indptr[b+1] of
+    k_new / v_new, [rows, Hkv, D]) at positions seq_len - n_b .. seq_len - 1."""
+    B = seq_lens.numel()
+    cp = pool.c()
+    per = cp.num_kv_heads * cp.head_dim
+    if k_new.numel() % per or v_new.numel() != k_new.numel():
+        raise ValueError("k_new and v_new must be [rows, num_kv_heads, head_dim]")
+    st = load_library().pkv_append_kv_ragged(
+        ctypes.byref(cp), _ptr(k_new, "k_new", _BF16), _ptr(v_new, "v_new", _BF16),
+        _ptr(qo_indptr, "qo_indptr", _I32, B + 1), _ptr(kv_indptr, "kv_indptr", _I32, B + 1),
+        _ptr(kv_indices, "kv_indices", _I32), kv_indices.numel(),
+        _ptr(seq_lens, "seq_lens", _I32), B, int(max_new_rows), _stream(stream))
+    _check("pkv_append_kv_ragged", st)
 
 
 def pkv_decode(pool: Pool, desc: Desc, q: torch.Tensor, kv_indptr: torch.Tensor,

@@ -109,7 +109,7 @@ const char* pkv_status_str(int status) {
   }
 }
 
-int32_t pkv_version(void) { return (2 << 16) | 4; }
+int32_t pkv_version(void) { return (2 << 16) | 5; }
 
 size_t pkv_workspace_bytes(const pkv_desc* desc) {
   WsLayout L;
@@ -155,7 +155,7 @@ int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
   // One thread per 8 channels of every K and V row; the kernel indexes in 32 bits.
   if ((long long)batch * pool->num_kv_heads * 2 * (pool->head_dim / 8) > 0x7fffffffLL)
     return PKV_ERR_INVALID_ARG;
-  AppendArgs a;
+  AppendArgs a{};
   a.k = static_cast<uint16_t*>(pool->k);
   a.v = static_cast<uint16_t*>(pool->v);
   a.k_new = static_cast<const uint16_t*>(k_new);
@@ -170,6 +170,40 @@ int pkv_append_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
   a.head_dim = pool->head_dim;
   a.batch = batch;
   return launch_status(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_append_kv_ragged(const pkv_pool* pool, const void* k_new, const void* v_new,
+                         const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_indices, int32_t num_indices, const int32_t* seq_lens,
+                         int32_t batch, int32_t max_new_rows, void* stream) {
+  int st = check_pool(pool, nullptr);
+  if (st != PKV_OK) return st;
+  if (!k_new || !v_new || !qo_indptr || !kv_indptr || (num_indices > 0 && !kv_indices) ||
+      !seq_lens || batch < 0 || num_indices < 0 || max_new_rows < 0 || pool->page_size < 1 ||
+      pool->num_kv_heads < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  const int row_blocks = (max_new_rows + 15) / 16;
+  // One workgroup per 16 rows of a (request, KV head); the grid is one dimension.
+  if ((long long)batch * pool->num_kv_heads * row_blocks > 0x7fffffffLL) return PKV_ERR_CAPACITY;
+  AppendArgs a{};
+  a.k = static_cast<uint16_t*>(pool->k);
+  a.v = static_cast<uint16_t*>(pool->v);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.seq_lens = seq_lens;
+  a.num_indices = num_indices;
+  a.num_pages = pool->num_pages;
+  a.page_size = pool->page_size;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.batch = batch;
+  a.qo_indptr = qo_indptr;
+  a.max_rows = max_new_rows;
+  a.row_blocks = row_blocks;
+  return launch_status(launch_append_rows(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
@@ -385,6 +419,9 @@ int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int3
   if (!ok) return PKV_ERR_LAUNCH;
 
   bool bad = hdr[kHdrError] != 0;
+  // The plan in the workspace must be this batch's, for this descriptor.
+  const int units = desc->num_q_heads / heads_per_group(desc->num_q_heads / desc->num_kv_heads);
+  if (hdr[kHdrBatch] != batch || hdr[kHdrUnits] != units) bad = true;
   long long acc = 0;
   if (ip[0] != 0) bad = true;
   for (int b = 0; b < batch; ++b) {

@@ -112,7 +112,6 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   constexpr bool MASKED = KIND == kMasked;
   constexpr bool TOKENS = KIND == kTokens;  // token-major K/V, 16-token blocks as pages
   constexpr int kStages = 2;  // register ring: steps in flight per wave
-  constexpr int kOut = (HG * D + kGroupThreads - 1) / kGroupThreads;  // outputs per thread
 
   // Pieces that leave a wave unfinished: slot 0 = the wave's first piece,
   // slot 1 = its last piece (every other piece is a whole segment).
@@ -141,8 +140,16 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // else from the plan.
   const int ngroups = a.hdr[kHdrGroups];
   const int nempty = a.hdr[kHdrEmpty];
+  // The plan must be the one built for this call's batch and head grouping:
+  // a plan of a larger batch would send waves to requests past the caller's
+  // arrays.  On a mismatch nothing is read or written but the error word.
+  const bool plan_ok = a.hdr[kHdrBatch] == a.batch && a.hdr[kHdrUnits] == a.units;
   const WaveRange rng = a.waves[grp * kWavesPerGroup + w];
   const GroupInfo gi0 = a.ginfo[grp];
+  if (!plan_ok) {  // uniform over the grid
+    if (grp == 0 && tid == 0) atomicOr(&a.hdr[kHdrError], (int)kErrPlanMismatch);
+    return;
+  }
   // Requests without tokens get zero rows (no tile covers them); workgroup 0
   // writes them, after its stream, or at once when the plan has no tile at all.
   auto zero_empty_rows = [&]() {

@@ -37,6 +37,7 @@ enum ErrorBit : int {
   kErrNegativeLength = 1,
   kErrBadPageId = 2,
   kErrBadIndexPos = 4,
+  kErrPlanMismatch = 8,  // a decode got a plan built for another batch or head grouping
 };
 
 // Range of one wave: tiles of request b, head group u, pages p, p+1, ... and
@@ -94,12 +95,16 @@ struct MetaArgs {
 struct AppendArgs {
   uint16_t* k;
   uint16_t* v;
-  const uint16_t* k_new;
+  const uint16_t* k_new;     // [batch][Hkv][D], or [rows][Hkv][D] with qo_indptr
   const uint16_t* v_new;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
   const int32_t* seq_lens;
   int32_t num_indices, num_pages, page_size, num_kv_heads, head_dim, batch;
+  // Several new tokens per request (extend): rows qo_indptr[b] .. qo_indptr[b+1]
+  // of k_new / v_new, at most max_rows per request, in blocks of 16 rows.
+  const int32_t* qo_indptr;
+  int32_t max_rows, row_blocks;
 };
 
 struct DecodeArgs {
@@ -150,6 +155,7 @@ struct PrefillArgs {
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, int groups,
                          hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int heads_per_group, int max_q_len,

@@ -299,6 +299,46 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   }
 }
 
+// Extend append: request b's n_b = qo_indptr[b+1] - qo_indptr[b] new rows go
+// to positions seq_len - n_b .. seq_len - 1.  A workgroup covers 16 rows of
+// one (request, KV head) with one thread per (row, 8-channel chunk), rows
+// fastest, so that the 16 rows' K chunks of one channel block (consecutive
+// tokens of a page: [c][t][8]) form one 256-byte run and their V values of
+// one channel (consecutive [c][t]) one 32-byte run.
+__global__ void __launch_bounds__(256) append_rows_kernel(AppendArgs a) {
+  const uint32_t nblk = (uint32_t)a.row_blocks;
+  const uint32_t bid = blockIdx.x;
+  const int blk = (int)(bid % nblk);
+  const int h = (int)((bid / nblk) % (uint32_t)a.num_kv_heads);
+  const int b = (int)(bid / nblk / (uint32_t)a.num_kv_heads);
+  const int i = blk * 16 + (int)(threadIdx.x & 15);  // row of request b
+  const int c = (int)(threadIdx.x >> 4);              // 8-channel chunk
+  const int r0 = a.qo_indptr[b];
+  const int n = a.qo_indptr[b + 1] - r0;
+  const int L = a.seq_lens[b];
+  const int ip = a.kv_indptr[b];
+  if (i >= n || i >= a.max_rows) return;
+  const int pos = L - n + i;
+  if (pos < 0) return;
+  const long long slot = (long long)ip + pos / a.page_size;
+  const bool slot_ok = slot >= 0 && slot < a.num_indices;
+  const int page = slot_ok ? a.kv_indices[slot] : -1;
+  if (page < 0 || page >= a.num_pages) return;
+  const size_t src = ((size_t)(r0 + i) * a.num_kv_heads + h) * a.head_dim + (size_t)c * 8;
+  const uint4 kw = *reinterpret_cast<const uint4*>(a.k_new + src);
+  const uint4 vw = *reinterpret_cast<const uint4*>(a.v_new + src);
+  const size_t tile = (((size_t)page * a.num_kv_heads + h) * a.page_size) * a.head_dim;
+  const int off = pos % a.page_size;
+  *reinterpret_cast<uint4*>(a.k + tile + ((size_t)c * a.page_size + off) * 8) = kw;
+  const uint32_t words[4] = {vw.x, vw.y, vw.z, vw.w};
+  uint16_t* col = a.v + tile + (size_t)c * 8 * a.page_size + off;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    col[(size_t)(2 * j) * a.page_size] = (uint16_t)(words[j] & 0xffffu);
+    col[(size_t)(2 * j + 1) * a.page_size] = (uint16_t)(words[j] >> 16);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
@@ -325,6 +365,18 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (threads == 0) return hipSuccess;
   const int blocks = (int)((threads + 255) / 256);
   hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv
+
+namespace pkv {
+
+hipError_t launch_append_rows(const AppendArgs& a, hipStream_t s) {
+  const long long blocks = (long long)a.batch * a.num_kv_heads * a.row_blocks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(append_rows_kernel, dim3((uint32_t)blocks), dim3(16 * (a.head_dim / 8)), 0, s,
+                     a);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def test_header_declares_expected_entry_points():
     names = pkv.declared_functions()
     assert set(names) == {
         "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
-        "pkv_append_kv", "pkv_decode", "pkv_decode_append", "pkv_decode_masked",
+        "pkv_append_kv", "pkv_append_kv_ragged", "pkv_decode", "pkv_decode_append", "pkv_decode_masked",
         "pkv_decode_tokens", "pkv_prefill", "pkv_debug_validate", "pkv_debug_read_ceiling"}
 
 
@@ -146,6 +146,16 @@ def test_host_checks_reject_before_launch(lib):
     # append with a head_dim that is not a multiple of 8 channels
     pool_odd = pkv._CPool(100, 16, 8, 60, 0x1000, 0x2000)
     assert _raw(lib, "pkv_append_kv", B(pool_odd), fake, fake, fake, fake, 10, fake, 4, None) == 2
+    # extend append: no query offsets, negative row bound, odd head_dim, a grid
+    # of 2^31 workgroups or more
+    assert _raw(lib, "pkv_append_kv_ragged", B(pool), fake, fake, None, fake, fake, 10, fake, 4,
+                8, None) == 1
+    assert _raw(lib, "pkv_append_kv_ragged", B(pool), fake, fake, fake, fake, fake, 10, fake, 4,
+                -1, None) == 1
+    assert _raw(lib, "pkv_append_kv_ragged", B(pool_odd), fake, fake, fake, fake, fake, 10, fake,
+                4, 8, None) == 2
+    assert _raw(lib, "pkv_append_kv_ragged", B(pool), fake, fake, fake, fake, fake, 10, fake,
+                65536, 1 << 20, None) == 4
 
 
 def test_binding_requires_gpu_tensors(lib):

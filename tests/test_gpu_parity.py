@@ -43,11 +43,31 @@ def _random_lengths_batch(seed, B, with_zeros):
                         lengths=L, poison=False)
 
 
-@pytest.mark.parametrize("case", ["c1", "c2", "c3", "c4", "c5", "rand0", "rand1", "rand_big"])
+# Plans away from four query heads per KV head and pages of 16 tokens:
+# (Hq, Hkv, P) -> head groups of G (G <= 4), of eight (G a multiple of 8, two
+# groups per KV head at G = 16) or of four (G = 12: three groups per KV head).
+PLAN_SHAPES = {
+    "g8": (64, 8, 16), "g3": (24, 8, 16), "g12": (48, 4, 16), "g1": (8, 8, 16),
+    "g16": (128, 8, 16), "g4_p32": (32, 8, 32), "g4_p64": (32, 8, 64), "g8_p64": (64, 8, 64),
+}
+
+
+def _shape_lengths_batch(case):
+    Hq, Hkv, P = PLAN_SHAPES[case]
+    rng = np.random.default_rng(sum(map(ord, case)))
+    L = rng.integers(0, 3000, size=29)
+    return W.make_batch(name=f"plan_{case}", seed=int(rng.integers(1 << 30)), B=29, Hq=Hq,
+                        Hkv=Hkv, D=64, P=P, lengths=L, poison=False)
+
+
+@pytest.mark.parametrize("case", ["c1", "c2", "c3", "c4", "c5", "rand0", "rand1", "rand_big"]
+                         + list(PLAN_SHAPES))
 @pytest.mark.parametrize("grid,forced", [(0, 0), (0, 3), (1000, 0)])
 def test_metadata_bit_exact(case, grid, forced):
     say(f"metadata case={case} grid={grid} forced={forced}")
-    if case.startswith("c"):
+    if case in PLAN_SHAPES:
+        batch = _shape_lengths_batch(case)
+    elif case.startswith("c"):
         batch = cfg(int(case[1]))
     elif case == "rand_big":
         batch = _random_lengths_batch(77, 1500, True)  # more requests than one block scans at once
@@ -95,6 +115,10 @@ FUSED_CASES = {  # name: (Hq, Hkv, D, P, lengths)
     "g4_p16": (8, 2, 64, 16, [1, 15, 16, 17, 40, 33]),
     "g8_p64": (32, 4, 128, 64, [100, 64, 65, 1, 300, 128]),
     "g1_p32": (8, 8, 128, 32, [31, 32, 33, 2, 257]),
+    # three head groups of four per KV head: only the first writes the token
+    "g12_p16": (48, 4, 128, 16, [1, 16, 17, 250, 47]),
+    # two head groups of eight per KV head
+    "g16_p32": (64, 4, 64, 32, [33, 1, 96, 500, 31]),
 }
 
 
@@ -225,7 +249,10 @@ def test_repeated_decodes_reuse_one_plan():
     (8, 8, 128, 16),   # G = 1
     (16, 8, 128, 16),  # G = 2
     (24, 8, 64, 16),   # G = 3
-    (64, 8, 128, 16),  # G = 8: two waves per KV head
+    (64, 8, 128, 16),  # G = 8: one head group of eight per KV head
+    (48, 4, 128, 16),  # G = 12: three head groups of four per KV head
+    (128, 8, 64, 16),  # G = 16: two head groups of eight per KV head
+    (96, 8, 128, 32),  # G = 12 with pages of 32
     (32, 4, 64, 32),   # two rounds per page at D = 64
     (8, 2, 128, 32),   # four rounds per page at D = 128
     (8, 2, 128, 64),   # eight rounds per page
@@ -403,3 +430,25 @@ def test_two_streams_with_separate_workspaces():
     assert np.array_equal(rb.out_bits(), alone_b)
     compare(alone_a, oracle_out(a), "stream 1")
     compare(alone_b, oracle_out(b), "stream 2")
+
+
+def test_plan_of_another_batch_is_refused():
+    # A decode whose workspace holds the plan of a different batch must not
+    # follow it (its ranges may name requests past this call's arrays): the
+    # kernel writes nothing and latches the error word, which validate reports.
+    say("plan mismatch")
+    batch = W.make_batch(name="mismatch", seed=12, B=6, Hq=32, Hkv=8, D=128, P=16,
+                         lengths=np.array([900, 17, 3000, 1, 64, 2500]))
+    run = GpuRun(batch, make_desc(batch))
+    run.metadata()
+    short = batch.B - 1
+    out = torch.full((short, batch.Hq, batch.D), 0x7FC0, dtype=torch.int16, device="cuda:0")
+    pkv.pkv_decode(run.pool, run.desc, run.t["q"][:short], run.kv_indptr[: short + 1],
+                   run.t["kv_indices"], run.t["seq_lens"][:short], batch.sm_scale, run.ws, out)
+    torch.cuda.synchronize()
+    assert (out == 0x7FC0).all(), "the decode wrote output under a plan of another batch"
+    assert run.validate()["status"] == pkv.PKV_ERR_DEVICE_DATA
+    # validate cleared the error word; a new plan for this batch decodes normally
+    got = run.step()
+    assert run.validate()["status"] == pkv.PKV_OK
+    compare(got, oracle_out(batch), "after mismatch")

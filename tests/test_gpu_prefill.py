@@ -28,7 +28,8 @@ CASES = {
 }
 
 
-def run_prefill(batch, causal, max_q_len=None, seq_lens=None, edit=None):
+def run_prefill(batch, causal, max_q_len=None, seq_lens=None, edit=None, pools_out=None):
+    """Metadata + (for a batch with new K/V rows) pkv_append_kv_ragged + prefill."""
     dev = "cuda:0"
     t = W.to_device(batch, dev)
     if edit is not None:  # change the device inputs (e.g. corrupt a page id)
@@ -42,17 +43,34 @@ def run_prefill(batch, causal, max_q_len=None, seq_lens=None, edit=None):
     pkv.pkv_build_metadata(desc, t["seq_lens"], 0, kv_indptr, ws)
     out = torch.full(tuple(batch.q_rows.shape), 0x7FC0, dtype=torch.int16, device=dev)
     q_lens = np.diff(batch.qo_indptr)
+    if batch.k_rows is not None:  # the new tokens reach the pool through the library
+        pkv.pkv_append_kv_ragged(pkv.Pool(t["k_pool"], t["v_pool"]), t["k_rows"], t["v_rows"],
+                                 t["qo_indptr"], kv_indptr, t["kv_indices"], t["seq_lens"],
+                                 int(q_lens.max()))
     pkv.pkv_prefill(pkv.Pool(t["k_pool"], t["v_pool"]), desc, t["q_rows"], t["qo_indptr"],
                     kv_indptr, t["kv_indices"], t["seq_lens"],
                     int(q_lens.max()) if max_q_len is None else max_q_len, causal,
                     batch.sm_scale, out)
     torch.cuda.synchronize()
+    if pools_out is not None:
+        pools_out.append((W.k_pool_token_major(t["k_pool"].cpu().numpy().view(np.uint16)),
+                          W.v_pool_token_major(t["v_pool"].cpu().numpy().view(np.uint16))))
     return out.cpu().numpy().view(np.uint16)
+
+
+def oracle_pools(batch):
+    """The pool after the batch's new K/V rows are written (unchanged without them)."""
+    if batch.k_rows is None:
+        return batch.k_pool, batch.v_pool
+    ip = oracle.kv_indptr(batch.seq_lens, batch.P)
+    return oracle.append_kv_rows(batch.k_pool, batch.v_pool, batch.k_rows, batch.v_rows,
+                                 batch.qo_indptr, ip, batch.kv_indices, batch.seq_lens, batch.P)
 
 
 def oracle_prefill(batch, causal):
     ip = oracle.kv_indptr(batch.seq_lens, batch.P)
-    return oracle.prefill(batch.q_rows, batch.k_pool, batch.v_pool, ip, batch.kv_indices,
+    k, v = oracle_pools(batch)
+    return oracle.prefill(batch.q_rows, k, v, ip, batch.kv_indices,
                           batch.seq_lens, batch.qo_indptr, batch.sm_scale, batch.P, causal)
 
 
@@ -79,17 +97,78 @@ def test_prefill_single_rows_match_decode_semantics():
 
 def test_prefill_ragged_extend_batch():
     # Many requests of a serving step's extend phase: ragged new-token counts
-    # (zero included) over ragged cached prefixes, G = 4, D = 128.
+    # (zero included) over ragged cached prefixes, G = 4, D = 128.  The new
+    # tokens' K/V start outside the pool (their slots hold NaN) and are written
+    # by pkv_append_kv_ragged before the prefill, as in a serving step.
     rng = np.random.default_rng(np.random.PCG64(61))
     q_lens = rng.integers(0, 41, size=24)
     q_lens[[3, 17]] = 0
     prefix = rng.integers(0, 301, size=24)
     say(f"prefill ragged extend: {int(q_lens.sum())} rows, {int((q_lens + prefix).sum())} keys")
     batch = W.make_prefill(name="extend24", seed=61, Hq=32, Hkv=8, D=128, P=16,
-                           q_lens=q_lens, prefix_lens=prefix)
+                           q_lens=q_lens, prefix_lens=prefix, new_rows=True)
+    k_ref, v_ref = oracle_pools(batch)
     for causal in (True, False):
-        got = run_prefill(batch, causal)
+        pools = []
+        got = run_prefill(batch, causal, pools_out=pools)
+        assert np.array_equal(pools[0][0], k_ref) and np.array_equal(pools[0][1], v_ref)
         compare(got, oracle_prefill(batch, causal), f"ragged extend causal={causal}")
+
+
+APPEND_ROWS_CASES = [  # (D, P, new rows per request, prefix per request)
+    (128, 16, [0, 1, 15, 16, 17, 300], [5, 0, 16, 1, 31, 40]),
+    (64, 16, [300, 17, 1, 0], [0, 3, 64, 9]),
+    (128, 32, [1, 15, 16, 17, 300, 0], [31, 0, 1, 63, 7, 12]),
+    (64, 64, [17, 300, 0, 16, 1, 15], [64, 1, 5, 0, 127, 200]),
+    (128, 64, [300, 1], [70, 0]),
+]
+
+
+@pytest.mark.parametrize("D,P,q_lens,prefix", APPEND_ROWS_CASES,
+                         ids=[f"d{c[0]}_p{c[1]}" for c in APPEND_ROWS_CASES])
+def test_append_rows_bit_exact(D, P, q_lens, prefix):
+    # pkv_append_kv_ragged writes every new row into the tile layout at
+    # positions seq_len - n .. seq_len - 1: pool bytes equal the oracle's.
+    say(f"append rows D={D} P={P} n={q_lens}")
+    batch = W.make_prefill(name=f"rows_d{D}_p{P}", seed=D + P + sum(q_lens), Hq=8, Hkv=2, D=D,
+                           P=P, q_lens=q_lens, prefix_lens=prefix, new_rows=True)
+    dev = "cuda:0"
+    t = W.to_device(batch, dev)
+    kv_indptr = torch.from_numpy(oracle.kv_indptr(batch.seq_lens, P).astype(np.int32)).to(dev)
+    pool = pkv.Pool(t["k_pool"], t["v_pool"])
+    pkv.pkv_append_kv_ragged(pool, t["k_rows"], t["v_rows"], t["qo_indptr"], kv_indptr,
+                             t["kv_indices"], t["seq_lens"], max(q_lens))
+    torch.cuda.synchronize()
+    k_ref, v_ref = oracle_pools(batch)
+    k = W.k_pool_token_major(t["k_pool"].cpu().numpy().view(np.uint16))
+    v = W.v_pool_token_major(t["v_pool"].cpu().numpy().view(np.uint16))
+    assert np.array_equal(k, k_ref)
+    assert np.array_equal(v, v_ref)
+    # a bound below the longest request writes exactly its first rows
+    t2 = W.to_device(batch, dev)
+    cut = 16
+    pkv.pkv_append_kv_ragged(pkv.Pool(t2["k_pool"], t2["v_pool"]), t2["k_rows"], t2["v_rows"],
+                             t2["qo_indptr"], kv_indptr, t2["kv_indices"], t2["seq_lens"], cut)
+    torch.cuda.synchronize()
+    qo = batch.qo_indptr
+    keep_rows = np.concatenate([np.arange(qo[b], qo[b] + min(cut, qo[b + 1] - qo[b]))
+                                for b in range(batch.B)]).astype(np.int64)
+    # expected: rows past the bound keep their pool contents
+    k_exp, v_exp = batch.k_pool.copy(), batch.v_pool.copy()
+    kr, vr = batch.k_rows.copy(), batch.v_rows.copy()
+    drop = np.setdiff1d(np.arange(int(qo[-1])), keep_rows)
+    ip_h = oracle.kv_indptr(batch.seq_lens, P)
+    k_all, v_all = oracle.append_kv_rows(k_exp, v_exp, kr, vr, qo, ip_h, batch.kv_indices,
+                                         batch.seq_lens, P)
+    for r in drop:  # restore the slots of the rows the bound leaves out
+        b = int(np.searchsorted(qo, r, side="right") - 1)
+        n = int(qo[b + 1] - qo[b])
+        pos = int(batch.seq_lens[b]) - n + int(r - qo[b])
+        page = int(batch.page_lists[b][pos // P])
+        k_all[page, :, pos % P] = batch.k_pool[page, :, pos % P]
+        v_all[page, :, pos % P] = batch.v_pool[page, :, pos % P]
+    assert np.array_equal(W.k_pool_token_major(t2["k_pool"].cpu().numpy().view(np.uint16)), k_all)
+    assert np.array_equal(W.v_pool_token_major(t2["v_pool"].cpu().numpy().view(np.uint16)), v_all)
 
 
 def test_prefill_rows_without_keys_are_zero():

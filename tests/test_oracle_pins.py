@@ -318,6 +318,36 @@ def pin_plan(mod):
         assert covered == tiles
 
 
+def pin_head_groups(mod):
+    """The decode plan's head grouping (a rule of this library's plan; the pages
+    only say that the query heads of one KV head read its K/V together).
+
+    Three independent statements of it: the table of head-group sizes for
+    G = 1 .. 16 that the library header documents (the whole group up to four
+    heads, eight when G is a multiple of eight, else four); the same sizes
+    found by search, as the largest head-group size the kernels are built for
+    (1, 2, 3, 4, 8) that divides G; and the structure every grouping must have
+    (a group lies inside one KV head, and the groups cover the query heads
+    exactly once)."""
+    table = {1: 1, 2: 2, 3: 3, 4: 4, 8: 8, 12: 4, 16: 8}
+    for G, hg in table.items():
+        for Hkv in (1, 2, 8):
+            assert mod.head_groups(G * Hkv, Hkv) == (hg, G * Hkv // hg), (G, Hkv)
+    built = (1, 2, 3, 4, 8)
+    for G in [g for g in range(1, 65) if g <= 4 or g % 4 == 0]:
+        for Hkv in (1, 3, 8):
+            Hq = G * Hkv
+            HG, U = mod.head_groups(Hq, Hkv)
+            assert HG == max(h for h in built if G % h == 0), (G, Hkv, HG)
+            assert HG * U == Hq
+            heads = []
+            for u in range(U):
+                grp = list(range(u * HG, (u + 1) * HG))
+                assert len({mod.kv_head_of(h, G) for h in grp}) == 1, (G, u)
+                heads.extend(grp)
+            assert heads == list(range(Hq))
+
+
 def pin_stream_pieces(mod):
     """The plan's pieces merge to the unsplit result for many grid sizes."""
     for batch in (tiny_batch(), gqa8_batch(), W.config(1)):
@@ -352,6 +382,55 @@ def pin_append(mod):
     out = mod.decode(batch.q, k2, v2, ip, batch.kv_indices, batch.seq_lens,
                      batch.sm_scale, batch.P)
     assert np.isfinite(out).all()
+
+
+def pin_append_rows(mod):
+    """The extend append: byte-level slots found by walking page lists, one
+    token per request equals the single-token append, n tokens equal n
+    single-token appends at growing lengths, and the written batch reads no
+    poison."""
+    batch = prefill_batch(seed=35, q_lens=(0, 1, 4, 5, 9, 3), prefix_lens=(6, 0, 3, 4, 0, 1),
+                          new_rows=True)
+    ip = mod.kv_indptr(batch.seq_lens, batch.P)
+    k2, v2 = mod.append_kv_rows(batch.k_pool, batch.v_pool, batch.k_rows, batch.v_rows,
+                                batch.qo_indptr, ip, batch.kv_indices, batch.seq_lens, batch.P)
+    changed = np.zeros((batch.num_pages, batch.P), bool)
+    for b in range(batch.B):
+        q0, q1 = int(batch.qo_indptr[b]), int(batch.qo_indptr[b + 1])
+        slots = _token_slots(batch, b)
+        for i, (p, o) in enumerate(slots[len(slots) - (q1 - q0):]):
+            assert np.array_equal(k2[p, :, o], batch.k_rows[q0 + i])
+            assert np.array_equal(v2[p, :, o], batch.v_rows[q0 + i])
+            changed[p, o] = True
+    keep = np.broadcast_to(~changed[:, None, :, None], k2.shape)
+    assert np.array_equal(k2[keep], batch.k_pool[keep])
+    assert np.array_equal(v2[keep], batch.v_pool[keep])
+    # every new slot written: the causal prefill over the batch reads no poison
+    out = mod.prefill(batch.q_rows, k2, v2, ip, batch.kv_indices, batch.seq_lens,
+                      batch.qo_indptr, batch.sm_scale, batch.P, True)
+    assert np.isfinite(out).all()
+    # n new tokens = n single-token appends, the length growing by one each time
+    kk, vv = batch.k_pool, batch.v_pool
+    nmax = int(np.max(np.diff(batch.qo_indptr)))
+    for j in range(nmax):
+        sl = batch.seq_lens.copy()
+        sel = []
+        for b in range(batch.B):
+            n = int(batch.qo_indptr[b + 1] - batch.qo_indptr[b])
+            # request b's j-th new token, at length seq_len - n + j + 1; none past n
+            sl[b] = sl[b] - n + j + 1 if j < n else 0
+            sel.append(int(batch.qo_indptr[b]) + min(j, max(n - 1, 0)))
+        kk, vv = mod.append_kv(kk, vv, batch.k_rows[sel], batch.v_rows[sel], ip,
+                               batch.kv_indices, sl, batch.P)
+    assert np.array_equal(kk, k2) and np.array_equal(vv, v2)
+    # one new token per request: exactly the single-token append
+    one = prefill_batch(seed=36, q_lens=(1, 1, 1, 1), prefix_lens=(0, 4, 7, 15), new_rows=True)
+    ip1 = mod.kv_indptr(one.seq_lens, one.P)
+    a = mod.append_kv_rows(one.k_pool, one.v_pool, one.k_rows, one.v_rows, one.qo_indptr, ip1,
+                           one.kv_indices, one.seq_lens, one.P)
+    b_ = mod.append_kv(one.k_pool, one.v_pool, one.k_rows, one.v_rows, ip1, one.kv_indices,
+                       one.seq_lens, one.P)
+    assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1])
 
 
 # ------------------------------------------------------------ poison (pin 9)
@@ -569,7 +648,8 @@ def pin_tokens(mod):
 
 
 PINS = [pin_brute_force, pin_seq_len_one, pin_permutation, pin_split_invariance, pin_q_zero,
-        pin_constant_v, pin_dominant_key, pin_sdpa, pin_kv_indptr, pin_plan, pin_stream_pieces,
+        pin_constant_v, pin_dominant_key, pin_sdpa, pin_kv_indptr, pin_plan, pin_head_groups,
+        pin_stream_pieces, pin_append_rows,
         pin_append, pin_poison, pin_mask, pin_prefill, pin_tokens]
 
 
@@ -645,6 +725,31 @@ def _mutants():
         r[-1] = (r[-1][0], max(r[-1][0], n - 1))
         return r
     m["ranges_drop_last_page"] = {"even_page_ranges": ranges_drop_last_page}
+
+    # the grouping before groups of eight existed: four heads whenever G > 4
+    m["head_groups_four_at_g8"] = {
+        "head_groups": lambda Hq, Hkv: ((Hq // Hkv if Hq // Hkv <= 4 else 4),
+                                        Hq // (Hq // Hkv if Hq // Hkv <= 4 else 4))}
+    # groups of eight for any G above four (splits a KV head's heads at G = 12)
+    m["head_groups_eight_above_four"] = {
+        "head_groups": lambda Hq, Hkv: ((Hq // Hkv if Hq // Hkv <= 4 else 8),
+                                        Hq // (Hq // Hkv if Hq // Hkv <= 4 else 8))}
+
+    def rows_reversed(k_pool, v_pool, k_rows, v_rows, qo, indptr, indices, seq_lens, P):
+        k_r, v_r = np.array(k_rows), np.array(v_rows)
+        for b in range(len(seq_lens)):
+            k_r[qo[b]:qo[b + 1]] = k_r[qo[b]:qo[b + 1]][::-1]
+            v_r[qo[b]:qo[b + 1]] = v_r[qo[b]:qo[b + 1]][::-1]
+        return OA.__dict__["_orig_append_kv_rows"](k_pool, v_pool, k_r, v_r, qo, indptr, indices,
+                                                    seq_lens, P)
+    m["append_rows_reversed"] = {"append_kv_rows": rows_reversed}
+
+    def rows_from_prefix_end(k_pool, v_pool, k_rows, v_rows, qo, indptr, indices, seq_lens, P):
+        # a plausible slip: new tokens placed right after a prefix of seq_len - n - 1
+        sl = np.maximum(np.asarray(seq_lens) - 1, 0)
+        return OA.__dict__["_orig_append_kv_rows"](k_pool, v_pool, k_rows, v_rows, qo, indptr,
+                                                    indices, sl, P)
+    m["append_rows_one_early"] = {"append_kv_rows": rows_from_prefix_end}
 
     m["page_count_floor"] = {"page_counts": lambda L, P: np.asarray(L, np.int64) // P}
 
@@ -741,6 +846,7 @@ MUTANTS = _mutants()
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistakes(name, monkeypatch):
     for fn in ("softmax_attend", "chunk_partial", "plan_stream", "decode_pieces", "append_kv",
+               "append_kv_rows",
                "decode_masked", "prefill", "decode_tokens"):
         monkeypatch.setitem(OA.__dict__, "_orig_" + fn, getattr(OA, fn))
     for attr, repl in MUTANTS[name].items():

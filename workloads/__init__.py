@@ -117,6 +117,10 @@ class DecodeBatch:
     # Prefill batches: query rows of every request, flattened, and their offsets.
     q_rows: Optional[np.ndarray] = None  # uint16 [total_q, Hq, D]
     qo_indptr: Optional[np.ndarray] = None  # int32 [B + 1]
+    # Extend batches whose new tokens are not in the pool yet: their K/V rows,
+    # one per query row, and the pool slots of those tokens hold poison.
+    k_rows: Optional[np.ndarray] = None  # uint16 [total_q, Hkv, D]
+    v_rows: Optional[np.ndarray] = None  # uint16 [total_q, Hkv, D]
 
     @property
     def kv_indices(self) -> np.ndarray:
@@ -157,6 +161,8 @@ def _poison(batch: DecodeBatch) -> None:
     written = np.zeros((batch.num_pages, P), dtype=bool)
     for b in range(batch.B):
         filled = int(batch.seq_lens[b]) - (1 if batch.append else 0)
+        if batch.k_rows is not None:  # the new tokens of an extend batch come later
+            filled = int(batch.seq_lens[b]) - int(batch.qo_indptr[b + 1] - batch.qo_indptr[b])
         pages = batch.page_lists[b]
         for j, page in enumerate(pages):
             ntok = min(P, filled - j * P)
@@ -228,21 +234,30 @@ def make_batch(
 
 
 def make_prefill(*, name: str, seed: int, Hq: int, Hkv: int, D: int, P: int, q_lens,
-                 prefix_lens, poison: bool = True, q_scale: float = 1.0) -> DecodeBatch:
+                 prefix_lens, poison: bool = True, q_scale: float = 1.0,
+                 new_rows: bool = False) -> DecodeBatch:
     """Prefill / extend batch: request b has prefix_lens[b] cached tokens and
-    q_lens[b] new ones, whose K/V are already in the pool (seq_len = prefix +
-    q_len); its q_lens[b] query rows are stored flattened in ``q_rows`` with
-    offsets ``qo_indptr``.  Draw order: pool layout and contents as in
-    make_batch, then the query rows."""
+    q_lens[b] new ones (seq_len = prefix + q_len); its q_lens[b] query rows are
+    stored flattened in ``q_rows`` with offsets ``qo_indptr``.  By default the
+    new tokens' K/V are already in the pool.  With ``new_rows`` they are drawn
+    as ``k_rows`` / ``v_rows`` (one row per query row) for an append to write,
+    and their pool slots hold poison like any unwritten slot.  Draw order: pool
+    layout and contents as in make_batch, the query rows, then k_rows and
+    v_rows."""
     rng = np.random.default_rng(np.random.PCG64(seed))
     ql = np.asarray(q_lens, dtype=np.int64)
     pl = np.asarray(prefix_lens, dtype=np.int64)
     batch = make_batch(name=name, seed=seed, B=ql.size, Hq=Hq, Hkv=Hkv, D=D, P=P,
-                       lengths=pl + ql, poison=poison, rng=rng)
+                       lengths=pl + ql, poison=False, rng=rng)
     offsets = np.zeros(ql.size + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(ql)
     batch.qo_indptr = offsets
     batch.q_rows = normal_bf16(rng, (int(offsets[-1]), Hq, D), q_scale)
+    if new_rows:
+        batch.k_rows = normal_bf16(rng, (int(offsets[-1]), Hkv, D))
+        batch.v_rows = normal_bf16(rng, (int(offsets[-1]), Hkv, D))
+    if poison:
+        _poison(batch)
     return batch
 
 
@@ -428,6 +443,9 @@ def to_device(batch: DecodeBatch, device="cuda:0") -> dict:
     if batch.q_rows is not None:
         d["q_rows"] = bits(batch.q_rows)
         d["qo_indptr"] = torch.from_numpy(batch.qo_indptr.astype(np.int32)).to(device)
+    if batch.k_rows is not None:
+        d["k_rows"] = bits(batch.k_rows)
+        d["v_rows"] = bits(batch.v_rows)
     return d
 
 
