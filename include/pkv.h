@@ -86,7 +86,9 @@ typedef enum pkv_status {
   PKV_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below pkv_workspace_bytes(desc) */
   PKV_ERR_CAPACITY = 4,             /* batch or forced split count above the descriptor's capacity */
   PKV_ERR_LAUNCH = 5,               /* the HIP runtime rejected a kernel launch */
-  PKV_ERR_DEVICE_DATA = 6           /* pkv_debug_validate found bad device metadata */
+  PKV_ERR_DEVICE_DATA = 6,          /* pkv_debug_validate found bad device metadata */
+  PKV_ERR_SCRATCH_TOO_SMALL = 7     /* pkv_decode_scratch: the descriptor's workspace exceeds
+                                       PKV_SCRATCH_BYTES */
 } pkv_status;
 
 /* Static description of one message of pkv_status (never NULL).  Errors are
@@ -361,6 +363,25 @@ int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int3
                        const int32_t* kv_indices, int32_t num_indices, int32_t num_pages,
                        int32_t batch, void* workspace, size_t workspace_bytes,
                        int32_t* groups_out, int32_t* waves_out, void* stream);
+
+/* Decode without a caller workspace, for callers that cannot allocate device
+ * memory: code under hipGraph capture, tight serving loops, harnesses that
+ * forbid allocation.  The same result as pkv_build_metadata(desc, seq_lens,
+ * batch, 0, kv_indptr, ws, ...) followed by pkv_decode(..., ws, ...) (two
+ * launches), with ws a static device array of PKV_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  Every call on
+ * a GPU shares that GPU's array and rewrites all of it that it reads, so calls
+ * that overlap on one GPU (other streams, other host threads) race; calls in
+ * one stream are safe.  Nothing is allocated (no hipMalloc / hipFree); the
+ * first call with a device current looks up that device's array address.
+ *  kv_indptr    device int32 [batch + 1], written (the step's page prefix sums)
+ * Every other argument is as for pkv_build_metadata and pkv_decode.  Errors:
+ * those of pkv_build_metadata and pkv_decode, and PKV_ERR_SCRATCH_TOO_SMALL when
+ * pkv_workspace_bytes(desc) exceeds PKV_SCRATCH_BYTES. */
+#define PKV_SCRATCH_BYTES 8388608 /* 8 MiB */
+int pkv_decode_scratch(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                       const int32_t* seq_lens, const int32_t* kv_indices, int32_t num_indices,
+                       int32_t batch, float sm_scale, int32_t* kv_indptr, void* out, void* stream);
 
 /* Diagnostic, not part of the attention path: one launch that reads `bytes`
  * of device memory at src (16-byte aligned, a multiple of 16) with the decode

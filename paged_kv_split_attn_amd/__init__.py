@@ -39,9 +39,11 @@ __all__ = [
     "pkv_decode_masked",
     "pkv_decode_tokens",
     "pkv_prefill",
+    "pkv_decode_scratch",
     "pkv_debug_validate",
     "pkv_debug_read_ceiling",
     "WAVES_PER_GROUP",
+    "SCRATCH_BYTES",
     "PKV_OK",
     "PKV_ERR_INVALID_ARG",
     "PKV_ERR_UNSUPPORTED",
@@ -49,6 +51,7 @@ __all__ = [
     "PKV_ERR_CAPACITY",
     "PKV_ERR_LAUNCH",
     "PKV_ERR_DEVICE_DATA",
+    "PKV_ERR_SCRATCH_TOO_SMALL",
 ]
 
 PKV_OK = 0
@@ -58,6 +61,7 @@ PKV_ERR_WORKSPACE_TOO_SMALL = 3
 PKV_ERR_CAPACITY = 4
 PKV_ERR_LAUNCH = 5
 PKV_ERR_DEVICE_DATA = 6
+PKV_ERR_SCRATCH_TOO_SMALL = 7
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "pkv.h")
 
@@ -124,6 +128,8 @@ _SIGNATURES = {
                                          _vp, _vp]),
     "pkv_prefill": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp, _vp,
                                    _vp, _i32, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp]),
+    "pkv_decode_scratch": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp,
+                                          _vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp]),
     "pkv_debug_read_ceiling": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _vp]),
     "pkv_debug_validate": (ctypes.c_int, [ctypes.POINTER(_CDesc), _vp, _vp, _vp, _i32, _i32, _i32,
                                           _vp, ctypes.c_size_t, _i32p, _i32p, _vp]),
@@ -377,6 +383,21 @@ def pkv_prefill(pool: Pool, desc: Desc, q: torch.Tensor, qo_indptr: torch.Tensor
     _check("pkv_prefill", st)
 
 
+def pkv_decode_scratch(pool: Pool, desc: Desc, q: torch.Tensor, seq_lens: torch.Tensor,
+                       kv_indices: torch.Tensor, sm_scale: float, kv_indptr: torch.Tensor,
+                       out: torch.Tensor, stream=None) -> None:
+    """pkv_build_metadata + pkv_decode with the library's static scratch as the
+    workspace (no workspace argument, nothing allocated); writes kv_indptr."""
+    B = seq_lens.numel()
+    n = B * desc.num_q_heads * desc.head_dim
+    st = load_library().pkv_decode_scratch(
+        ctypes.byref(pool.c()), ctypes.byref(desc.c()), _ptr(q, "q", _BF16, n),
+        _ptr(seq_lens, "seq_lens", _I32), _ptr(kv_indices, "kv_indices", _I32),
+        kv_indices.numel(), B, float(sm_scale), _ptr(kv_indptr, "kv_indptr", _I32, B + 1),
+        _ptr(out, "out", _BF16, n), _stream(stream))
+    _check("pkv_decode_scratch", st)
+
+
 def pkv_debug_validate(desc: Desc, seq_lens: torch.Tensor, kv_indptr: torch.Tensor,
                        kv_indices: torch.Tensor, num_pages: int, workspace: torch.Tensor,
                        stream=None) -> dict:
@@ -402,6 +423,7 @@ def pkv_debug_validate(desc: Desc, seq_lens: torch.Tensor, kv_indptr: torch.Tens
 
 
 READ_CEILING_GROUPS = _header_define("PKV_READ_CEILING_GROUPS")
+SCRATCH_BYTES = _header_define("PKV_SCRATCH_BYTES")  # static scratch of pkv_decode_scratch
 
 
 def pkv_debug_read_ceiling(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

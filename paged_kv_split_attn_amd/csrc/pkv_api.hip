@@ -3,6 +3,7 @@
 // except pkv_debug_validate, which is documented as syncing.
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "pkv_internal.h"
@@ -105,6 +106,8 @@ const char* pkv_status_str(int status) {
     case PKV_ERR_CAPACITY: return "batch above the descriptor's capacity";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_DEVICE_DATA: return "invalid device metadata";
+    case PKV_ERR_SCRATCH_TOO_SMALL:
+      return "the descriptor needs more workspace than the library's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -451,3 +454,59 @@ int pkv_debug_validate(const pkv_desc* desc, const int32_t* seq_lens, const int3
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate (code
+// under graph capture, tight serving loops, harnesses that forbid it).  The
+// plan, partials and counters live in `scratch`, a file-scope device array of
+// PKV_SCRATCH_BYTES that every GPU the library runs on holds until the process
+// ends.  In host code the array's name is only a stand-in for its symbol: its
+// device address is looked up once per device with hipGetSymbolAddress and
+// that address, never the name, is what the kernels receive.
+
+static __device__ __align__(256) unsigned char scratch[PKV_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's copy of `scratch` (looked up on the first
+// call made with that device current).  Returns PKV_OK or an error status.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_LAUNCH;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PKV_ERR_LAUNCH;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_decode_scratch(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                                  const int32_t* seq_lens, const int32_t* kv_indices,
+                                  int32_t num_indices, int32_t batch, float sm_scale,
+                                  int32_t* kv_indptr, void* out, void* stream) {
+  WsLayout L;
+  int st = check_desc(desc, &L);
+  if (st != PKV_OK) return st;
+  st = check_pool(pool, desc);
+  if (st != PKV_OK) return st;
+  if (!q || !seq_lens || (num_indices > 0 && !kv_indices) || !kv_indptr || !out || batch < 0 ||
+      num_indices < 0 || !(sm_scale == sm_scale))
+    return PKV_ERR_INVALID_ARG;
+  if (batch > desc->max_batch) return PKV_ERR_CAPACITY;
+  if (L.total > (size_t)PKV_SCRATCH_BYTES) return PKV_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != PKV_OK) return st;
+  st = pkv_build_metadata(desc, seq_lens, batch, 0, kv_indptr, ws, L.total, stream);
+  if (st != PKV_OK) return st;
+  return pkv_decode(pool, desc, q, kv_indptr, kv_indices, num_indices, seq_lens, batch, sm_scale,
+                    ws, L.total, out, stream);
+}

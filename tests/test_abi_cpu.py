@@ -25,7 +25,7 @@ def test_header_declares_expected_entry_points():
     assert set(names) == {
         "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
         "pkv_append_kv", "pkv_append_kv_ragged", "pkv_decode", "pkv_decode_append", "pkv_decode_masked",
-        "pkv_decode_tokens", "pkv_prefill", "pkv_debug_validate", "pkv_debug_read_ceiling"}
+        "pkv_decode_tokens", "pkv_prefill", "pkv_decode_scratch", "pkv_debug_validate", "pkv_debug_read_ceiling"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -146,6 +146,17 @@ def test_host_checks_reject_before_launch(lib):
     # append with a head_dim that is not a multiple of 8 channels
     pool_odd = pkv._CPool(100, 16, 8, 60, 0x1000, 0x2000)
     assert _raw(lib, "pkv_append_kv", B(pool_odd), fake, fake, fake, fake, 10, fake, 4, None) == 2
+    # static-scratch decode: a descriptor whose workspace exceeds the scratch,
+    # and null arguments, are refused before anything is looked up or launched
+    big = _desc(num_workgroups=65536).c()
+    assert pkv.pkv_workspace_bytes(_desc(num_workgroups=65536)) > pkv.SCRATCH_BYTES
+    assert _raw(lib, "pkv_decode_scratch", B(pool), B(big), fake, fake, fake, 10, 4, 0.1, fake,
+                fake, None) == pkv.PKV_ERR_SCRATCH_TOO_SMALL
+    assert _raw(lib, "pkv_decode_scratch", B(pool), B(d), None, fake, fake, 10, 4, 0.1, fake,
+                fake, None) == 1
+    assert _raw(lib, "pkv_decode_scratch", B(pool), B(d), fake, fake, fake, 10, 17, 0.1, fake,
+                fake, None) == 4
+    assert pkv.pkv_status_str(pkv.PKV_ERR_SCRATCH_TOO_SMALL).startswith("the descriptor needs")
     # extend append: no query offsets, negative row bound, odd head_dim, a grid
     # of 2^31 workgroups or more
     assert _raw(lib, "pkv_append_kv_ragged", B(pool), fake, fake, None, fake, fake, 10, fake, 4,
