@@ -11,8 +11,11 @@ step streams its K/V from HBM.
 
 Timing: after W warm-up steps, a bounded spin kernel holds the GPU while the
 host enqueues all K timed steps; two HIP events on the stream the kernels run
-on bracket the K steps (step time).  The decode kernel alone is then timed the
-same way over K back-to-back launches (kernel time, the roofline figure).
+on bracket the K steps (step time).  The decode kernel alone is then timed
+over at least 100 launches, each between its own pair of HIP events on that
+stream (median and p10/p90: the roofline figure), and as the mean of as many
+back-to-back launches; a cache-warm figure (no pool rotation) is reported
+beside it, labelled.
 
 Prints one JSON line.  `value` is algorithmic GB/s of the whole step:
 bytes the method must move (K/V attended, q, output, page ids, appended rows)
@@ -57,6 +60,10 @@ def parse():
                     help="also time a model-like decode step: one metadata build, then N layers of "
                          "fused append + decode (each layer its own pool and q), issued eagerly and "
                          "replayed from one captured hipGraph, timed on the device and host-paced")
+    ap.add_argument("--graph-buckets", type=int, default=0, metavar="N",
+                    help="also time the step-graph harness: N layers of fused append + decode "
+                         "per step, one graph per power-of-two batch 1..64 (ragged lengths "
+                         "uniform in [1, 4096]), replay against eager, host-paced")
     ap.add_argument("--mask-keep", type=float, default=None, metavar="P",
                     help="also time pkv_decode_masked with a random keep mask of density P")
     ap.add_argument("--prefill", action="store_true",
@@ -102,28 +109,92 @@ def unique_kv_bytes(batch):
     return sum(used.values()) * batch.Hkv * batch.D * 2 * 2
 
 
-def cpu_baseline(batch, budget_s):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_units(batch):
+    """The per-request units of one decode call and the function that runs the
+    oracle on one of them: oracle.decode of request b alone (an [1, Hq, D]
+    output)."""
     import oracle
-    from threadpoolctl import threadpool_limits
 
     ip = oracle.kv_indptr(batch.seq_lens, batch.P)
     idx = batch.kv_indices
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        reps = 0
-        while True:
-            oracle.decode(batch.q, batch.k_pool, batch.v_pool, ip, idx, batch.seq_lens,
-                          batch.sm_scale, batch.P)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s or reps >= 1000:
+    units = [b for b in range(batch.B) if batch.seq_lens[b] > 0]
+
+    def unit(b):
+        return oracle.decode(batch.q[b:b + 1], batch.k_pool, batch.v_pool, ip[b:b + 2] - ip[b],
+                             idx[int(ip[b]):int(ip[b + 1])], batch.seq_lens[b:b + 1],
+                             batch.sm_scale, batch.P)
+    return units, unit
+
+
+_WORKER = {}
+
+
+def _worker_init(cfg):
+    # A fresh interpreter: rebuild the same seeded batch (no data is shipped).
+    import workloads as W
+
+    batch = W.config(cfg, poison=False)
+    _WORKER["unit"] = oracle_units(batch)[1]
+
+
+def _worker_unit(b):
+    t0 = time.perf_counter()
+    _WORKER["unit"](b)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(batch, budget_s, cfg=None):
+    """The fp64 oracle, as it is, timed on the host cores: one decode call is
+    split into its requests, each an oracle.decode of that request, run by a
+    pool of worker processes (each with one BLAS thread; they rebuild the same
+    seeded batch when they start).  One warm-up call, then calls until about
+    budget_s seconds, at least 3 and at most 7, median reported.  cfg=None runs
+    the units in this process, one after another (small batches, tests)."""
+    import multiprocessing as mp
+
+    units, unit = oracle_units(batch)
+    cores = min(len(os.sched_getaffinity(0)), 16, max(1, len(units)))  # box share: 16
+    times = []
+    if cfg is None:
+        cores = 1
+        run = lambda: [unit(b) for b in units]  # noqa: E731
+        pool = None
+    else:
+        os.environ.setdefault("OMP_NUM_THREADS", "1")
+        pool = mp.get_context("spawn").Pool(cores, initializer=_worker_init, initargs=(cfg,))
+        run = lambda: pool.map(_worker_unit, units, chunksize=1)  # noqa: E731
+    try:
+        run()  # warm-up
+        t_all = time.perf_counter()
+        while len(times) < 7:
+            t0 = time.perf_counter()
+            run()
+            times.append(time.perf_counter() - t0)
+            if len(times) >= 3 and time.perf_counter() - t_all >= budget_s:
                 break
-    per_call = el / reps
+    finally:
+        if pool is not None:
+            pool.close()
+            pool.join()
+    per_call = float(np.median(times))
     call_bytes, _ = algorithmic_bytes(batch)
-    return {"value": round(call_bytes / per_call / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "us_per_call": round(per_call * 1e6, 1),
-            "sample": f"{reps} full decode calls of the {batch.name} batch (fp64 numpy oracle, "
-                      f"one thread), {el:.1f} s"}
+    how = (f"{len(units)} per-request units on {cores} worker processes" if pool is not None
+           else "its requests one after another in one process")
+    return {"value": round(call_bytes / per_call / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "cpu": cpu_model(), "kind": "oracle", "us_per_call": round(per_call * 1e6, 1),
+            "sample": f"median of {len(times)} full decode calls of the {batch.name} batch "
+                      f"(fp64 numpy oracle, {how}, after one warm-up call), "
+                      f"{sum(times):.1f} s"}
 
 
 def counters_for_current_kernel():
@@ -237,10 +308,12 @@ def bench_ceiling(pkv, torch, dev, stream, K, nbytes):
         pkv.pkv_debug_read_ceiling(bufs[i % copies], sink, stream)
     for i in range(3):
         call(i)
-    ms = timed(stream, K, call)
-    gbps = n / (ms * 1e-3) / 1e9
-    return {"bytes": n, "us_per_call": round(ms * 1e3, 2), "GBps": round(gbps, 1),
-            "frac": round(gbps / PEAK_HBM_GBPS, 4), "copies": copies}
+    med, p10, p90, _ = timed_each(stream, max(K, 100), call)
+    ms_b2b = timed(stream, max(K, 100), call)
+    gbps = n / (med * 1e-3) / 1e9
+    return {"bytes": n, "us_per_call": round(med * 1e3, 2), "us_p10": round(p10 * 1e3, 2),
+            "us_p90": round(p90 * 1e3, 2), "us_per_call_back_to_back": round(ms_b2b * 1e3, 2),
+            "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4), "copies": copies}
 
 
 def bench_layers(pkv, torch, stream, K, batch, desc, base, nl):
@@ -290,6 +363,37 @@ def bench_layers(pkv, torch, stream, K, batch, desc, base, nl):
     return res
 
 
+def bench_graph_buckets(pkv, W, torch, dev, K, layers):
+    """Host-paced step time of the step-graph harness against the same step
+    issued eagerly, for every bucket 1..64 (live batch = the bucket size)."""
+    from paged_kv_split_attn_amd.step_graphs import StepGraphs
+
+    uni = W.make_batch(name="buckets", seed=81, B=64, Hq=32, Hkv=8, D=128, P=16,
+                       lengths=lambda r: r.integers(1, 4097, size=64), poison=False, append=True)
+    base = W.to_device(uni, dev)
+    pools = [pkv.Pool(base["k_pool"].clone(), base["v_pool"].clone()) for _ in range(layers)]
+    tmpl = pkv.Desc(max_batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16)
+    sg = StepGraphs(tmpl, pools, uni.sm_scale, max_batch=64, max_pages=len(uni.kv_indices))
+    sg.capture()
+    rng = np.random.default_rng(82)
+    res = []
+    for B in sorted(sg.buckets):
+        lens = uni.seq_lens[:B].astype(np.int32)
+        idx = np.concatenate(uni.page_lists[:B]).astype(np.int32)
+        q = torch.from_numpy(W.normal_bf16(rng, (layers, B, 32, 128)).view(np.int16)).to(dev)
+        kn = torch.from_numpy(W.normal_bf16(rng, (layers, B, 8, 128)).view(np.int16)).to(dev)
+        vn = torch.from_numpy(W.normal_bf16(rng, (layers, B, 8, 128)).view(np.int16)).to(dev)
+        bk = sg.load(torch.from_numpy(lens).to(dev), torch.from_numpy(idx).to(dev), q, kn, vn)
+        torch.cuda.synchronize()
+        kp = max(10, K // 4)
+        g_us = paced(kp, lambda i: sg.replay(bk)) * 1e3
+        e_us = paced(kp, lambda i: sg.eager(bk)) * 1e3
+        res.append({"batch": B, "kv_tokens": int(lens.sum()), "graph_host_paced_us": round(g_us, 1),
+                    "eager_host_paced_us": round(e_us, 1),
+                    "graph_speedup": round(e_us / g_us, 3)})
+    return {"layers": layers, "buckets": res}
+
+
 def paced(K, fn):
     """Mean wall-clock ms of fn(i) over K calls issued by the host one after
     another, the GPU idle at the start: host launch cost included."""
@@ -301,6 +405,25 @@ def paced(K, fn):
         fn(i)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / K
+
+
+def timed_each(stream, K, fn):
+    """Per-call ms of fn(i) for K calls, each bracketed by its own pair of HIP
+    events on the stream, enqueued behind a bounded spin: returns
+    (median, p10, p90, all)."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(40e6))
+    for i in range(K):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return float(np.median(ms)), float(np.percentile(ms, 10)), float(np.percentile(ms, 90)), ms
 
 
 def timed(stream, K, fn):
@@ -445,7 +568,12 @@ def main():
         "call_bytes": call_bytes,
     }
     if not args.no_kernel_loop:
-        call_ms = timed(stream, K, decode_only)
+        # Decode-only launches (pool rotated): per-launch events, median and
+        # p10/p90 of at least 100; the mean of as many back-to-back launches
+        # beside it.
+        KL = max(K, 100)
+        call_ms, p10_ms, p90_ms, _ = timed_each(stream, KL, decode_only)
+        b2b_ms = timed(stream, KL, decode_only)
         achieved = call_bytes / (call_ms * 1e-3) / 1e9
         ctr = counters_for_current_kernel()
         traffic = None
@@ -456,8 +584,21 @@ def main():
         if uniq < kv_bytes:  # shared prefixes: also the rate over bytes counted once
             res["unique_call_bytes"] = call_bytes - kv_bytes + uniq
             res["unique_call_GBps"] = round(res["unique_call_bytes"] / (call_ms * 1e-3) / 1e9, 1)
+        # Cache-warm: the same pool every launch (it then sits in the 256 MB
+        # Infinity Cache); labelled, never the roofline figure.
+        def decode_warm(i):
+            pool, q = copies[0]
+            pkv.pkv_decode(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, stream)
+        warm_ms, _, _, _ = timed_each(stream, KL, decode_warm)
         res.update({
             "us_per_call": round(call_ms * 1e3, 2),
+            "us_per_call_p10": round(p10_ms * 1e3, 2),
+            "us_per_call_p90": round(p90_ms * 1e3, 2),
+            "us_per_call_back_to_back": round(b2b_ms * 1e3, 2),
+            "launches_timed": KL,
+            "warm": {"us_per_call": round(warm_ms * 1e3, 2),
+                     "GBps": round(call_bytes / (warm_ms * 1e-3) / 1e9, 1),
+                     "note": "cache-warm: one pool copy, read again every launch"},
             "call_GBps": round(achieved, 1),
             "call_frac_of_peak": round(achieved / PEAK_HBM_GBPS, 4),
             "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(achieved, 1),
@@ -474,6 +615,8 @@ def main():
         res["read_ceiling"] = bench_ceiling(pkv, torch, dev, stream, K, call_bytes)
     if args.layers > 0:
         res["layered_step"] = bench_layers(pkv, torch, stream, K, batch, desc, base, args.layers)
+    if args.graph_buckets > 0:
+        res["graph_buckets"] = bench_graph_buckets(pkv, W, torch, dev, K, args.graph_buckets)
     if args.mask_keep is not None:
         S = -(-int(batch.seq_lens.max()) // 4) * 4
         rng = np.random.default_rng(np.random.PCG64(2000 + args.config))
@@ -488,7 +631,7 @@ def main():
                          "GBps": round((call_bytes + batch.B * S) / (masked_ms * 1e-3) / 1e9, 1)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, cfg=args.config)
     print(json.dumps(res), flush=True)
 
 
