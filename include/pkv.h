@@ -18,15 +18,19 @@
  *
  * Paged KV pool.  K and V of one layer live in fixed-size pages of a pool shared
  * by all requests.  This library lays a pool out page-major, then head-major,
- * and stores each (page, KV head) tile in the order its matrix-core loads read
- * it:
+ * and stores each (page, KV head) tile as page_size / 16 steps of 16 tokens,
+ * each step in the order the matrix-core loads read it:
  *
- *     K : bf16 [num_pages][Hkv][head_dim / 8][page_size][8]
- *     V : bf16 [num_pages][Hkv][head_dim][page_size]
+ *     K : bf16 [num_pages][Hkv][page_size / 16][head_dim / 8][16][8]
+ *     V : bf16 [num_pages][Hkv][page_size / 16][head_dim][16]
  *
- * K(t, c) of a tile sits at [c / 8][t][c % 8] and V(t, c) at [c][t].  One tile
- * is one contiguous run of bytes, and every load instruction of the decode
- * reads whole contiguous blocks (1 KiB of K, 512 B of V).  Token t of request b
+ * K(t, c) of a tile sits at [t / 16][c / 8][t % 16][c % 8] and V(t, c) at
+ * [t / 16][c][t % 16].  One tile is one contiguous run of bytes, one 16-token
+ * step of it (4 KiB of K and 4 KiB of V at head_dim 128) another, at every page
+ * size, and every load instruction of the decode reads whole contiguous blocks
+ * (1 KiB of K, 512 B of V).  (The pages' pool is token-major, [slot][Hkv][D]
+ * per layer: the same bytes per token, ordered differently inside a page; the
+ * library's append calls write new tokens into this layout.)  Token t of request b
  * lives in page
  * kv_indices[kv_indptr[b] + t / page_size] at offset t % page_size (the pages'
  * PagePool addressing: page index pos // page_size, offset pos % page_size,
@@ -103,8 +107,8 @@ const char* pkv_status_str(int status);
 int32_t pkv_version(void);
 
 /* One layer's paged K/V pool (device memory owned by the caller), contiguous:
- * k: bf16 [num_pages][num_kv_heads][head_dim / 8][page_size][8]
- * v: bf16 [num_pages][num_kv_heads][head_dim][page_size] */
+ * k: bf16 [num_pages][num_kv_heads][page_size / 16][head_dim / 8][16][8]
+ * v: bf16 [num_pages][num_kv_heads][page_size / 16][head_dim][16] */
 typedef struct pkv_pool {
   int32_t num_pages;
   int32_t page_size;

@@ -220,20 +220,23 @@ class Desc:
 
 @dataclass
 class Pool:
-    """One layer's pool: bf16 device tensors k [num_pages, Hkv, head_dim/8, page_size, 8]
-    and v [num_pages, Hkv, head_dim, page_size] (the library's tile layouts)."""
+    """One layer's pool: bf16 device tensors k [num_pages, Hkv, P/16, head_dim/8, 16, 8]
+    and v [num_pages, Hkv, P/16, head_dim, 16] (the library's tile layouts: each
+    16-token step of a page stored K in 8-channel blocks, V channel-major)."""
 
     k: torch.Tensor
     v: torch.Tensor
 
     def c(self) -> _CPool:
-        if self.k.dim() != 5 or self.v.dim() != 4 or self.k.shape[4] != 8:
-            raise ValueError("k must be [num_pages, Hkv, head_dim/8, page_size, 8] and v 4-D")
-        n, h, d8, p, _ = self.k.shape
-        d = d8 * 8
-        if tuple(self.v.shape) != (n, h, d, p):
-            raise ValueError("v must be [num_pages, Hkv, head_dim, page_size]")
-        return _CPool(n, p, h, d, _ptr(self.k, "pool.k", _BF16), _ptr(self.v, "pool.v", _BF16))
+        if self.k.dim() != 6 or self.v.dim() != 5 or self.k.shape[4:] != (16, 8) or \
+                self.v.shape[4] != 16:
+            raise ValueError("k must be [num_pages, Hkv, P/16, head_dim/8, 16, 8] and v "
+                             "[num_pages, Hkv, P/16, head_dim, 16]")
+        n, h, s, d8 = self.k.shape[:4]
+        if tuple(self.v.shape) != (n, h, s, d8 * 8, 16):
+            raise ValueError("v must be [num_pages, Hkv, P/16, head_dim, 16] matching k")
+        return _CPool(n, s * 16, h, d8 * 8, _ptr(self.k, "pool.k", _BF16),
+                      _ptr(self.v, "pool.v", _BF16))
 
 
 def pkv_status_str(status: int) -> str:

@@ -21,13 +21,15 @@
 // Arithmetic on the matrix cores.  A wave consumes 16 tokens of one tile per
 // step.  Scores S^T[token][head] = K . q^T come from D/32
 // v_mfma_f32_16x16x32_bf16 (K rows are the A operand, q the B operand; query
-// heads beyond HG are zero columns).  K tiles are stored [D/8][P][8], so the A
-// operand of one MFMA (channels 32kk .. 32kk+31 of 16 tokens) is one
-// contiguous kilobyte: lane (g, r) reads channel block 4kk + g of token r.  The result leaves lane (g, r) = (l / 16,
-// l % 16) holding the scores of head r for tokens 4g .. 4g+3, which is exactly
-// the A-operand layout of v_mfma_f32_16x16x16_bf16 for P . V, so the softmax
-// weights never move between lanes.  V tiles are stored channel-major, so the
-// B operand (4 tokens of one channel per lane) is one 8-byte load.  The weights
+// heads beyond HG are zero columns).  Each 16-token step of a K tile is stored
+// [D/8][16][8], so the A operand of one MFMA (channels 32kk .. 32kk+31 of 16
+// tokens) is one contiguous kilobyte: lane (g, r) reads channel block 4kk + g
+// of token r.  The result leaves lane (g, r) = (l / 16, l % 16) holding the
+// scores of head r for tokens 4g .. 4g+3, which is exactly the A-operand layout
+// of v_mfma_f32_16x16x16_bf16 for P . V, so the softmax weights never move
+// between lanes.  Each V step is stored channel-major ([D][16]), so the B
+// operand (4 tokens of one channel per lane) is one 8-byte load, and one load
+// instruction reads 512 contiguous bytes at every page size.  The weights
 // enter the product as bf16 hi + lo parts (two MFMAs), keeping the p.V sum
 // accurate to about 2^-16 relative, while the softmax sums stay in fp32.  K and
 // V go straight from HBM into registers: every element is used once.
@@ -182,9 +184,12 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const int P = a.page_size;
   const int log2_s = a.log2_steps;  // steps of 16 tokens per page
   const size_t tile_b = (size_t)P * D * 2;  // bytes of one (page, head) tile
+  // A tile is P / 16 steps of 16 tokens, each laid out K [D/8][16][8] and
+  // V [D][16], kStepBytes apiece.
+  constexpr size_t kStepBytes = (size_t)16 * D * 2;
   // Lane byte offsets inside a step: K block g4, token r16; V^T channel r16, tokens 4*g4.
-  const uint32_t k_boff = (uint32_t)(g4 * P + r16) * 16;
-  const uint32_t v_boff = (uint32_t)(r16 * P + 4 * g4) * 2;
+  const uint32_t k_boff = (uint32_t)(g4 * 16 + r16) * 16;
+  const uint32_t v_boff = (uint32_t)(r16 * 16 + 4 * g4) * 2;
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
   const size_t slot_b = (size_t)a.num_kv_heads * D * 2;  // bytes of one token slot (TOKENS)
@@ -317,19 +322,19 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         const int sub = jc & ((1 << log2_s) - 1);
         const int pid = __builtin_amdgcn_readlane(vpage, pg);
         const size_t base = (size_t)(pid < 0 ? 0 : pid) * a.num_kv_heads * tile_b + head_b;
-        const char* kp = kbase + base + (size_t)sub * 16 * 16 + k_boff;
-        const char* vp = vbase + base + (size_t)sub * 16 * 2 + v_boff;
+        const char* kp = kbase + base + (size_t)sub * kStepBytes + k_boff;
+        const char* vp = vbase + base + (size_t)sub * kStepBytes + v_boff;
         const int tok = fresh_token(j);
         // The lanes of the appended token read its K row from k_new.
         const bool knew = tok >= 0 && r16 == tok;
         const char* kq = knew ? knew_row + g4 * 16 : kp;
-        const size_t kstride = knew ? 4 * 16 : (size_t)4 * P * 16;
+        const size_t kstride = knew ? 4 * 16 : 4 * 16 * 16;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
           sd.k[kk] = *reinterpret_cast<const uint4*>(kq + (size_t)kk * kstride);
 #pragma unroll
         for (int vb = 0; vb < D / 16; ++vb)
-          sd.v[vb] = *reinterpret_cast<const uint2*>(vp + (size_t)vb * 16 * P * 2);
+          sd.v[vb] = *reinterpret_cast<const uint2*>(vp + (size_t)vb * 16 * 16 * 2);
         if constexpr (MASKED) {
           // Keep bytes of this lane's four tokens; a row shorter than the
           // request reads 0 (dropped) past the end of the mask buffer.
@@ -382,18 +387,19 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         }
         if (writer && pid >= 0) {
           const size_t base = (size_t)pid * a.num_kv_heads * tile_b + head_b;
-          const int off = sub * 16 + tok;  // token offset inside the page
-          if (r16 == tok) {
+          if (r16 == tok) {  // token tok of step sub of the page
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk)
               *reinterpret_cast<uint4*>(const_cast<char*>(kbase) + base +
-                                        ((size_t)(4 * kk + g4) * P + off) * 16) = sd.k[kk];
+                                        (size_t)sub * kStepBytes +
+                                        ((size_t)(4 * kk + g4) * 16 + tok) * 16) = sd.k[kk];
           }
           if (vlane) {
 #pragma unroll
             for (int vb = 0; vb < D / 16; ++vb)
               *reinterpret_cast<uint16_t*>(const_cast<char*>(vbase) + base +
-                                           ((size_t)(16 * vb + r16) * P + off) * 2) = vn[vb];
+                                           (size_t)sub * kStepBytes +
+                                           ((size_t)(16 * vb + r16) * 16 + tok) * 2) = vn[vb];
           }
         }
         st.step(sd, live, g4, a.scale_log2, bias);

@@ -258,10 +258,11 @@ __global__ void __launch_bounds__(THREADS) metadata_kernel(MetaArgs a) {
   }
 }
 
-// One thread per 8-channel chunk of (request, KV head, K or V) rows.  A K tile
-// keeps 8-channel blocks of each token together ([D/8][P][8]): one 16-byte
-// store per chunk.  V tiles are channel-major ([D][P]), so a V row is a column
-// of its tile: eight 2-byte stores, page_size apart.
+// One thread per 8-channel chunk of (request, KV head, K or V) rows.  A tile is
+// page_size / 16 steps of 16 tokens; a K step keeps 8-channel blocks of each
+// token together ([D/8][16][8]): one 16-byte store per chunk.  V steps are
+// channel-major ([D][16]), so a V row is a column of its step: eight 2-byte
+// stores, 16 elements apart.
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   // 32-bit index arithmetic: the host checks that the grid fits.
   const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -284,17 +285,19 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   const bool slot_ok = L > 0 && slot >= 0 && slot < a.num_indices;
   const int page = slot_ok ? a.kv_indices[slot] : -1;
   if (!slot_ok || page < 0 || page >= a.num_pages) return;
-  const size_t tile = (((size_t)page * a.num_kv_heads + h) * a.page_size) * a.head_dim;
   const int off = pos % a.page_size;
+  // Step off / 16 of the (page, head) tile, then token off % 16 in it.
+  const size_t step = ((((size_t)page * a.num_kv_heads + h) * a.page_size) + (off & ~15)) *
+                      a.head_dim;
   if (which == 0) {
-    *reinterpret_cast<uint4*>(a.k + tile + ((size_t)c * a.page_size + off) * 8) = w;
+    *reinterpret_cast<uint4*>(a.k + step + ((size_t)c * 16 + (off & 15)) * 8) = w;
   } else {
     const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-    uint16_t* col = a.v + tile + (size_t)c * 8 * a.page_size + off;
+    uint16_t* col = a.v + step + (size_t)c * 8 * 16 + (off & 15);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      col[(size_t)(2 * j) * a.page_size] = (uint16_t)(words[j] & 0xffffu);
-      col[(size_t)(2 * j + 1) * a.page_size] = (uint16_t)(words[j] >> 16);
+      col[(size_t)(2 * j) * 16] = (uint16_t)(words[j] & 0xffffu);
+      col[(size_t)(2 * j + 1) * 16] = (uint16_t)(words[j] >> 16);
     }
   }
 }
@@ -302,9 +305,9 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
 // Extend append: request b's n_b = qo_indptr[b+1] - qo_indptr[b] new rows go
 // to positions seq_len - n_b .. seq_len - 1.  A workgroup covers 16 rows of
 // one (request, KV head) with one thread per (row, 8-channel chunk), rows
-// fastest, so that the 16 rows' K chunks of one channel block (consecutive
-// tokens of a page: [c][t][8]) form one 256-byte run and their V values of
-// one channel (consecutive [c][t]) one 32-byte run.
+// fastest, so that the K chunks of one channel block of a step's consecutive
+// tokens ([c][t][8]) form one run and their V values of one channel ([c][t])
+// another.
 __global__ void __launch_bounds__(256) append_rows_kernel(AppendArgs a) {
   const uint32_t nblk = (uint32_t)a.row_blocks;
   const uint32_t bid = blockIdx.x;
@@ -327,15 +330,16 @@ __global__ void __launch_bounds__(256) append_rows_kernel(AppendArgs a) {
   const size_t src = ((size_t)(r0 + i) * a.num_kv_heads + h) * a.head_dim + (size_t)c * 8;
   const uint4 kw = *reinterpret_cast<const uint4*>(a.k_new + src);
   const uint4 vw = *reinterpret_cast<const uint4*>(a.v_new + src);
-  const size_t tile = (((size_t)page * a.num_kv_heads + h) * a.page_size) * a.head_dim;
   const int off = pos % a.page_size;
-  *reinterpret_cast<uint4*>(a.k + tile + ((size_t)c * a.page_size + off) * 8) = kw;
+  const size_t step = ((((size_t)page * a.num_kv_heads + h) * a.page_size) + (off & ~15)) *
+                      a.head_dim;
+  *reinterpret_cast<uint4*>(a.k + step + ((size_t)c * 16 + (off & 15)) * 8) = kw;
   const uint32_t words[4] = {vw.x, vw.y, vw.z, vw.w};
-  uint16_t* col = a.v + tile + (size_t)c * 8 * a.page_size + off;
+  uint16_t* col = a.v + step + (size_t)c * 8 * 16 + (off & 15);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    col[(size_t)(2 * j) * a.page_size] = (uint16_t)(words[j] & 0xffffu);
-    col[(size_t)(2 * j + 1) * a.page_size] = (uint16_t)(words[j] >> 16);
+    col[(size_t)(2 * j) * 16] = (uint16_t)(words[j] & 0xffffu);
+    col[(size_t)(2 * j + 1) * 16] = (uint16_t)(words[j] >> 16);
   }
 }
 

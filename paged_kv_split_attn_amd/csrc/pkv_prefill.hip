@@ -343,8 +343,9 @@ prefill_kernel(PrefillArgs a) {
       }
       const int sub = (c * kHalves + hf) & ((1 << log2_s) - 1);
       const char* tile = (is_v ? vbase : kbase) + (size_t)pid * a.num_kv_heads * tile_b + head_b;
-      const int off = is_v ? ((y >> 1) * P + sub * 16 + 8 * (y & 1)) * 2
-                           : ((y >> 4) * P + sub * 16 + (y & 15)) * 16;
+      // Step sub of the tile: V [D][16], K [D/8][16][8].
+      const int off = sub * 16 * D * 2 + (is_v ? ((y >> 1) * 16 + 8 * (y & 1)) * 2
+                                               : ((y >> 4) * 16 + (y & 15)) * 16);
       stage[i] = *reinterpret_cast<const uint4*>(tile + off);
     }
   };

@@ -396,25 +396,30 @@ def identity_layout(batch: DecodeBatch) -> DecodeBatch:
 
 
 def v_pool_channel_major(v_pool: np.ndarray) -> np.ndarray:
-    """[pages][Hkv][P][D] -> [pages][Hkv][D][P]: the device layout of V tiles."""
-    return np.ascontiguousarray(np.swapaxes(v_pool, 2, 3))
+    """[pages][Hkv][P][D] -> [pages][Hkv][P/16][D][16]: the device layout of V
+    tiles (each 16-token step of a page channel-major)."""
+    n, h, p, d = v_pool.shape
+    return np.ascontiguousarray(v_pool.reshape(n, h, p // 16, 16, d).transpose(0, 1, 2, 4, 3))
 
 
 def v_pool_token_major(v_dev: np.ndarray) -> np.ndarray:
     """Inverse of v_pool_channel_major."""
-    return np.ascontiguousarray(np.swapaxes(v_dev, 2, 3))
+    n, h, s, d, t = v_dev.shape
+    return np.ascontiguousarray(v_dev.transpose(0, 1, 2, 4, 3).reshape(n, h, s * t, d))
 
 
 def k_pool_blocked(k_pool: np.ndarray) -> np.ndarray:
-    """[pages][Hkv][P][D] -> [pages][Hkv][D/8][P][8]: the device layout of K tiles."""
+    """[pages][Hkv][P][D] -> [pages][Hkv][P/16][D/8][16][8]: the device layout
+    of K tiles (each 16-token step of a page in 8-channel blocks)."""
     n, h, p, d = k_pool.shape
-    return np.ascontiguousarray(k_pool.reshape(n, h, p, d // 8, 8).transpose(0, 1, 3, 2, 4))
+    return np.ascontiguousarray(
+        k_pool.reshape(n, h, p // 16, 16, d // 8, 8).transpose(0, 1, 2, 4, 3, 5))
 
 
 def k_pool_token_major(k_dev: np.ndarray) -> np.ndarray:
     """Inverse of k_pool_blocked."""
-    n, h, d8, p, e = k_dev.shape
-    return np.ascontiguousarray(k_dev.transpose(0, 1, 3, 2, 4).reshape(n, h, p, d8 * e))
+    n, h, s, d8, t, e = k_dev.shape
+    return np.ascontiguousarray(k_dev.transpose(0, 1, 2, 4, 3, 5).reshape(n, h, s * t, d8 * e))
 
 
 def to_device(batch: DecodeBatch, device="cuda:0") -> dict:
@@ -422,8 +427,8 @@ def to_device(batch: DecodeBatch, device="cuda:0") -> dict:
 
     Returns a dict with q, k_pool, v_pool, seq_lens, kv_indices and, for an
     append batch, k_new and v_new.  The batch keeps K and V token-major; the
-    device copies use the library's tile layouts (K [D/8][P][8], V [D][P] inside
-    each (page, head) tile).  Data movement only.
+    device copies use the library's tile layouts (inside each (page, head) tile,
+    P / 16 steps of K [D/8][16][8] and V [D][16]).  Data movement only.
     """
     import torch
 
