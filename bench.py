@@ -2,9 +2,12 @@
 
 One step = the whole hot path for one layer of one decode step: build the step
 metadata (page prefix sums + work plan), append this step's K/V token of every
-request and run the split-KV decode (partials and their merge).  By default the
-append and the decode are one launch (pkv_decode_append); --append separate
-runs pkv_append_kv and pkv_decode as two launches.  Inputs are seeded synthetic
+request and run the split-KV decode (partials and their merge).  By default
+all three are one launch (pkv_decode_plan: every workgroup plans the step in
+LDS, then appends and decodes); --plan metadata builds the plan in its own
+launch first (pkv_build_metadata + pkv_decode_append), and --append separate
+runs pkv_build_metadata, pkv_append_kv and pkv_decode as three launches.  The
+step planned the other way is timed beside it (step_other_plan).  Inputs are seeded synthetic
 batches already resident in HBM.  Between steps the pool rotates over several
 identical copies whose total size exceeds the 256 MB Infinity Cache, so every
 step streams its K/V from HBM.
@@ -55,6 +58,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append", choices=("fused", "separate"), default="fused",
                     help="KV append fused into the decode launch, or its own launch")
+    ap.add_argument("--plan", choices=("launch", "metadata"), default="launch",
+                    help="plan the step inside the decode launch (pkv_decode_plan), or with "
+                         "its own metadata launch first (pkv_build_metadata)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured hipGraph (one graph per pool copy)")
     ap.add_argument("--layers", type=int, default=0, metavar="N",
@@ -318,11 +324,13 @@ def bench_ceiling(pkv, torch, dev, stream, K, nbytes):
             "frac": round(gbps / PEAK_HBM_GBPS, 4), "copies": copies}
 
 
-def bench_layers(pkv, torch, stream, K, batch, desc, base, nl):
-    """A decode step of an nl-layer model's attention: pkv_build_metadata once,
-    then pkv_decode_append for every layer (its own pool and q), eager and as
-    one hipGraph replay.  Device-timed (host enqueues ahead) and host-paced
-    (GPU idle at the start, launch cost included)."""
+def bench_layers(pkv, torch, stream, K, batch, desc, base, nl, plan="launch"):
+    """A decode step of an nl-layer model's attention: the first layer's
+    pkv_decode_plan (plan = "launch"; else pkv_build_metadata, then that
+    layer's pkv_decode_append), then pkv_decode_append for every later layer
+    (each its own pool and q), eager and as one hipGraph replay.  Device-timed
+    (host enqueues ahead) and host-paced (GPU idle at the start, launch cost
+    included)."""
     layers = [(pkv.Pool(base["k_pool"].clone(), base["v_pool"].clone()), base["q"].clone())
               for _ in range(nl)]
     ws = torch.zeros(pkv.pkv_workspace_bytes(desc), dtype=torch.uint8, device=stream.device)
@@ -331,8 +339,13 @@ def bench_layers(pkv, torch, stream, K, batch, desc, base, nl):
     seq, idx = base["seq_lens"], base["kv_indices"]
 
     def step_on(st):
-        pkv.pkv_build_metadata(desc, seq, 0, kv_indptr, ws, st)
-        for pool, q in layers:
+        for li, (pool, q) in enumerate(layers):
+            if li == 0 and plan == "launch":
+                pkv.pkv_decode_plan(pool, desc, q, base["k_new"], base["v_new"], seq, 0, kv_indptr,
+                                    idx, batch.sm_scale, ws, out, st)
+                continue
+            if li == 0:
+                pkv.pkv_build_metadata(desc, seq, 0, kv_indptr, ws, st)
             pkv.pkv_decode_append(pool, desc, q, base["k_new"], base["v_new"], kv_indptr, idx, seq,
                                   batch.sm_scale, ws, out, st)
 
@@ -355,7 +368,7 @@ def bench_layers(pkv, torch, stream, K, batch, desc, base, nl):
     eager = lambda i: step_on(stream)  # noqa: E731
     replay = lambda i: g.replay()  # noqa: E731
     kl = max(5, K // 4)
-    res = {"layers": nl, "workload": batch.name,
+    res = {"layers": nl, "workload": batch.name, "plan": plan,
            "eager_device_us": timed(stream, kl, eager) * 1e3,
            "graph_device_us": timed(stream, kl, replay) * 1e3,
            "eager_host_paced_us": paced(kl, eager) * 1e3,
@@ -493,8 +506,12 @@ def main():
     k_new, v_new = base["k_new"], base["v_new"]
     stream = torch.cuda.current_stream()
 
-    def step_on(i, st):
+    def step_with(i, st, plan):
         pool, q = copies[i % ncopies]
+        if args.append == "fused" and plan == "launch":
+            pkv.pkv_decode_plan(pool, desc, q, k_new, v_new, seq, 0, kv_indptr, idx,
+                                batch.sm_scale, ws, out, st)
+            return
         pkv.pkv_build_metadata(desc, seq, 0, kv_indptr, ws, st)
         if args.append == "fused":
             pkv.pkv_decode_append(pool, desc, q, k_new, v_new, kv_indptr, idx, seq,
@@ -502,6 +519,9 @@ def main():
         else:
             pkv.pkv_append_kv(pool, k_new, v_new, kv_indptr, idx, seq, st)
             pkv.pkv_decode(pool, desc, q, kv_indptr, idx, seq, batch.sm_scale, ws, out, st)
+
+    def step_on(i, st):
+        step_with(i, st, args.plan)
 
     def step(i):
         step_on(i, stream)
@@ -564,11 +584,18 @@ def main():
                    "kv_tokens": batch.kv_tokens, "pool_pages": batch.num_pages,
                    "pool_copies": ncopies, "decode_grid": desc.groups(),
                    "plan_workgroups": plan["groups"], "append": args.append,
+                   "plan": args.plan if args.append == "fused" else "metadata",
                    "graph": bool(args.graph),
                    "parallelism": "single-gpu"},
         "step_bytes": step_bytes,
         "call_bytes": call_bytes,
     }
+    if args.append == "fused" and not args.graph:
+        # The step with its plan made the other way, for comparison.
+        other = "metadata" if args.plan == "launch" else "launch"
+        res["step_other_plan"] = {
+            "plan": other,
+            "ms_per_step": round(timed(stream, K, lambda i: step_with(i, stream, other)), 5)}
     if not args.no_kernel_loop:
         # Decode-only launches (pool rotated): per-launch events, median and
         # p10/p90 of at least 100; the mean of as many back-to-back launches
@@ -619,7 +646,8 @@ def main():
     if not args.no_ceiling and not args.no_kernel_loop:
         res["read_ceiling"] = bench_ceiling(pkv, torch, dev, stream, K, call_bytes)
     if args.layers > 0:
-        res["layered_step"] = bench_layers(pkv, torch, stream, K, batch, desc, base, args.layers)
+        res["layered_step"] = bench_layers(pkv, torch, stream, K, batch, desc, base, args.layers,
+                                           args.plan)
     if args.graph_buckets > 0:
         res["graph_buckets"] = bench_graph_buckets(pkv, W, torch, dev, K, args.graph_buckets)
     if args.mask_keep is not None:

@@ -270,6 +270,35 @@ int pkv_decode_append(const pkv_pool* pool, const pkv_desc* desc, const void* q,
                       int32_t batch, float sm_scale, void* workspace, size_t workspace_bytes,
                       void* out, void* stream);
 
+/* Step metadata and the first layer's decode in one launch: the same results
+ * (kv_indptr, the plan in the workspace, the pool and out) as
+ *   pkv_build_metadata(desc, seq_lens, batch, forced_groups, kv_indptr, ws)
+ * followed by pkv_decode_append(..., k_new, v_new, ...), or by pkv_decode(...)
+ * when k_new and v_new are both NULL.  The pages build the step's page prefix
+ * sums once and reuse them in every layer (AstrAI commit 05739629,
+ * astrai/inference, bind_tasks bullets); here each workgroup of the first
+ * layer's launch computes the plan from seq_lens in its own LDS, starts its
+ * tiles at once and writes its part of the plan for the step's later layers,
+ * which call pkv_decode / pkv_decode_append with the same kv_indptr and
+ * workspace.  Deterministic: bitwise the result of the two-call sequence.
+ *  seq_lens       device int32 [batch], read by this launch only
+ *  kv_indptr      device int32 [batch + 1], written (as pkv_build_metadata)
+ *  forced_groups  as for pkv_build_metadata
+ * Every other argument is as for pkv_decode_append.  Differences from the
+ * two-call sequence: the workspace error word is not cleared, new error bits
+ * are ORed into it (pkv_debug_validate reads and clears it); and the merge's
+ * arrival counters must be zero when the launch starts, which holds for a
+ * workspace that has been through pkv_build_metadata once, since every decode
+ * leaves them at zero (a workspace that never has must be zero-filled).  For
+ * batch 0 or batch above 1024 the call runs the metadata kernel and then the
+ * decode, two launches.
+ * Errors: those of pkv_build_metadata and pkv_decode_append. */
+int pkv_decode_plan(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                    const void* k_new, const void* v_new, const int32_t* seq_lens, int32_t batch,
+                    int32_t forced_groups, int32_t* kv_indptr, const int32_t* kv_indices,
+                    int32_t num_indices, float sm_scale, void* workspace, size_t workspace_bytes,
+                    void* out, void* stream);
+
 /* Decode attention with a per-token keep mask (one launch): the optional 2-D
  * bool mask [batch, max_seq_len], True = keep, of the pages' paged decode
  * wrapper (attention_ops.py, attn_paged_decode docstring, on the compare page).

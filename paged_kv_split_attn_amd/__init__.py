@@ -36,6 +36,7 @@ __all__ = [
     "pkv_append_kv_ragged",
     "pkv_decode",
     "pkv_decode_append",
+    "pkv_decode_plan",
     "pkv_decode_masked",
     "pkv_decode_tokens",
     "pkv_prefill",
@@ -120,6 +121,9 @@ _SIGNATURES = {
     "pkv_decode_append": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp,
                                          _vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
                                          ctypes.c_size_t, _vp, _vp]),
+    "pkv_decode_plan": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp,
+                                       _vp, _vp, _i32, _i32, _vp, _vp, _i32, ctypes.c_float, _vp,
+                                       ctypes.c_size_t, _vp, _vp]),
     "pkv_decode_masked": (ctypes.c_int, [ctypes.POINTER(_CPool), ctypes.POINTER(_CDesc), _vp, _vp,
                                          _i32, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
                                          ctypes.c_size_t, _vp, _vp]),
@@ -325,6 +329,28 @@ def pkv_decode_append(pool: Pool, desc: Desc, q: torch.Tensor, k_new: torch.Tens
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(out, "out", _BF16, n), _stream(stream))
     _check("pkv_decode_append", st)
+
+
+def pkv_decode_plan(pool: Pool, desc: Desc, q: torch.Tensor, k_new: Optional[torch.Tensor],
+                    v_new: Optional[torch.Tensor], seq_lens: torch.Tensor, forced_groups: int,
+                    kv_indptr: torch.Tensor, kv_indices: torch.Tensor, sm_scale: float,
+                    workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """pkv_build_metadata followed by pkv_decode_append (or pkv_decode when
+    k_new and v_new are None), in one launch."""
+    B = seq_lens.numel()
+    n = B * desc.num_q_heads * desc.head_dim
+    nkv = B * desc.num_kv_heads * desc.head_dim
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    kp = None if k_new is None else _ptr(k_new, "k_new", _BF16, nkv)
+    vp = None if v_new is None else _ptr(v_new, "v_new", _BF16, nkv)
+    st = load_library().pkv_decode_plan(
+        ctypes.byref(pool.c()), ctypes.byref(desc.c()), _ptr(q, "q", _BF16, n), kp, vp,
+        _ptr(seq_lens, "seq_lens", _I32), B, int(forced_groups),
+        _ptr(kv_indptr, "kv_indptr", _I32, B + 1), _ptr(kv_indices, "kv_indices", _I32),
+        kv_indices.numel(), float(sm_scale), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(out, "out", _BF16, n), _stream(stream))
+    _check("pkv_decode_plan", st)
 
 
 def pkv_decode_masked(pool: Pool, desc: Desc, q: torch.Tensor, mask: torch.Tensor,

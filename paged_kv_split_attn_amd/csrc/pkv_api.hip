@@ -112,7 +112,7 @@ const char* pkv_status_str(int status) {
   }
 }
 
-int32_t pkv_version(void) { return (2 << 16) | 5; }
+int32_t pkv_version(void) { return (2 << 16) | 6; }
 
 size_t pkv_workspace_bytes(const pkv_desc* desc) {
   WsLayout L;
@@ -143,6 +143,7 @@ int pkv_build_metadata(const pkv_desc* desc, const int32_t* seq_lens, int32_t ba
   a.groups = L.groups;
   a.min_tiles = desc->min_tiles_per_group > 0 ? desc->min_tiles_per_group : kDefaultMinTiles;
   a.forced = forced_groups;
+  a.segments = L.segments;
   return launch_status(launch_metadata(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -213,14 +214,15 @@ int pkv_append_kv_ragged(const pkv_pool* pool, const void* k_new, const void* v_
 
 namespace {
 
-// pkv_decode and pkv_decode_append: the same launch, with or without the
-// token to append.
-int decode_impl(const pkv_pool* pool, const pkv_desc* desc, const void* q, const void* k_new,
-                const void* v_new, const uint8_t* mask, int32_t mask_stride,
-                const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
-                const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
-                size_t workspace_bytes, void* out, void* stream) {
-  WsLayout L;
+// Checks of pkv_decode / pkv_decode_append / pkv_decode_masked /
+// pkv_decode_plan and the launch arguments they share (the plan fields are
+// left off).
+int prepare_decode(const pkv_pool* pool, const pkv_desc* desc, const void* q, const void* k_new,
+                   const void* v_new, const uint8_t* mask, int32_t mask_stride,
+                   const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
+                   const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
+                   size_t workspace_bytes, void* out, WsLayout* Lp, int* hg_out, DecodeArgs* dp) {
+  WsLayout& L = *Lp;
   int st = check_desc(desc, &L);
   if (st != PKV_OK) return st;
   st = check_pool(pool, desc);
@@ -234,8 +236,7 @@ int decode_impl(const pkv_pool* pool, const pkv_desc* desc, const void* q, const
   if (mask && (mask_stride < 0 || mask_stride % 4 != 0 ||
                (long long)mask_stride * batch > 0x7fffffffLL))
     return PKV_ERR_INVALID_ARG;
-  if (batch == 0) return PKV_OK;
-  DecodeArgs d;
+  DecodeArgs d{};
   d.mask = mask;
   d.mask_stride = mask ? mask_stride : 0;
   d.k = static_cast<uint16_t*>(pool->k);
@@ -267,6 +268,27 @@ int decode_impl(const pkv_pool* pool, const pkv_desc* desc, const void* q, const
   d.slot_table = nullptr;
   d.table_stride = 0;
   d.num_slots = 0;
+  d.plan = 0;
+  *hg_out = hg;
+  *dp = d;
+  return PKV_OK;
+}
+
+// pkv_decode and pkv_decode_append: the same launch, with or without the
+// token to append.
+int decode_impl(const pkv_pool* pool, const pkv_desc* desc, const void* q, const void* k_new,
+                const void* v_new, const uint8_t* mask, int32_t mask_stride,
+                const int32_t* kv_indptr, const int32_t* kv_indices, int32_t num_indices,
+                const int32_t* seq_lens, int32_t batch, float sm_scale, void* workspace,
+                size_t workspace_bytes, void* out, void* stream) {
+  WsLayout L;
+  DecodeArgs d;
+  int hg = 0;
+  const int st = prepare_decode(pool, desc, q, k_new, v_new, mask, mask_stride, kv_indptr,
+                                kv_indices, num_indices, seq_lens, batch, sm_scale, workspace,
+                                workspace_bytes, out, &L, &hg, &d);
+  if (st != PKV_OK) return st;
+  if (batch == 0) return PKV_OK;
   return launch_status(
       launch_decode(d, desc->head_dim, hg, L.groups, static_cast<hipStream_t>(stream)));
 }
@@ -303,6 +325,38 @@ int pkv_decode_append(const pkv_pool* pool, const pkv_desc* desc, const void* q,
   if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
   return decode_impl(pool, desc, q, k_new, v_new, nullptr, 0, kv_indptr, kv_indices, num_indices,
                      seq_lens, batch, sm_scale, workspace, workspace_bytes, out, stream);
+}
+
+int pkv_decode_plan(const pkv_pool* pool, const pkv_desc* desc, const void* q,
+                    const void* k_new, const void* v_new, const int32_t* seq_lens, int32_t batch,
+                    int32_t forced_groups, int32_t* kv_indptr, const int32_t* kv_indices,
+                    int32_t num_indices, float sm_scale, void* workspace, size_t workspace_bytes,
+                    void* out, void* stream) {
+  WsLayout L;
+  DecodeArgs d;
+  int hg = 0;
+  if (forced_groups < 0) return PKV_ERR_INVALID_ARG;
+  int st = prepare_decode(pool, desc, q, k_new, v_new, nullptr, 0, kv_indptr, kv_indices,
+                          num_indices, seq_lens, batch, sm_scale, workspace, workspace_bytes, out,
+                          &L, &hg, &d);
+  if (st != PKV_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0 || batch > kPlanLdsRequests) {
+    // No request, or more than the planning launch keeps in LDS: the metadata
+    // kernel plans, then the decode runs on its plan (the same results).
+    st = pkv_build_metadata(desc, seq_lens, batch, forced_groups, kv_indptr, workspace,
+                            workspace_bytes, stream);
+    if (st != PKV_OK || batch == 0) return st;
+    return launch_status(launch_decode(d, desc->head_dim, hg, L.groups, s));
+  }
+  d.plan = 1;
+  d.groups = L.groups;
+  d.min_tiles = desc->min_tiles_per_group > 0 ? desc->min_tiles_per_group : kDefaultMinTiles;
+  d.forced = forced_groups;
+  d.plan_indptr = kv_indptr;
+  d.plan_waves = at<WaveRange>(workspace, L.waves);
+  d.plan_ginfo = at<GroupInfo>(workspace, L.ginfo);
+  return launch_status(launch_decode(d, desc->head_dim, hg, L.groups, s));
 }
 
 int pkv_decode_tokens(const pkv_desc* desc, const void* k_cache, const void* v_cache,

@@ -48,6 +48,7 @@
 // 16-token blocks and V^T operands are gathered element by element.
 
 #include "pkv_mfma.h"
+#include "pkv_plan.h"
 
 namespace pkv {
 namespace {
@@ -108,7 +109,7 @@ struct Combine4 {
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kCoherent = 16;
 
-template <int D, int HG, int KIND>
+template <int D, int HG, int KIND, bool PLAN>
 __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   constexpr bool APPEND = KIND == kAppend;
   constexpr bool MASKED = KIND == kMasked;
@@ -127,6 +128,11 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   __shared__ GroupInfo s_gi;  // the workgroup's merge record, for the epilogue
   __shared__ EpiloguePtrs s_ptr;
   __shared__ uint32_t s_vn[APPEND ? kWavesPerGroup : 1][kWave];  // appended V row, per wave
+  // The step's page prefix sums and lengths, when this launch plans the step.
+  __shared__ int32_t s_pip[PLAN ? kPlanLdsRequests + 1 : 1];
+  __shared__ int32_t s_plen[PLAN ? kPlanLdsRequests : 1];
+  __shared__ int s_scan[kWavesPerGroup];
+  __shared__ int s_pcount[2];  // requests without pages, error bits
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -136,28 +142,102 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int Hq = a.num_q_heads;
 
-  // The plan size, this wave's range and the workgroup's merge record are
-  // fetched together (the test reads all three, so no load waits for another):
-  // the first K/V loads wait on them, and the merges at the end need nothing
-  // else from the plan.
-  const int ngroups = a.hdr[kHdrGroups];
-  const int nempty = a.hdr[kHdrEmpty];
-  // The plan must be the one built for this call's batch and head grouping:
-  // a plan of a larger batch would send waves to requests past the caller's
-  // arrays.  On a mismatch nothing is read or written but the error word.
-  const bool plan_ok = a.hdr[kHdrBatch] == a.batch && a.hdr[kHdrUnits] == a.units;
-  const WaveRange rng = a.waves[grp * kWavesPerGroup + w];
-  const GroupInfo gi0 = a.ginfo[grp];
-  if (!plan_ok) {  // uniform over the grid
-    if (grp == 0 && tid == 0) atomicOr(&a.hdr[kHdrError], (int)kErrPlanMismatch);
-    return;
+  int ngroups, nempty;
+  WaveRange rng;
+  GroupInfo gi0;
+  if constexpr (PLAN) {
+    // The step's plan, computed here from the lengths with the arithmetic of
+    // the metadata kernel: prefix sums of page counts (in LDS), the tile count,
+    // the workgroup count, then this workgroup's merge record and each wave's
+    // range.  The launch reads its plan from LDS only; what it writes to the
+    // workspace and kv_indptr serves the calls that follow in the step.
+    if (tid == 0) {
+      s_pip[0] = 0;
+      s_pcount[0] = 0;
+      s_pcount[1] = 0;
+    }
+    __syncthreads();
+    int carry = 0, empty = 0, perr = 0;
+    for (int base = 0; base < a.batch; base += kGroupThreads) {  // uniform trip count
+      const int b = base + tid;
+      int n = 0;
+      if (b < a.batch) {
+        const int L = a.seq_lens[b];
+        s_plen[b] = L;
+        if (L < 0) perr |= kErrNegativeLength;
+        n = pages_of(L, a.page_size);
+        empty += n == 0;
+      }
+      int total;
+      const int incl = block_inclusive_scan<kGroupThreads>(n, s_scan, &total);
+      if (b < a.batch) s_pip[b + 1] = carry + incl;
+      carry += total;
+    }
+    if (empty) atomicAdd(&s_pcount[0], empty);
+    if (perr) atomicOr(&s_pcount[1], perr);
+    __syncthreads();
+    const long long T = (long long)carry * U;
+    ngroups = plan_groups(T, a.groups, a.min_tiles, a.forced);
+    nempty = s_pcount[0];
+    const Locator loc{s_pip, s_plen, a.batch, U};
+    if (T < 0x80000000LL) {
+      const PlanMath<uint32_t> pm((uint32_t)T, (uint32_t)max(ngroups, 1));
+      rng = plan_wave_range<uint32_t>(loc, pm, ngroups, grp, w);
+      if (tid < 2) plan_group_half<uint32_t>(loc, pm, ngroups, U, grp, tid, &s_gi);
+    } else {
+      const PlanMath<uint64_t> pm((uint64_t)T, (uint32_t)max(ngroups, 1));
+      rng = plan_wave_range<uint64_t>(loc, pm, ngroups, grp, w);
+      if (tid < 2) plan_group_half<uint64_t>(loc, pm, ngroups, U, grp, tid, &s_gi);
+    }
+    __syncthreads();
+    gi0 = s_gi;
+    if (lane == 0) a.plan_waves[grp * kWavesPerGroup + w] = rng;
+    if (tid == 0) a.plan_ginfo[grp] = gi0;
+    if (grp == 0) {
+      for (int b = tid; b <= a.batch; b += kGroupThreads) a.plan_indptr[b] = s_pip[b];
+      if (tid == 0) {
+        a.hdr[kHdrGroups] = ngroups;
+        a.hdr[kHdrTiles] = (int)T;
+        a.hdr[kHdrUnits] = U;
+        a.hdr[kHdrBatch] = a.batch;
+        a.hdr[kHdrEmpty] = nempty;
+        // Other workgroups may already have latched decode errors: OR, never store.
+        if (s_pcount[1]) atomicOr(&a.hdr[kHdrError], s_pcount[1]);
+      }
+    }
+  } else {
+    // The plan size, this wave's range and the workgroup's merge record are
+    // fetched together (the test reads all three, so no load waits for
+    // another): the first K/V loads wait on them, and the merges at the end
+    // need nothing else from the plan.
+    ngroups = a.hdr[kHdrGroups];
+    nempty = a.hdr[kHdrEmpty];
+    // The plan must be the one built for this call's batch and head grouping:
+    // a plan of a larger batch would send waves to requests past the caller's
+    // arrays.  On a mismatch nothing is read or written but the error word.
+    const bool plan_ok = a.hdr[kHdrBatch] == a.batch && a.hdr[kHdrUnits] == a.units;
+    rng = a.waves[grp * kWavesPerGroup + w];
+    gi0 = a.ginfo[grp];
+    if (!plan_ok) {  // uniform over the grid
+      if (grp == 0 && tid == 0) atomicOr(&a.hdr[kHdrError], (int)kErrPlanMismatch);
+      return;
+    }
   }
+  // Page prefix sum and length of request i, from LDS when this launch planned.
+  auto indptr_at = [&](int i) -> int {
+    if constexpr (PLAN) return s_pip[i];
+    else return a.kv_indptr[i];
+  };
+  auto len_at = [&](int i) -> int {
+    if constexpr (PLAN) return s_plen[i];
+    else return a.seq_lens[i];
+  };
   // Requests without tokens get zero rows (no tile covers them); workgroup 0
   // writes them, after its stream, or at once when the plan has no tile at all.
   auto zero_empty_rows = [&]() {
     if (nempty > 0 && w == 0) {
       for (int eb = lane; eb < a.batch; eb += kWave) {
-        if (a.kv_indptr[eb + 1] == a.kv_indptr[eb]) {
+        if (indptr_at(eb + 1) == indptr_at(eb)) {
           uint4* row = reinterpret_cast<uint4*>(a.out + (size_t)eb * Hq * D);
           for (int i = 0; i < Hq * D / 8; ++i) row[i] = make_uint4(0, 0, 0, 0);
         }
@@ -169,7 +249,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     return;
   }
   if (tid == 0) {  // parked in LDS until the epilogue
-    s_gi = gi0;
+    if constexpr (!PLAN) s_gi = gi0;
     s_ptr = EpiloguePtrs{a.hdr, a.counters, a.lse, a.opart};
   }
   if (lane == 0) {
@@ -471,10 +551,10 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       p = 0;
       if (++u == U) {
         u = 0;
-        do { ++b; } while (b < a.batch - 1 && a.kv_indptr[b + 1] == a.kv_indptr[b]);
-        ip0 = a.kv_indptr[b];
-        n = a.kv_indptr[b + 1] - ip0;
-        L = max(a.seq_lens[b], 0);
+        do { ++b; } while (b < a.batch - 1 && indptr_at(b + 1) == indptr_at(b));
+        ip0 = indptr_at(b);
+        n = indptr_at(b + 1) - ip0;
+        L = max(len_at(b), 0);
       }
     }
   }
@@ -720,39 +800,42 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int KIND>
+template <int D, int KIND, bool PLAN>
 hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
   const dim3 grid(groups), block(kGroupThreads);
   switch (hg) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, 1, KIND>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, KIND>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_kernel<D, 3, KIND>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, KIND>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, KIND>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<D, 1, KIND, PLAN>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, KIND, PLAN>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<D, 3, KIND, PLAN>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, KIND, PLAN>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, KIND, PLAN>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_head_dim(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
+  if (a.token_major) return launch_d<D, kTokens, false>(a, hg, groups, s);
+  if (a.k_new != nullptr) {
+    return a.plan ? launch_d<D, kAppend, true>(a, hg, groups, s)
+                  : launch_d<D, kAppend, false>(a, hg, groups, s);
+  }
+  if (a.mask != nullptr) return launch_d<D, kMasked, false>(a, hg, groups, s);
+  return a.plan ? launch_d<D, kPlain, true>(a, hg, groups, s)
+                : launch_d<D, kPlain, false>(a, hg, groups, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int hg, int groups, hipStream_t s) {
   if (groups <= 0) return hipSuccess;
-  const int kind = a.token_major ? kTokens
-                   : a.k_new != nullptr ? kAppend
-                                        : (a.mask != nullptr ? kMasked : kPlain);
-  if (head_dim == 128) {
-    if (kind == kTokens) return launch_d<128, kTokens>(a, hg, groups, s);
-    if (kind == kAppend) return launch_d<128, kAppend>(a, hg, groups, s);
-    if (kind == kMasked) return launch_d<128, kMasked>(a, hg, groups, s);
-    return launch_d<128, kPlain>(a, hg, groups, s);
-  }
-  if (head_dim == 64) {
-    if (kind == kTokens) return launch_d<64, kTokens>(a, hg, groups, s);
-    if (kind == kAppend) return launch_d<64, kAppend>(a, hg, groups, s);
-    if (kind == kMasked) return launch_d<64, kMasked>(a, hg, groups, s);
-    return launch_d<64, kPlain>(a, hg, groups, s);
-  }
+  // Planning launches cover plain and fused-append decodes of at most
+  // kPlanLdsRequests requests (the host checks).
+  if (a.plan && (a.token_major || a.mask != nullptr || a.batch > kPlanLdsRequests))
+    return hipErrorInvalidValue;
+  if (head_dim == 128) return launch_head_dim<128>(a, hg, groups, s);
+  if (head_dim == 64) return launch_head_dim<64>(a, hg, groups, s);
   return hipErrorInvalidValue;
 }
 

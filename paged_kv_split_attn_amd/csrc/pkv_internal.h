@@ -21,6 +21,9 @@ constexpr int kDefaultMinTiles = 16;  // fewer tiles per workgroup measured slow
 constexpr int kMaxBatch = 65536;
 constexpr int kMaxGroups = 65536;
 constexpr int kMetaLdsRequests = 8192;  // kv_indptr entries the metadata kernel keeps in LDS
+// Largest batch a decode that plans its own step handles in one launch (its
+// prefix sums and lengths live in LDS next to the decode's own buffers).
+constexpr int kPlanLdsRequests = 1024;
 
 // Header words at the start of the workspace (int32).
 enum HeaderWord : int {
@@ -90,6 +93,7 @@ struct MetaArgs {
   GroupInfo* ginfo;    // [groups]
   int32_t* counters;   // [segments]: arrivals for the cross-workgroup merge
   int32_t batch, page_size, units, groups, min_tiles, forced;
+  int32_t segments;    // counters of the descriptor (max_batch * units), all cleared
 };
 
 struct AppendArgs {
@@ -136,6 +140,15 @@ struct DecodeArgs {
   const int32_t* slot_table;
   int32_t table_stride;
   int32_t num_slots;
+  // Planning inside the launch (plan != 0, batch <= kPlanLdsRequests): every
+  // workgroup computes the step's plan from seq_lens in LDS, uses it at once
+  // and writes its own part of it (waves, ginfo; workgroup 0 also kv_indptr
+  // and the header) for the calls that follow in the step.
+  int32_t plan;
+  int32_t groups, min_tiles, forced;
+  int32_t* plan_indptr;
+  WaveRange* plan_waves;
+  GroupInfo* plan_ginfo;
 };
 
 struct PrefillArgs {

@@ -11,7 +11,7 @@
 // never reads seq_lens.
 #include <algorithm>
 
-#include "pkv_internal.h"
+#include "pkv_plan.h"
 
 namespace pkv {
 namespace {
@@ -25,149 +25,21 @@ constexpr int kMetaThreadsTiny = 64;
 constexpr int kMetaThreadsSmall = 256;
 constexpr int kMetaThreadsLarge = 1024;
 
-// Inclusive prefix sum over the THREADS threads of the block.  `total`
-// receives the block sum.  smem holds THREADS / 64 ints.
-template <int THREADS>
-__device__ int block_inclusive_scan(int x, int* smem, int* total) {
-  constexpr int kMetaWaves = THREADS / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
-  if (lane == kWave - 1) smem[w] = x;
-  __syncthreads();
-  if (w == 0) {
-    int v = lane < kMetaWaves ? smem[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < kMetaWaves; off <<= 1) {
-      const int y = __shfl_up(v, off, kWave);
-      if (lane >= off) v += y;
-    }
-    if (lane < kMetaWaves) smem[lane] = v;
-  }
-  __syncthreads();
-  const int prefix = w > 0 ? smem[w - 1] : 0;
-  *total = smem[kMetaWaves - 1];
-  __syncthreads();  // smem is reused by the next scan
-  return x + prefix;
-}
-
-__device__ __forceinline__ int pages_of(int len, int P) { return len > 0 ? (len + P - 1) / P : 0; }
-
-// Integer arithmetic of the plan, in I = uint32_t when the step has fewer than
-// 2^31 tiles (every division a 32-bit one) and uint64_t otherwise.  All
-// results are the exact floors the plan defines, whatever I is.
-template <typename I>
-struct PlanMath {
-  I T;         // tiles
-  uint32_t W;  // workgroups, 1 <= W <= min(T, 65536)
-  I q, r;      // T = q W + r
-  __device__ PlanMath(I tiles, uint32_t groups) : T(tiles), W(groups), q(tiles / groups),
-                                                  r(tiles % groups) {}
-  // First tile of workgroup i (i <= W): floor(i T / W) = i q + floor(i r / W),
-  // where i r <= 65536 * 65535 fits 32 bits.
-  __device__ I start(uint32_t i) const { return (I)i * q + (I)(i * (uint32_t)r / W); }
-  // floor(w len / 8) without forming w len.
-  __device__ static I part(I len, int w) {
-    return (I)w * (len >> 3) + (I)(((uint32_t)w * (uint32_t)(len & 7)) >> 3);
-  }
-  // Workgroup that owns tile t: floor(((t + 1) W - 1) / T), the largest i with
-  // start(i) <= t.  In 32-bit plans the dividend is below 2^47, so a double
-  // division is within one of the floor, and one integer check fixes it.
-  __device__ uint32_t owner(I t) const {
-    const uint64_t num = ((uint64_t)t + 1) * W - 1;
-    if constexpr (sizeof(I) == 4) {
-      uint64_t q = (uint64_t)((double)num / (double)T);
-      if (q * T > num) --q;
-      else if ((q + 1) * T <= num) ++q;
-      return (uint32_t)q;
-    } else {
-      return (uint32_t)(num / T);
-    }
-  }
-};
-
-struct Locator {
-  const int32_t* ip;  // page prefix sums (LDS copy or global)
-  const int32_t* seq_lens;  // (LDS copy or global)
-  int batch, units;
-  // (request, head group, page) of tile t < T: the request is the largest b
-  // with ip[b] * U <= t (requests without pages have empty ranges).
-  template <typename I>
-  __device__ WaveRange at(I t, int count) const {
-    int lo = 0, hi = batch;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((I)ip[mid] * (I)units <= t) lo = mid;
-      else hi = mid - 1;
-    }
-    const int n = ip[lo + 1] - ip[lo];
-    const I rr = t - (I)ip[lo] * (I)units;
-    const int u = (int)(rr / (I)n);
-    WaveRange w;
-    w.b = lo;
-    w.u = u;
-    w.p = (int)(rr - (I)u * (I)n);
-    w.count = count;
-    w.ip0 = ip[lo];
-    w.pages = n;
-    w.len = max(seq_lens[lo], 0);
-    w.pad = 0;
-    return w;
-  }
-};
-
 // Phases 2 and 3 of the metadata kernel (see there), in integer type I.  The
 // work items -- one per wave of the grid, then two per workgroup record -- are
 // dealt to the threads of all metadata workgroups.
 template <int THREADS, typename I>
 __device__ void build_plan(const MetaArgs& a, const Locator& loc, I T, int W) {
-  const int U = a.units;
   const PlanMath<I> pm(T, (uint32_t)max(W, 1));
   const int nw = a.groups * kWavesPerGroup;
   for (int x = blockIdx.x * THREADS + threadIdx.x; x < nw + 2 * a.groups;
        x += gridDim.x * THREADS) {
     if (x < nw) {
-      // Phase 2: the range of wave w of group i.  Group i covers
-      // [start(i), start(i + 1)); its wave w the w-th of kWavesPerGroup equal
-      // parts.
       const int i = x / kWavesPerGroup;
-      const int w = x - i * kWavesPerGroup;
-      WaveRange r{0, 0, 0, 0, 0, 0, 0, 0};
-      if (i < W) {
-        const I g0 = pm.start(i), len = pm.start(i + 1) - g0;
-        const I t0 = g0 + PlanMath<I>::part(len, w);
-        const I t1 = g0 + PlanMath<I>::part(len, w + 1);
-        if (t1 > t0) r = loc.at(t0, (int)(t1 - t0));
-      }
-      a.waves[x] = r;
+      a.waves[x] = plan_wave_range<I>(loc, pm, W, i, x - i * kWavesPerGroup);
     } else {
-      // Phase 3: half k of the merge record of group i (two threads per
-      // group): its first (k = 0) or last (k = 1) segment (b * U + u), and the
-      // workgroups that segment's tiles span.  A segment is the first segment
-      // of a workgroup exactly when that workgroup's range starts inside it.
       const int i = (x - nw) >> 1, k = (x - nw) & 1;
-      int seg = -1, lo = 0, hi = -1, slot = 0;
-      const I g0 = i < W ? pm.start(i) : 0;
-      const I g1 = i < W ? pm.start(i + 1) : 0;
-      if (g1 > g0) {
-        const WaveRange e = loc.at(k == 0 ? g0 : g1 - 1, 0);
-        const I t0 = (I)e.ip0 * (I)U + (I)e.u * (I)e.pages;
-        const I t1 = t0 + (I)(e.pages - 1);
-        const uint32_t l = pm.owner(t0);
-        seg = e.b * U + e.u;
-        lo = (int)l;
-        hi = (int)pm.owner(t1);
-        slot = pm.start(l) >= t0 ? 0 : 1;
-      }
-      GroupInfo& gi = a.ginfo[i];
-      gi.seg[k] = seg;
-      gi.lo[k] = lo;
-      gi.hi[k] = hi;
-      gi.slot_lo[k] = slot;
+      plan_group_half<I>(loc, pm, W, a.units, i, k, &a.ginfo[i]);
     }
   }
 }
@@ -217,16 +89,7 @@ __global__ void __launch_bounds__(THREADS) metadata_kernel(MetaArgs a) {
 
   const int U = a.units;
   const long long T = (long long)carry * U;
-  int W = 0;
-  if (T > 0) {
-    if (a.forced > 0) {
-      W = min(a.forced, a.groups);
-      if ((long long)W > T) W = (int)T;  // every workgroup gets at least one tile
-    } else {
-      const long long want = (T + a.min_tiles - 1) / a.min_tiles;
-      W = (int)(want < a.groups ? want : a.groups);
-    }
-  }
+  const int W = plan_groups(T, a.groups, a.min_tiles, a.forced);
   // The searches read the prefix sums from LDS when they fit there (a
   // separate instantiation, so that they compile to LDS loads).
   const bool small = T < 0x80000000LL;
@@ -241,8 +104,10 @@ __global__ void __launch_bounds__(THREADS) metadata_kernel(MetaArgs a) {
   }
 
   if (!lead) return;
-  // Phase 4: arrival counters of the cross-workgroup merge.
-  for (int sgi = tid; sgi < a.batch * U; sgi += THREADS) a.counters[sgi] = 0;
+  // Phase 4: arrival counters of the cross-workgroup merge, all of the
+  // descriptor's (every decode leaves them at zero again, so a later step of
+  // any batch, planned in its decode launch, finds them cleared).
+  for (int sgi = tid; sgi < a.segments; sgi += THREADS) a.counters[sgi] = 0;
 
   if (err) atomicOr(&s_err, err);
   if (empty) atomicAdd(&s_empty, empty);

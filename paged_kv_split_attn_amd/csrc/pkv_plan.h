@@ -1,0 +1,164 @@
+// Device-side planning shared by the metadata kernel and the decode that
+// plans its own step: prefix sums of page counts, the split of the step's
+// tiles into workgroup and wave ranges, and the workgroups' merge records.
+// The plan cuts the step's tiles (request, head group, page) into equal
+// contiguous ranges, one per workgroup and one per wave (the pages tuned their
+// split count to the number of blocks that saturates bandwidth: commits by
+// ViperEkura, compute_num_splits bullets).
+#pragma once
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+// Inclusive prefix sum over the THREADS threads of the block.  `total`
+// receives the block sum.  smem holds THREADS / 64 ints.
+template <int THREADS>
+__device__ int block_inclusive_scan(int x, int* smem, int* total) {
+  constexpr int kMetaWaves = THREADS / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) smem[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int v = lane < kMetaWaves ? smem[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kMetaWaves; off <<= 1) {
+      const int y = __shfl_up(v, off, kWave);
+      if (lane >= off) v += y;
+    }
+    if (lane < kMetaWaves) smem[lane] = v;
+  }
+  __syncthreads();
+  const int prefix = w > 0 ? smem[w - 1] : 0;
+  *total = smem[kMetaWaves - 1];
+  __syncthreads();  // smem is reused by the next scan
+  return x + prefix;
+}
+
+__device__ __forceinline__ int pages_of(int len, int P) { return len > 0 ? (len + P - 1) / P : 0; }
+
+// Integer arithmetic of the plan, in I = uint32_t when the step has fewer than
+// 2^31 tiles (every division a 32-bit one) and uint64_t otherwise.  All
+// results are the exact floors the plan defines, whatever I is.
+template <typename I>
+struct PlanMath {
+  I T;         // tiles
+  uint32_t W;  // workgroups, 1 <= W <= min(T, 65536)
+  I q, r;      // T = q W + r
+  __device__ PlanMath(I tiles, uint32_t groups) : T(tiles), W(groups), q(tiles / groups),
+                                                  r(tiles % groups) {}
+  // First tile of workgroup i (i <= W): floor(i T / W) = i q + floor(i r / W),
+  // where i r <= 65536 * 65535 fits 32 bits.
+  __device__ I start(uint32_t i) const { return (I)i * q + (I)(i * (uint32_t)r / W); }
+  // floor(w len / 8) without forming w len.
+  __device__ static I part(I len, int w) {
+    return (I)w * (len >> 3) + (I)(((uint32_t)w * (uint32_t)(len & 7)) >> 3);
+  }
+  // Workgroup that owns tile t: floor(((t + 1) W - 1) / T), the largest i with
+  // start(i) <= t.  In 32-bit plans the dividend is below 2^47, so a double
+  // division is within one of the floor, and one integer check fixes it.
+  __device__ uint32_t owner(I t) const {
+    const uint64_t num = ((uint64_t)t + 1) * W - 1;
+    if constexpr (sizeof(I) == 4) {
+      uint64_t q = (uint64_t)((double)num / (double)T);
+      if (q * T > num) --q;
+      else if ((q + 1) * T <= num) ++q;
+      return (uint32_t)q;
+    } else {
+      return (uint32_t)(num / T);
+    }
+  }
+};
+
+struct Locator {
+  const int32_t* ip;  // page prefix sums (LDS copy or global)
+  const int32_t* seq_lens;  // (LDS copy or global)
+  int batch, units;
+  // (request, head group, page) of tile t < T: the request is the largest b
+  // with ip[b] * U <= t (requests without pages have empty ranges).
+  template <typename I>
+  __device__ WaveRange at(I t, int count) const {
+    int lo = 0, hi = batch;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((I)ip[mid] * (I)units <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    const int n = ip[lo + 1] - ip[lo];
+    const I rr = t - (I)ip[lo] * (I)units;
+    const int u = (int)(rr / (I)n);
+    WaveRange w;
+    w.b = lo;
+    w.u = u;
+    w.p = (int)(rr - (I)u * (I)n);
+    w.count = count;
+    w.ip0 = ip[lo];
+    w.pages = n;
+    w.len = max(seq_lens[lo], 0);
+    w.pad = 0;
+    return w;
+  }
+};
+
+// Workgroups of a plan of T tiles: min(groups, ceil(T / min_tiles)), or
+// min(forced, groups, T) when forced > 0; 0 when there is no tile.
+__device__ __forceinline__ int plan_groups(long long T, int groups, int min_tiles, int forced) {
+  if (T <= 0) return 0;
+  if (forced > 0) {
+    const int W = min(forced, groups);
+    return (long long)W > T ? (int)T : W;  // every workgroup gets at least one tile
+  }
+  const long long want = (T + min_tiles - 1) / min_tiles;
+  return (int)(want < groups ? want : groups);
+}
+
+// Range of wave w of workgroup i: workgroup i covers [start(i), start(i + 1));
+// its wave w the w-th of kWavesPerGroup equal parts.  Empty past the plan.
+template <typename I>
+__device__ WaveRange plan_wave_range(const Locator& loc, const PlanMath<I>& pm, int W, int i,
+                                     int w) {
+  WaveRange r{0, 0, 0, 0, 0, 0, 0, 0};
+  if (i < W) {
+    const I g0 = pm.start(i), len = pm.start(i + 1) - g0;
+    const I t0 = g0 + PlanMath<I>::part(len, w);
+    const I t1 = g0 + PlanMath<I>::part(len, w + 1);
+    if (t1 > t0) r = loc.at(t0, (int)(t1 - t0));
+  }
+  return r;
+}
+
+// Half k of the merge record of workgroup i: its first (k = 0) or last (k = 1)
+// segment (b * U + u), and the workgroups that segment's tiles span.  A
+// segment is the first segment of a workgroup exactly when that workgroup's
+// range starts inside it.
+template <typename I>
+__device__ void plan_group_half(const Locator& loc, const PlanMath<I>& pm, int W, int U, int i,
+                                int k, GroupInfo* gi) {
+  int seg = -1, lo = 0, hi = -1, slot = 0;
+  const I g0 = i < W ? pm.start(i) : 0;
+  const I g1 = i < W ? pm.start(i + 1) : 0;
+  if (g1 > g0) {
+    const WaveRange e = loc.at(k == 0 ? g0 : g1 - 1, 0);
+    const I t0 = (I)e.ip0 * (I)U + (I)e.u * (I)e.pages;
+    const I t1 = t0 + (I)(e.pages - 1);
+    const uint32_t l = pm.owner(t0);
+    seg = e.b * U + e.u;
+    lo = (int)l;
+    hi = (int)pm.owner(t1);
+    slot = pm.start(l) >= t0 ? 0 : 1;
+  }
+  gi->seg[k] = seg;
+  gi->lo[k] = lo;
+  gi->hi[k] = hi;
+  gi->slot_lo[k] = slot;
+}
+
+}  // namespace
+}  // namespace pkv

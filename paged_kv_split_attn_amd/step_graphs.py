@@ -1,8 +1,10 @@
 """Whole-step hipGraph harness: one captured graph per power-of-two batch size.
 
-A decode step of an N-layer model's attention is one pkv_build_metadata
-followed by one pkv_decode_append per layer (the layer's new K/V token is
-written into its pool and attended in the same launch).  The pages capture
+A decode step of an N-layer model's attention is one launch per layer: the
+first layer's pkv_decode_plan builds the step's plan and kv_indptr (what
+pkv_build_metadata does) in the same launch as its fused append + decode, and
+every later layer's pkv_decode_append runs on that plan (each layer's new K/V
+token is written into its pool and attended in the same launch).  The pages capture
 such steps once per power-of-two batch size at start-up and replay them with
 every input at a fixed workspace address (AstrAI commit 05739629,
 astrai/inference: the _warmup_cuda_graphs and CudaGraphContext bullets).
@@ -27,7 +29,8 @@ from typing import List, Optional, Sequence
 
 import torch
 
-from . import Desc, Pool, pkv_build_metadata, pkv_decode_append, pkv_workspace_bytes
+from . import Desc, Pool, pkv_build_metadata, pkv_decode_append, pkv_decode_plan, \
+    pkv_workspace_bytes
 
 
 def buckets_up_to(max_batch: int) -> List[int]:
@@ -53,6 +56,9 @@ class _Bucket:
         self.kv_indices = torch.zeros(max(1, max_pages), **i32)
         self.kv_indptr = torch.zeros(B + 1, **i32)
         self.ws = torch.zeros(pkv_workspace_bytes(self.desc), dtype=torch.uint8, device=device)
+        # one metadata build: every arrival counter starts at zero (the planning
+        # launch relies on it, and every decode leaves them so)
+        pkv_build_metadata(self.desc, self.seq_lens, 0, self.kv_indptr, self.ws)
         bf = dict(dtype=torch.int16, device=device)
         self.q = torch.zeros((layers, B, Hq, D), **bf)
         self.k_new = torch.zeros((layers, B, Hkv, D), **bf)
@@ -86,11 +92,15 @@ class StepGraphs:
         raise ValueError(f"batch {n} above the largest bucket {max(self.buckets)}")
 
     def _step_on(self, bk: _Bucket, stream) -> None:
-        pkv_build_metadata(bk.desc, bk.seq_lens, 0, bk.kv_indptr, bk.ws, stream)
         for layer, pool in enumerate(self.pools):
-            pkv_decode_append(pool, bk.desc, bk.q[layer], bk.k_new[layer], bk.v_new[layer],
-                              bk.kv_indptr, bk.kv_indices, bk.seq_lens, self.sm_scale, bk.ws,
-                              bk.out[layer], stream)
+            if layer == 0:
+                pkv_decode_plan(pool, bk.desc, bk.q[0], bk.k_new[0], bk.v_new[0], bk.seq_lens, 0,
+                                bk.kv_indptr, bk.kv_indices, self.sm_scale, bk.ws, bk.out[0],
+                                stream)
+            else:
+                pkv_decode_append(pool, bk.desc, bk.q[layer], bk.k_new[layer], bk.v_new[layer],
+                                  bk.kv_indptr, bk.kv_indices, bk.seq_lens, self.sm_scale, bk.ws,
+                                  bk.out[layer], stream)
 
     def capture(self) -> None:
         """Capture every bucket's step (after one eager run of it on a side stream).

@@ -24,7 +24,8 @@ def test_header_declares_expected_entry_points():
     names = pkv.declared_functions()
     assert set(names) == {
         "pkv_status_str", "pkv_version", "pkv_workspace_bytes", "pkv_build_metadata",
-        "pkv_append_kv", "pkv_append_kv_ragged", "pkv_decode", "pkv_decode_append", "pkv_decode_masked",
+        "pkv_append_kv", "pkv_append_kv_ragged", "pkv_decode", "pkv_decode_append", "pkv_decode_plan",
+        "pkv_decode_masked",
         "pkv_decode_tokens", "pkv_prefill", "pkv_decode_scratch", "pkv_debug_validate", "pkv_debug_read_ceiling"}
 
 
@@ -51,7 +52,7 @@ def test_status_strings_and_version(lib):
     for st in range(1, 7):
         assert pkv.pkv_status_str(st) not in ("ok", "unknown status")
     assert pkv.pkv_status_str(99) == "unknown status"
-    assert pkv.pkv_version() >> 16 == 2 and pkv.pkv_version() & 0xffff >= 2
+    assert pkv.pkv_version() >> 16 == 2 and pkv.pkv_version() & 0xffff >= 6
 
 
 def _desc(**kw):
@@ -157,6 +158,18 @@ def test_host_checks_reject_before_launch(lib):
     assert _raw(lib, "pkv_decode_scratch", B(pool), B(d), fake, fake, fake, 10, 17, 0.1, fake,
                 fake, None) == 4
     assert pkv.pkv_status_str(pkv.PKV_ERR_SCRATCH_TOO_SMALL).startswith("the descriptor needs")
+    # planning decode: no lengths, no kv_indptr, one of k_new / v_new, a
+    # negative forced count, batch above capacity, a small workspace
+    args = lambda **kw: [B(pool), B(d), kw.get("q", fake), kw.get("kn", fake), kw.get("vn", fake),
+                         kw.get("sl", fake), kw.get("b", 4), kw.get("f", 0), kw.get("ip", fake),
+                         fake, 10, 0.1, fake, kw.get("ws", ws_bytes), fake, None]
+    assert _raw(lib, "pkv_decode_plan", *args(sl=None)) == 1
+    assert _raw(lib, "pkv_decode_plan", *args(ip=None)) == 1
+    assert _raw(lib, "pkv_decode_plan", *args(vn=None)) == 1
+    assert _raw(lib, "pkv_decode_plan", *args(f=-1)) == 1
+    assert _raw(lib, "pkv_decode_plan", *args(b=17)) == 4
+    assert _raw(lib, "pkv_decode_plan", *args(ws=ws_bytes - 1)) == 3
+    assert _raw(lib, "pkv_decode_plan", *args(q=None)) == 1
     # extend append: no query offsets, negative row bound, odd head_dim, a grid
     # of 2^31 workgroups or more
     assert _raw(lib, "pkv_append_kv_ragged", B(pool), fake, fake, None, fake, fake, 10, fake, 4,
