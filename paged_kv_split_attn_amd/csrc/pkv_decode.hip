@@ -145,66 +145,87 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   int ngroups, nempty;
   WaveRange rng;
   GroupInfo gi0;
+  long long ptiles = 0;  // planning launch: tiles of the plan
+  int perr_bits = 0;     // and its error bits
   if constexpr (PLAN) {
     // The step's plan, computed here from the lengths with the arithmetic of
-    // the metadata kernel: prefix sums of page counts (in LDS), the tile count,
-    // the workgroup count, then this workgroup's merge record and each wave's
-    // range.  The launch reads its plan from LDS only; what it writes to the
-    // workspace and kv_indptr serves the calls that follow in the step.
-    if (tid == 0) {
-      s_pip[0] = 0;
-      s_pcount[0] = 0;
-      s_pcount[1] = 0;
-    }
-    __syncthreads();
-    int carry = 0, empty = 0, perr = 0;
-    for (int base = 0; base < a.batch; base += kGroupThreads) {  // uniform trip count
-      const int b = base + tid;
-      int n = 0;
-      if (b < a.batch) {
-        const int L = a.seq_lens[b];
-        s_plen[b] = L;
-        if (L < 0) perr |= kErrNegativeLength;
-        n = pages_of(L, a.page_size);
-        empty += n == 0;
+    // the metadata kernel: prefix sums of page counts, the tile count, the
+    // workgroup count and each wave's range (this workgroup's merge record is
+    // only needed at the end, and is made there).  The launch reads its plan
+    // from registers and LDS only; what it stores for the step's later calls
+    // goes out at the end.
+    int carry = 0;
+    if (a.batch <= kWave) {
+      // Every wave plans on its own, the requests on its lanes: no barrier.
+      const int Lb = lane < a.batch ? a.seq_lens[lane] : 0;
+      const int nb = pages_of(Lb, a.page_size);
+      int incl = nb;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += y;
       }
-      int total;
-      const int incl = block_inclusive_scan<kGroupThreads>(n, s_scan, &total);
-      if (b < a.batch) s_pip[b + 1] = carry + incl;
-      carry += total;
-    }
-    if (empty) atomicAdd(&s_pcount[0], empty);
-    if (perr) atomicOr(&s_pcount[1], perr);
-    __syncthreads();
-    const long long T = (long long)carry * U;
-    ngroups = plan_groups(T, a.groups, a.min_tiles, a.forced);
-    nempty = s_pcount[0];
-    const Locator loc{s_pip, s_plen, a.batch, U};
-    if (T < 0x80000000LL) {
-      const PlanMath<uint32_t> pm((uint32_t)T, (uint32_t)max(ngroups, 1));
-      rng = plan_wave_range<uint32_t>(loc, pm, ngroups, grp, w);
-      if (tid < 2) plan_group_half<uint32_t>(loc, pm, ngroups, U, grp, tid, &s_gi);
+      carry = __shfl(incl, kWave - 1, kWave);
+      if (lane < a.batch) {
+        s_plen[lane] = Lb;
+        s_pip[lane + 1] = incl;
+      }
+      if (lane == 0) s_pip[0] = 0;  // every wave writes the same values
+      nempty = (int)__popcll(__ballot(lane < a.batch && nb == 0));
+      perr_bits = __ballot(lane < a.batch && Lb < 0) ? (int)kErrNegativeLength : 0;
+      const long long T = (long long)carry * U;
+      ngroups = plan_groups(T, a.groups, a.min_tiles, a.forced);
+      ptiles = T;
+      const WaveLocator loc{incl - nb, nb, Lb, a.batch, U};
+      if (T < 0x80000000LL) {
+        const PlanMath<uint32_t> pm((uint32_t)T, (uint32_t)max(ngroups, 1));
+        rng = plan_wave_range<uint32_t>(loc, pm, ngroups, grp, w);
+      } else {
+        const PlanMath<uint64_t> pm((uint64_t)T, (uint32_t)max(ngroups, 1));
+        rng = plan_wave_range<uint64_t>(loc, pm, ngroups, grp, w);
+      }
     } else {
-      const PlanMath<uint64_t> pm((uint64_t)T, (uint32_t)max(ngroups, 1));
-      rng = plan_wave_range<uint64_t>(loc, pm, ngroups, grp, w);
-      if (tid < 2) plan_group_half<uint64_t>(loc, pm, ngroups, U, grp, tid, &s_gi);
-    }
-    __syncthreads();
-    gi0 = s_gi;
-    if (lane == 0) a.plan_waves[grp * kWavesPerGroup + w] = rng;
-    if (tid == 0) a.plan_ginfo[grp] = gi0;
-    if (grp == 0) {
-      for (int b = tid; b <= a.batch; b += kGroupThreads) a.plan_indptr[b] = s_pip[b];
+      // A block-wide scan over the requests, the prefix sums in LDS.
       if (tid == 0) {
-        a.hdr[kHdrGroups] = ngroups;
-        a.hdr[kHdrTiles] = (int)T;
-        a.hdr[kHdrUnits] = U;
-        a.hdr[kHdrBatch] = a.batch;
-        a.hdr[kHdrEmpty] = nempty;
-        // Other workgroups may already have latched decode errors: OR, never store.
-        if (s_pcount[1]) atomicOr(&a.hdr[kHdrError], s_pcount[1]);
+        s_pip[0] = 0;
+        s_pcount[0] = 0;
+        s_pcount[1] = 0;
+      }
+      __syncthreads();
+      int empty = 0, perr = 0;
+      for (int base = 0; base < a.batch; base += kGroupThreads) {  // uniform trip count
+        const int b = base + tid;
+        int n = 0;
+        if (b < a.batch) {
+          const int L = a.seq_lens[b];
+          s_plen[b] = L;
+          if (L < 0) perr |= kErrNegativeLength;
+          n = pages_of(L, a.page_size);
+          empty += n == 0;
+        }
+        int total;
+        const int incl = block_inclusive_scan<kGroupThreads>(n, s_scan, &total);
+        if (b < a.batch) s_pip[b + 1] = carry + incl;
+        carry += total;
+      }
+      if (empty) atomicAdd(&s_pcount[0], empty);
+      if (perr) atomicOr(&s_pcount[1], perr);
+      __syncthreads();
+      const long long T = (long long)carry * U;
+      ngroups = plan_groups(T, a.groups, a.min_tiles, a.forced);
+      ptiles = T;
+      nempty = s_pcount[0];
+      perr_bits = s_pcount[1];
+      const Locator loc{s_pip, s_plen, a.batch, U};
+      if (T < 0x80000000LL) {
+        const PlanMath<uint32_t> pm((uint32_t)T, (uint32_t)max(ngroups, 1));
+        rng = plan_wave_range<uint32_t>(loc, pm, ngroups, grp, w);
+      } else {
+        const PlanMath<uint64_t> pm((uint64_t)T, (uint32_t)max(ngroups, 1));
+        rng = plan_wave_range<uint64_t>(loc, pm, ngroups, grp, w);
       }
     }
+    gi0 = GroupInfo{{-1, -1}, {0, 0}, {0, 0}, {0, 0}};  // made at the end
   } else {
     // The plan size, this wave's range and the workgroup's merge record are
     // fetched together (the test reads all three, so no load waits for
@@ -244,8 +265,53 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       }
     }
   };
+  // Planning launch: this workgroup's merge record, made by wave 0 (lanes 0
+  // and 1, one half each) from the prefix sums in LDS, which that wave wrote
+  // itself or saw complete at a barrier.
+  auto make_group_info = [&]() {
+    if constexpr (PLAN) {
+      if (w == 0 && lane < 2) {
+        const Locator loc{s_pip, s_plen, a.batch, U};
+        if (ptiles < 0x80000000LL) {
+          const PlanMath<uint32_t> pm((uint32_t)ptiles, (uint32_t)max(ngroups, 1));
+          plan_group_half<uint32_t>(loc, pm, ngroups, U, grp, lane, &s_gi);
+        } else {
+          const PlanMath<uint64_t> pm((uint64_t)ptiles, (uint32_t)max(ngroups, 1));
+          plan_group_half<uint64_t>(loc, pm, ngroups, U, grp, lane, &s_gi);
+        }
+      }
+    }
+  };
+  // The plan this launch made, stored for the step's later calls (nothing in
+  // this launch reads it back): each wave its range, wave 0 the merge record
+  // (after make_group_info) and, in workgroup 0, kv_indptr and the header.
+  // Stores count with loads in a wave's vector-memory counter, so they go out
+  // after the wave's last load: issued before the K/V stream, every wait for a
+  // K/V step would also wait for them to be acknowledged.
+  auto store_plan = [&]() {
+    if constexpr (PLAN) {
+      if (lane == 0) a.plan_waves[grp * kWavesPerGroup + w] = rng;
+      if (w == 0) {
+        if (lane == 0) a.plan_ginfo[grp] = s_gi;
+        if (grp == 0) {
+          for (int b = lane; b <= a.batch; b += kWave) a.plan_indptr[b] = s_pip[b];
+          if (lane == 0) {
+            a.hdr[kHdrGroups] = ngroups;
+            a.hdr[kHdrTiles] = (int)ptiles;
+            a.hdr[kHdrUnits] = U;
+            a.hdr[kHdrBatch] = a.batch;
+            a.hdr[kHdrEmpty] = nempty;
+            // Other workgroups may already have latched decode errors: OR, never store.
+            if (perr_bits) atomicOr(&a.hdr[kHdrError], perr_bits);
+          }
+        }
+      }
+    }
+  };
   if ((grp >= ngroups) | (rng.count < 0) | (gi0.seg[0] < -1)) {  // uniform over the workgroup
     if (grp == 0) zero_empty_rows();
+    make_group_info();
+    store_plan();
     return;
   }
   if (tid == 0) {  // parked in LDS until the epilogue
@@ -287,6 +353,32 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   int b = rng.b, u = rng.u, p = rng.p, left = rng.count, piece = 0;
   int ip0 = rng.ip0, n = rng.pages, L = rng.len;  // request b (reloaded when b changes)
   MfmaWave<D, HG> st;
+  // Fused append: the appended token's rows (K one 8-channel chunk per lane,
+  // V two channels per lane), fetched when a piece reaches a request's last
+  // page, and the pool slot they still have to be written to (page -1: none).
+  // The pool write waits until the wave's loads are all issued: a store counts
+  // with loads in the wave's vector-memory counter, so one issued mid-stream
+  // would hold up every later wait for a K/V step until it is acknowledged.
+  uint4 knew4 = make_uint4(0, 0, 0, 0);
+  uint32_t vnew2 = 0;
+  int pend_page = -1, pend_head = 0, pend_sub = 0, pend_tok = 0;
+  auto flush_token = [&]() {
+    if constexpr (APPEND) {
+      if (pend_page >= 0) {
+        const size_t off = (size_t)pend_page * a.num_kv_heads * tile_b +
+                           (size_t)pend_head * tile_b + (size_t)pend_sub * kStepBytes;
+        if (lane < D / 8)  // K chunk `lane` of the token: [D/8][16][8] step layout
+          *reinterpret_cast<uint4*>(const_cast<char*>(kbase) + off +
+                                    ((size_t)lane * 16 + pend_tok) * 16) = knew4;
+        uint16_t* vcol = reinterpret_cast<uint16_t*>(const_cast<char*>(vbase) + off);
+        if (lane < D / 2) {  // V channels 2 lane, 2 lane + 1: [D][16] step layout
+          vcol[(size_t)(2 * lane) * 16 + pend_tok] = (uint16_t)(vnew2 & 0xffffu);
+          vcol[(size_t)(2 * lane + 1) * 16 + pend_tok] = (uint16_t)(vnew2 >> 16);
+        }
+        pend_page = -1;
+      }
+    }
+  };
   while (left > 0) {  // one piece = the part of segment (b, u) inside this wave's range
     const int len = min(left, n - p);
     if (len <= 0) break;  // only reachable with metadata that does not match kv_indptr
@@ -311,11 +403,15 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     const uint16_t* vnew_row = fuse_append ? a.v_new + new_off : a.v;
     const bool writer = hq0 % G == 0;  // first head group of KV head g
     const int mask_row = MASKED ? b * a.mask_stride : 0;  // byte offset of request b's keep row
-    // V row of the appended token, two channels per lane, fetched when this
-    // piece reaches the request's last page.
-    uint32_t vnew2 = 0;
+    // Rows of the appended token, fetched when this piece reaches the
+    // request's last page (a write still pending from an earlier request goes
+    // out first: it needs these registers).
     if constexpr (APPEND) {
-      if (p + len == n && lane < D / 2) vnew2 = reinterpret_cast<const uint32_t*>(vnew_row)[lane];
+      if (p + len == n) {
+        flush_token();
+        if (lane < D / 2) vnew2 = reinterpret_cast<const uint32_t*>(vnew_row)[lane];
+        if (lane < D / 8) knew4 = reinterpret_cast<const uint4*>(knew_row)[lane];
+      }
     }
 
     // Token-major K/V: blocks of 4 steps, lane i holding the slot of token
@@ -404,14 +500,9 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         const size_t base = (size_t)(pid < 0 ? 0 : pid) * a.num_kv_heads * tile_b + head_b;
         const char* kp = kbase + base + (size_t)sub * kStepBytes + k_boff;
         const char* vp = vbase + base + (size_t)sub * kStepBytes + v_boff;
-        const int tok = fresh_token(j);
-        // The lanes of the appended token read its K row from k_new.
-        const bool knew = tok >= 0 && r16 == tok;
-        const char* kq = knew ? knew_row + g4 * 16 : kp;
-        const size_t kstride = knew ? 4 * 16 : 4 * 16 * 16;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
-          sd.k[kk] = *reinterpret_cast<const uint4*>(kq + (size_t)kk * kstride);
+          sd.k[kk] = *reinterpret_cast<const uint4*>(kp + (size_t)kk * 4 * 16 * 16);
 #pragma unroll
         for (int vb = 0; vb < D / 16; ++vb)
           sd.v[vb] = *reinterpret_cast<const uint2*>(vp + (size_t)vb * 16 * 16 * 2);
@@ -442,12 +533,22 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
           st.step(sd, live, g4, a.scale_log2, bias);
           return;
         }
-        // Lanes whose four V tokens include the appended one take its value
-        // from v_new (in place: the ring slot is reloaded after this step).
-        // The row, fetched at the start of the piece two channels per lane,
-        // is passed between lanes through this wave's LDS row.  The KV head's
-        // first head group also writes the token into the pool (K row from
-        // the lanes that read it, V column from these lanes).
+        // The appended token replaces what the pool slot held (in place: the
+        // ring slot is reloaded after this step).  K: the lanes of token tok
+        // take chunk 4 kk + g4 of the row from the lane that fetched it.  V:
+        // the lanes whose four tokens include it take their channel's value,
+        // passed between lanes through this wave's LDS row.  The KV head's
+        // first head group also marks the token for its pool write.
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+          const int src = 4 * kk + g4;
+          uint4 x;
+          x.x = (uint32_t)__shfl((int)knew4.x, src, kWave);
+          x.y = (uint32_t)__shfl((int)knew4.y, src, kWave);
+          x.z = (uint32_t)__shfl((int)knew4.z, src, kWave);
+          x.w = (uint32_t)__shfl((int)knew4.w, src, kWave);
+          if (r16 == tok) sd.k[kk] = x;
+        }
         if (lane < D / 2) s_vn[w][lane] = vnew2;
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const uint16_t* vrow = reinterpret_cast<const uint16_t*>(&s_vn[w][0]);
@@ -466,21 +567,10 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
           }
         }
         if (writer && pid >= 0) {
-          const size_t base = (size_t)pid * a.num_kv_heads * tile_b + head_b;
-          if (r16 == tok) {  // token tok of step sub of the page
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk)
-              *reinterpret_cast<uint4*>(const_cast<char*>(kbase) + base +
-                                        (size_t)sub * kStepBytes +
-                                        ((size_t)(4 * kk + g4) * 16 + tok) * 16) = sd.k[kk];
-          }
-          if (vlane) {
-#pragma unroll
-            for (int vb = 0; vb < D / 16; ++vb)
-              *reinterpret_cast<uint16_t*>(const_cast<char*>(vbase) + base +
-                                           (size_t)sub * kStepBytes +
-                                           ((size_t)(16 * vb + r16) * 16 + tok) * 2) = vn[vb];
-          }
+          pend_page = pid;
+          pend_head = g;
+          pend_sub = sub;
+          pend_tok = tok;
         }
         st.step(sd, live, g4, a.scale_log2, bias);
       };
@@ -558,8 +648,10 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       }
     }
   }
+  flush_token();
   if (grp == 0) zero_empty_rows();
-  __syncthreads();  // also publishes s_gi and s_ptr, written before the loop
+  make_group_info();
+  __syncthreads();  // also publishes s_gi and s_ptr
   const GroupInfo gi = s_gi;
   float* const lse_p = uniform_ptr(s_ptr.lse);
   float* const opart_p = uniform_ptr(s_ptr.opart);
@@ -677,6 +769,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // Cross-workgroup merge: publish the partials, count arrivals, and let the
   // last workgroup of each segment combine every workgroup's partial in order.
   // Lanes 0 and 1 arrive for the first and the last segment at the same time.
+  store_plan();
   wait_stores();
   __syncthreads();
   if (tid < 2) {

@@ -107,6 +107,37 @@ struct Locator {
   }
 };
 
+// The same search when the requests are the lanes of one wave (batch <= 64):
+// lane b holds request b's page prefix sum, page count and length, and one
+// ballot finds the request (the lanes with prefix * U <= t form a prefix of
+// the wave, since the prefix sums do not decrease).
+struct WaveLocator {
+  int excl;   // this lane's request: pages of the requests before it
+  int pages;  // its pages
+  int len;    // its length (tokens, may be negative)
+  int batch, units;
+  template <typename I>
+  __device__ WaveRange at(I t, int count) const {
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool before = lane < batch && (I)excl * (I)units <= t;
+    const int b = __popcll(__ballot(before)) - 1;
+    const int ip0 = __shfl(excl, b, kWave);
+    const int n = __shfl(pages, b, kWave);
+    const I rr = t - (I)ip0 * (I)units;
+    const int u = (int)(rr / (I)n);
+    WaveRange w;
+    w.b = b;
+    w.u = u;
+    w.p = (int)(rr - (I)u * (I)n);
+    w.count = count;
+    w.ip0 = ip0;
+    w.pages = n;
+    w.len = max(__shfl(len, b, kWave), 0);
+    w.pad = 0;
+    return w;
+  }
+};
+
 // Workgroups of a plan of T tiles: min(groups, ceil(T / min_tiles)), or
 // min(forced, groups, T) when forced > 0; 0 when there is no tile.
 __device__ __forceinline__ int plan_groups(long long T, int groups, int min_tiles, int forced) {
@@ -115,14 +146,18 @@ __device__ __forceinline__ int plan_groups(long long T, int groups, int min_tile
     const int W = min(forced, groups);
     return (long long)W > T ? (int)T : W;  // every workgroup gets at least one tile
   }
-  const long long want = (T + min_tiles - 1) / min_tiles;
+  // ceil(T / min_tiles), in 32-bit arithmetic when T leaves room for it
+  const long long want = T < 0x40000000LL
+                             ? (long long)(((uint32_t)T + (uint32_t)min_tiles - 1u) /
+                                           (uint32_t)min_tiles)
+                             : (T + min_tiles - 1) / min_tiles;
   return (int)(want < groups ? want : groups);
 }
 
 // Range of wave w of workgroup i: workgroup i covers [start(i), start(i + 1));
 // its wave w the w-th of kWavesPerGroup equal parts.  Empty past the plan.
-template <typename I>
-__device__ WaveRange plan_wave_range(const Locator& loc, const PlanMath<I>& pm, int W, int i,
+template <typename I, typename Loc>
+__device__ WaveRange plan_wave_range(const Loc& loc, const PlanMath<I>& pm, int W, int i,
                                      int w) {
   WaveRange r{0, 0, 0, 0, 0, 0, 0, 0};
   if (i < W) {
