@@ -123,7 +123,6 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   __shared__ float s_l[kWavesPerGroup][2][HG];
   __shared__ int s_seg[kWavesPerGroup][2];
   __shared__ __align__(16) float s_out[kWavesPerGroup][HG][D];  // per-wave transpose of finished rows
-  __shared__ int s_glob[2];   // segments this workgroup left as global partials
   __shared__ int s_merge[2];  // of those, the ones this workgroup merges
   __shared__ GroupInfo s_gi;  // the workgroup's merge record, for the epilogue
   __shared__ EpiloguePtrs s_ptr;
@@ -322,7 +321,6 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     s_seg[w][0] = -1;
     s_seg[w][1] = -1;
   }
-  if (tid < 2) s_glob[tid] = -1;
 
   const int g4 = lane >> 4;   // lane group: tokens 4*g4 .. 4*g4+3 of a step
   const int r16 = lane & 15;  // head of the scores / channel of the outputs
@@ -683,59 +681,40 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // valid slots between two changes of segment, in wave order).  A segment
   // inside this workgroup is written to the output; the first and the last
   // segment, if they reach other workgroups, leave a normalised partial and its
-  // log-sum-exp.  Pass 1 (one thread per slot and head): the segment's max and
-  // sum, the slot's normalised weight, and per slot where its segment goes.
-  // Pass 2 (one thread per output element): weighted sums of the slots.
+  // log-sum-exp.  Where each slot's segment goes is the same for every thread
+  // (scalar work on the slot table); each thread then folds the slots of its
+  // output element in order with a running max, as the pieces themselves did.
   constexpr int NS = 2 * kWavesPerGroup;
-  static_assert(NS * HG <= kGroupThreads, "pass 1: one thread per slot and head");
-  __shared__ float s_w[NS][HG];    // normalised weight of slot k for head h
-  __shared__ float s_lse[NS][HG];  // log2-domain log-sum-exp of slot k's segment
-  __shared__ int s_row[NS];        // output row of head 0 of slot k's segment
-  __shared__ int s_kind[NS];       // -1: written here; 0 / 1: partial slot
-  __shared__ int s_end[NS];        // slot k is its segment's last valid slot
+  static_assert(NS <= kWave, "one lane per slot");
+  // Slot k on lane k (vector work: the scalar unit is shared by the waves of
+  // a compute unit, and all of them build the same table).  Segments do not
+  // decrease along the valid slots, so slot k ends its segment exactly when
+  // the smallest valid segment after it differs.
+  const int sk_l = lane < NS ? reinterpret_cast<const int*>(s_seg)[lane] : -1;
+  int after = __shfl_down(sk_l < 0 ? 0x7fffffff : sk_l, 1, kWave);  // every lane shuffles
+  after = lane + 1 < NS ? after : 0x7fffffff;
+#pragma unroll
+  for (int off = 1; off < NS; off <<= 1) {
+    const int y = __shfl_down(after, off, kWave);
+    if (lane + off < NS) after = min(after, y);
+  }
+  const int slot_l = sk_l == gi.seg[0] ? 0 : (sk_l == gi.seg[1] ? 1 : -1);
+  const bool local_l = slot_l < 0 || (slot_l == 0 ? (gi.lo[0] == grp && gi.hi[0] == grp)
+                                                  : (gi.lo[1] == grp && gi.hi[1] == grp));
+  const bool valid_l = lane < NS && sk_l >= 0;
+  const uint32_t validm = (uint32_t)__ballot(valid_l);
+  const uint32_t endm = (uint32_t)__ballot(valid_l && after != sk_l);
+  const uint32_t localm = (uint32_t)__ballot(valid_l && local_l);
+  const uint32_t kind1m = (uint32_t)__ballot(valid_l && !local_l && slot_l == 1);
+  const uint32_t glob0m = (uint32_t)__ballot(valid_l && !local_l && slot_l == 0);
+  const uint32_t glob1m = kind1m;
   int segs[NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) segs[k] = s_seg[k >> 1][k & 1];
-  if (tid < NS * HG) {
-    const int k = tid / HG;
-    const int h = tid - k * HG;
-    int sk = -1;
-#pragma unroll
-    for (int k2 = 0; k2 < NS; ++k2) sk = k2 == k ? segs[k2] : sk;
-    float mk[NS], lk[NS];
-#pragma unroll
-    for (int k2 = 0; k2 < NS; ++k2) {
-      mk[k2] = s_m[k2 >> 1][k2 & 1][h];
-      lk[k2] = s_l[k2 >> 1][k2 & 1][h];
-    }
-    float M = kFloorMax, mine = kFloorMax;
-#pragma unroll
-    for (int k2 = 0; k2 < NS; ++k2) {
-      if (segs[k2] == sk) M = fmaxf(M, mk[k2]);
-      if (k2 == k) mine = mk[k2];
-    }
-    float L = 0.f;
-#pragma unroll
-    for (int k2 = 0; k2 < NS; ++k2)
-      if (segs[k2] == sk) L += fast_exp2(mk[k2] - M) * lk[k2];
-    const bool live = sk >= 0 && L > 0.f;
-    s_w[k][h] = live ? fast_exp2(mine - M) * __builtin_amdgcn_rcpf(L) : 0.f;
-    s_lse[k][h] = live ? M + fast_log2(L) : kMinusInf;
-    if (h == 0) {
-      int next = -1;  // segment of the next valid slot
-#pragma unroll
-      for (int k2 = NS - 1; k2 >= 0; --k2)
-        if (k2 > k && segs[k2] >= 0) next = segs[k2];
-      const int slot = sk < 0 ? -1 : (sk == gi.seg[0] ? 0 : (sk == gi.seg[1] ? 1 : -1));
-      const bool local = slot < 0 || (lo_of(slot) == grp && hi_of(slot) == grp);
-      const int eb = sk >= 0 ? sk / U : 0;
-      s_row[k] = eb * Hq + (sk - eb * U) * HG;
-      s_kind[k] = local ? -1 : slot;
-      s_end[k] = sk >= 0 && next != sk;
-      if (sk >= 0 && !local) s_glob[slot] = sk;
-    }
-  }
-  __syncthreads();
+  for (int k = 0; k < NS; ++k) segs[k] = __shfl(sk_l, k, kWave);
+  // segments this workgroup leaves as partials (first, last)
+  const int g0s = __shfl(sk_l, glob0m ? __builtin_ctz(glob0m) : 0, kWave);
+  const int g1s = __shfl(sk_l, glob1m ? __builtin_ctz(glob1m) : 0, kWave);
+  const int glob[2] = {glob0m ? g0s : -1, glob1m ? g1s : -1};
   constexpr int kP2 = (HG * D + kGroupThreads - 1) / kGroupThreads;  // passes over the outputs
 #pragma unroll
   for (int r2 = 0; r2 < kP2; ++r2) {
@@ -744,23 +723,43 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     const int h = e2 / D;
     const int c = e2 - h * D;
     const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
-    float acc = 0.f;
+    // Every slot's max, sum and value are loaded up front (independent LDS
+    // reads); slots without a segment are skipped.
+    float mv[NS], lv[NS], xv[NS];
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      if (segs[k] < 0) continue;
-      acc += s_w[k][h] * s_acc[k >> 1][k & 1][h][c];
-      if (__builtin_amdgcn_readfirstlane(s_end[k]) == 0) continue;
-      const int kind = __builtin_amdgcn_readfirstlane(s_kind[k]);
-      if (kind < 0) {
-        a.out[(size_t)(s_row[k] + h) * D + c] = (uint16_t)bf16_rne(acc);
+      mv[k] = s_m[k >> 1][k & 1][h];
+      lv[k] = s_l[k >> 1][k & 1][h];
+      xv[k] = s_acc[k >> 1][k & 1][h][c];
+    }
+    float M = kFloorMax, L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      if (!((validm >> k) & 1u)) continue;
+      const float mn = fmaxf(M, mv[k]);
+      const float ca = fast_exp2(M - mn);
+      const float cb = fast_exp2(mv[k] - mn);
+      L = L * ca + lv[k] * cb;
+      acc = acc * ca + xv[k] * cb;
+      M = mn;
+      if (!((endm >> k) & 1u)) continue;
+      const bool live = L > 0.f;
+      const float val = live ? acc * __builtin_amdgcn_rcpf(L) : 0.f;
+      const int sk = segs[k];
+      if ((localm >> k) & 1u) {
+        const int eb = sk / U;
+        const int row0 = eb * Hq + (sk - eb * U) * HG;
+        a.out[(size_t)(row0 + h) * D + c] = (uint16_t)bf16_rne(val);
       } else {
-        const int row = (2 * grp + kind) * HG + h;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), opart_rs, (row * D + c) * 4,
+        const int row = (2 * grp + (int)((kind1m >> k) & 1u)) * HG + h;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), opart_rs, (row * D + c) * 4,
                                               0, kCoherent);
         if (c == 0)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_lse[k][h]), lse_rs, row * 4, 0,
-                                                kCoherent);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __float_as_uint(live ? M + fast_log2(L) : kMinusInf), lse_rs, row * 4, 0, kCoherent);
       }
+      M = kFloorMax;
+      L = 0.f;
       acc = 0.f;
     }
   }
@@ -774,9 +773,9 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (tid < 2) {
     const int k = tid;
-    const int sgm = s_glob[k];
+    const int sgm = k == 0 ? glob[0] : glob[1];
     int merge = -1;
-    if (sgm >= 0 && !(k == 1 && sgm == s_glob[0])) {
+    if (sgm >= 0 && !(k == 1 && sgm == glob[0])) {
       // The last arrival of a call brings the counter to a multiple of the
       // contributor count n (the metadata build zeroes it).  That workgroup
       // takes n off again at once (no result needed), so the counter is back
