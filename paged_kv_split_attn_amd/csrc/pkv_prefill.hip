@@ -34,8 +34,12 @@ __device__ __forceinline__ uint32_t keys_upto(int d) {
 // reduction index runs over the eight keys lane group g holds (4g .. 4g+3 of
 // half 0, then of half 1): the weights never move between lanes, and the
 // double-rate instruction does twice the work of the 16-key one in the same
-// time.  P enters as bf16 hi + lo parts.  Output: lane (g, r) register i of
-// block vb of tile t holds O[row 4g+i of t][channel 16 vb + r].
+// time.  P enters rounded to bf16 (the weights are at most 1; the row sum
+// keeps their fp32 values, and the rounding adds about 3e-5 to the mean
+// error of the fp32-accumulated output, against a 1e-3 bar; splitting P into
+// bf16 high and low parts cost a third more matrix-core time for that).
+// Output: lane (g, r) register i of block vb of tile t holds O[row 4g+i of
+// t][channel 16 vb + r].
 template <int D, int NT>
 struct Wave32 {
   static constexpr int KB = D / 32;  // q.K MFMAs per half and tile
@@ -121,7 +125,7 @@ struct Wave32 {
         vv[vb].w &= msk[3];
       }
     }
-    bf16x8_t phi[NT], plo[NT];
+    bf16x8_t pb[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       float pm = fmaxf(fmaxf(s[t][0], s[t][1]), fmaxf(s[t][2], s[t][3]));
@@ -144,11 +148,7 @@ struct Wave32 {
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[t][i] - m[t]);
       l[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const __bf16 h = (__bf16)p[i];
-        phi[t][i] = h;
-        plo[t][i] = (__bf16)(p[i] - (float)h);
-      }
+      for (int i = 0; i < 8; ++i) pb[t][i] = (__bf16)p[i];
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
@@ -157,8 +157,7 @@ struct Wave32 {
       const bf16x8_t vt = __builtin_bit_cast(bf16x8_t, vv[vb]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        o[t][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[t], vt, o[t][vb], 0, 0, 0);
-        o[t][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[t], vt, o[t][vb], 0, 0, 0);
+        o[t][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[t], vt, o[t][vb], 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
