@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--groups", type=int, default=0, help="decode grid (0 = one workgroup per CU)")
     ap.add_argument("--min-tiles", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0 = enough for 768 MB)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="CPU work (seconds x worker processes) of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append", choices=("fused", "separate"), default="fused",
                     help="KV append fused into the decode launch, or its own launch")
@@ -165,8 +166,9 @@ def cpu_baseline(batch, budget_s, cfg=None):
     split into its requests, each an oracle.decode of that request, run by a
     pool of worker processes (each with one BLAS thread; they rebuild the same
     seeded batch when they start).  One warm-up call, then calls until about
-    budget_s seconds, at least 3 and at most 7, median reported.  cfg=None runs
-    the units in this process, one after another (small batches, tests)."""
+    budget_s seconds of CPU work (wall time x worker processes), at least 3,
+    median reported.  cfg=None runs the units in this process, one after
+    another (small batches, tests)."""
     import multiprocessing as mp
 
     units, unit = oracle_units(batch)
@@ -183,11 +185,11 @@ def cpu_baseline(batch, budget_s, cfg=None):
     try:
         run()  # warm-up
         t_all = time.perf_counter()
-        while len(times) < 7:
+        while len(times) < 1000:
             t0 = time.perf_counter()
             run()
             times.append(time.perf_counter() - t0)
-            if len(times) >= 3 and time.perf_counter() - t_all >= budget_s:
+            if len(times) >= 3 and (time.perf_counter() - t_all) * cores >= budget_s:
                 break
     finally:
         if pool is not None:
@@ -201,7 +203,7 @@ def cpu_baseline(batch, budget_s, cfg=None):
             "cpu": cpu_model(), "kind": "oracle", "us_per_call": round(per_call * 1e6, 1),
             "sample": f"median of {len(times)} full decode calls of the {batch.name} batch "
                       f"(fp64 numpy oracle, {how}, after one warm-up call), "
-                      f"{sum(times):.1f} s"}
+                      f"{sum(times):.1f} s wall, about {sum(times) * cores:.0f} s of CPU work"}
 
 
 def counters_for_current_kernel():
