@@ -804,7 +804,13 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // pairs, lower first), so the result depends only on the plan and no
   // barrier is needed.
   constexpr int kQuarters = 4;
-  constexpr int kPer = 8;  // contributors per quarter and segment in one round
+  // Output groups per lane: one pass covers 128 groups (a single pass when
+  // HG * D <= 512); with more, one lane takes several groups and the loads of
+  // all of them go out together (one round trip, not one per pass), with
+  // proportionally fewer contributors per quarter and round.
+  constexpr int NO = kVecPasses;
+  constexpr int kPer = 8 / NO;  // contributors per quarter and segment in one round
+  static_assert(kPer >= 1, "output groups per lane");
   const int q = lane >> 4;
   // Segment k's contributors are workgroups lo[k] .. hi[k] (none if not merged
   // here).  Workgroup j > lo holds the segment as its first segment (slot 0);
@@ -815,80 +821,94 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
   const int span = max(hi[0] - lo[0], hi[1] - lo[1]) + 1;
   const int rounds = (span + kQuarters * kPer - 1) / (kQuarters * kPer);
-  // One pass per 128 output groups (a single pass when HG * D <= 512).
+  int h[NO], c[NO];
+  bool tact[NO];
 #pragma unroll
-  for (int og = 0; og < kVecPasses; ++og) {
-  const int t = og * kVecPass + w * 16 + (lane & 15);
-  const bool tact = t < kVec;
-  const int h = tact ? t / (D / 4) : 0;
-  const int c = tact ? (t - h * (D / 4)) * 4 : 0;
-  Combine4 mc[2];
+  for (int og = 0; og < NO; ++og) {
+    const int t = og * kVecPass + w * 16 + (lane & 15);
+    tact[og] = t < kVec;
+    h[og] = tact[og] ? t / (D / 4) : 0;
+    c[og] = tact[og] ? (t - h[og] * (D / 4)) * 4 : 0;
+  }
+  Combine4 mc[2][NO];
 #pragma unroll 1
   for (int rd = 0; rd < rounds; ++rd) {
-    float ls[2][kPer];
-    f4 ov[2][kPer];
+    float ls[2][NO][kPer];
+    f4 ov[2][NO][kPer];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int j = lo[k] + (rd * kPer + i) * kQuarters + q;
-        ls[k][i] = kFloorMax;
-        ov[k][i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int og = 0; og < NO; ++og) {
+          ls[k][og][i] = kFloorMax;
+          ov[k][og][i] = f4{0.f, 0.f, 0.f, 0.f};
+        }
         if (j <= hi[k]) {  // uniform over a quarter
-          const int row = (2 * j + (j == lo[k] ? slot0[k] : 0)) * HG + h;
-          ls[k][i] = __uint_as_float(
-              __builtin_amdgcn_raw_buffer_load_b32(lse_rs, row * 4, 0, kCoherent));
-          ov[k][i] = __builtin_bit_cast(
-              f4, __builtin_amdgcn_raw_buffer_load_b128(opart_rs, (row * D + c) * 4, 0, kCoherent));
+#pragma unroll
+          for (int og = 0; og < NO; ++og) {
+            const int row = (2 * j + (j == lo[k] ? slot0[k] : 0)) * HG + h[og];
+            ls[k][og][i] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(lse_rs, row * 4, 0, kCoherent));
+            ov[k][og][i] = __builtin_bit_cast(
+                f4, __builtin_amdgcn_raw_buffer_load_b128(opart_rs, (row * D + c[og]) * 4, 0,
+                                                          kCoherent));
+          }
         }
       }
     }
     // This round's contributors: max first, then one exponential each.
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      float mr = kFloorMax;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) mr = fmaxf(mr, ls[k][i]);
-      float den = 0.f;
-      f4 num = {0.f, 0.f, 0.f, 0.f};
+      for (int og = 0; og < NO; ++og) {
+        float mr = kFloorMax;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) {
-          const float wi = fast_exp2(ls[k][i] - mr);
-          den += wi;
-          num += ov[k][i] * wi;
+        for (int i = 0; i < kPer; ++i)
+          if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) mr = fmaxf(mr, ls[k][og][i]);
+        float den = 0.f;
+        f4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) {
+            const float wi = fast_exp2(ls[k][og][i] - mr);
+            den += wi;
+            num += ov[k][og][i] * wi;
+          }
         }
+        mc[k][og].add(mr, den, num);
       }
-      mc[k].add(mr, den, num);
     }
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     if (msg[k] < 0) continue;
-    Combine4 x = mc[k];
 #pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      // Both lanes of the pair get (lower, upper) and add the upper to the lower.
-      auto pr = [&](float v) { return off == 16 ? pair16(v) : pair32(v); };
-      const LanePair m = pr(x.m), den = pr(x.den), nx = pr(x.num.x), ny = pr(x.num.y),
-                     nz = pr(x.num.z), nw = pr(x.num.w);
-      Combine4 r;
-      r.m = m.lo;
-      r.den = den.lo;
-      r.num = f4{nx.lo, ny.lo, nz.lo, nw.lo};
-      r.add(m.hi, den.hi, f4{nx.hi, ny.hi, nz.hi, nw.hi});
-      x = r;
+    for (int og = 0; og < NO; ++og) {
+      Combine4 x = mc[k][og];
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        // Both lanes of the pair get (lower, upper) and add the upper to the lower.
+        auto pr = [&](float v) { return off == 16 ? pair16(v) : pair32(v); };
+        const LanePair m = pr(x.m), den = pr(x.den), nx = pr(x.num.x), ny = pr(x.num.y),
+                       nz = pr(x.num.z), nw = pr(x.num.w);
+        Combine4 r;
+        r.m = m.lo;
+        r.den = den.lo;
+        r.num = f4{nx.lo, ny.lo, nz.lo, nw.lo};
+        r.add(m.hi, den.hi, f4{nx.hi, ny.hi, nz.hi, nw.hi});
+        x = r;
+      }
+      if (q == 0 && tact[og]) {
+        const int eb = msg[k] / U;
+        const int hq = (msg[k] - eb * U) * HG + h[og];
+        const float inv = x.den > 0.f ? 1.0f / x.den : 0.f;
+        const f4 val = x.num * inv;
+        *reinterpret_cast<uint2*>(a.out + ((size_t)eb * Hq + hq) * D + c[og]) =
+            make_uint2(pack_bf16x2(val.x, val.y), pack_bf16x2(val.z, val.w));
+      }
     }
-    if (q == 0 && tact) {
-      const int eb = msg[k] / U;
-      const int hq = (msg[k] - eb * U) * HG + h;
-      const float inv = x.den > 0.f ? 1.0f / x.den : 0.f;
-      const f4 val = x.num * inv;
-      *reinterpret_cast<uint2*>(a.out + ((size_t)eb * Hq + hq) * D + c) =
-          make_uint2(pack_bf16x2(val.x, val.y), pack_bf16x2(val.z, val.w));
-    }
-  }
   }
 }
 
