@@ -109,6 +109,46 @@ struct Combine4 {
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kCoherent = 16;
 
+// The in-workgroup merge slots: slot 2w + j is wave w's first (j = 0) or last
+// (j = 1) piece when that piece leaves its segment unfinished.
+constexpr int kSlots = 2 * kWavesPerGroup;
+static_assert(kSlots <= 32, "slot masks of 32 bits");
+
+// Where each slot's segment goes, as lane masks over the slots: valid slots,
+// slots that end their segment, segments written to the output here, and
+// segments left as the workgroup's first / last partial.  Slot k's segment
+// (-1: none) is on lane k.  Vector work, one slot per lane: the scalar unit is
+// shared by the waves of a compute unit, and all of them build the same table.
+struct SlotTable {
+  uint32_t validm, endm, localm, kind1m, glob0m;
+  int sk;
+};
+
+__device__ __forceinline__ SlotTable make_slot_table(int sk_l, int lane, int grp,
+                                                     const GroupInfo& g) {
+  // Segments do not decrease along the valid slots, so slot k ends its
+  // segment exactly when the smallest valid segment after it differs.
+  int after = __shfl_down(sk_l < 0 ? 0x7fffffff : sk_l, 1, kWave);  // every lane shuffles
+  after = lane + 1 < kSlots ? after : 0x7fffffff;
+#pragma unroll
+  for (int off = 1; off < kSlots; off <<= 1) {
+    const int y = __shfl_down(after, off, kWave);
+    if (lane + off < kSlots) after = min(after, y);
+  }
+  const int slot_l = sk_l == g.seg[0] ? 0 : (sk_l == g.seg[1] ? 1 : -1);
+  const bool local_l = slot_l < 0 || (slot_l == 0 ? (g.lo[0] == grp && g.hi[0] == grp)
+                                                  : (g.lo[1] == grp && g.hi[1] == grp));
+  const bool valid_l = lane < kSlots && sk_l >= 0;
+  SlotTable t;
+  t.validm = (uint32_t)__ballot(valid_l);
+  t.endm = (uint32_t)__ballot(valid_l && after != sk_l);
+  t.localm = (uint32_t)__ballot(valid_l && local_l);
+  t.kind1m = (uint32_t)__ballot(valid_l && !local_l && slot_l == 1);
+  t.glob0m = (uint32_t)__ballot(valid_l && !local_l && slot_l == 0);
+  t.sk = sk_l;
+  return t;
+}
+
 template <int D, int HG, int KIND, bool PLAN>
 __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   constexpr bool APPEND = KIND == kAppend;
@@ -121,7 +161,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   __shared__ __align__(16) float s_acc[kWavesPerGroup][2][HG][D];
   __shared__ float s_m[kWavesPerGroup][2][HG];
   __shared__ float s_l[kWavesPerGroup][2][HG];
-  __shared__ int s_seg[kWavesPerGroup][2];
+  __shared__ int s_seg[PLAN ? kWavesPerGroup : 1][2];  // planning launch: the slot segments
   __shared__ __align__(16) float s_out[kWavesPerGroup][HG][D];  // per-wave transpose of finished rows
   __shared__ int s_merge[2];  // of those, the ones this workgroup merges
   __shared__ GroupInfo s_gi;  // the workgroup's merge record, for the epilogue
@@ -287,11 +327,20 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // Stores count with loads in a wave's vector-memory counter, so they go out
   // after the wave's last load: issued before the K/V stream, every wait for a
   // K/V step would also wait for them to be acknowledged.
-  auto store_plan = [&]() {
+  auto store_plan = [&](bool streamed) {
     if constexpr (PLAN) {
       if (lane == 0) a.plan_waves[grp * kWavesPerGroup + w] = rng;
       if (w == 0) {
-        if (lane == 0) a.plan_ginfo[grp] = s_gi;
+        // Words 0..7 from s_gi, then the slot segments this workgroup's
+        // waves recorded (none when it had no range).
+        constexpr int kHead = 8, kWords = (int)(sizeof(GroupInfo) / 4);
+        static_assert(kHead + 2 * kWavesPerGroup == kWords, "merge record layout");
+        if (lane < kWords) {
+          const int v = lane < kHead ? reinterpret_cast<const int*>(&s_gi)[lane]
+                                     : (streamed ? reinterpret_cast<const int*>(s_seg)[lane - kHead]
+                                                 : -1);
+          reinterpret_cast<int*>(&a.plan_ginfo[grp])[lane] = v;
+        }
         if (grp == 0) {
           for (int b = lane; b <= a.batch; b += kWave) a.plan_indptr[b] = s_pip[b];
           if (lane == 0) {
@@ -310,16 +359,18 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   if ((grp >= ngroups) | (rng.count < 0) | (gi0.seg[0] < -1)) {  // uniform over the workgroup
     if (grp == 0) zero_empty_rows();
     make_group_info();
-    store_plan();
+    store_plan(false);
     return;
   }
   if (tid == 0) {  // parked in LDS until the epilogue
     if constexpr (!PLAN) s_gi = gi0;
     s_ptr = EpiloguePtrs{a.hdr, a.counters, a.lse, a.opart};
   }
-  if (lane == 0) {
-    s_seg[w][0] = -1;
-    s_seg[w][1] = -1;
+  if constexpr (PLAN) {
+    if (lane == 0) {
+      s_seg[w][0] = -1;
+      s_seg[w][1] = -1;
+    }
   }
 
   const int g4 = lane >> 4;   // lane group: tokens 4*g4 .. 4*g4+3 of a step
@@ -631,7 +682,9 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
           s_l[w][slot][i] = lt;
         }
       }
-      if (lane == 0) s_seg[w][slot] = seg;
+      if constexpr (PLAN) {
+        if (lane == 0) s_seg[w][slot] = seg;
+      }
     }
     left -= len;
     ++piece;
@@ -649,8 +702,21 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   flush_token();
   if (grp == 0) zero_empty_rows();
   make_group_info();
-  __syncthreads();  // also publishes s_gi and s_ptr
+  constexpr int NS = kSlots;
+  SlotTable tab;
+  if constexpr (!PLAN) {
+    // The slot segments come with the plan: the table is built here, while
+    // the workgroup's other waves may still stream.
+    int sk = -1;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) sk = lane == k ? gi0.slot_seg[k] : sk;
+    tab = make_slot_table(sk, lane, grp, gi0);
+  }
+  __syncthreads();  // also publishes s_gi, s_seg and s_ptr
   const GroupInfo gi = s_gi;
+  if constexpr (PLAN)
+    tab = make_slot_table(lane < NS ? reinterpret_cast<const int*>(s_seg)[lane] : -1, lane, grp,
+                          gi);
   float* const lse_p = uniform_ptr(s_ptr.lse);
   float* const opart_p = uniform_ptr(s_ptr.opart);
   int32_t* const counters_p = uniform_ptr(s_ptr.counters);
@@ -682,38 +748,16 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // inside this workgroup is written to the output; the first and the last
   // segment, if they reach other workgroups, leave a normalised partial and its
   // log-sum-exp.  Where each slot's segment goes is the same for every thread
-  // (scalar work on the slot table); each thread then folds the slots of its
-  // output element in order with a running max, as the pieces themselves did.
-  constexpr int NS = 2 * kWavesPerGroup;
-  static_assert(NS <= kWave, "one lane per slot");
-  // Slot k on lane k (vector work: the scalar unit is shared by the waves of
-  // a compute unit, and all of them build the same table).  Segments do not
-  // decrease along the valid slots, so slot k ends its segment exactly when
-  // the smallest valid segment after it differs.
-  const int sk_l = lane < NS ? reinterpret_cast<const int*>(s_seg)[lane] : -1;
-  int after = __shfl_down(sk_l < 0 ? 0x7fffffff : sk_l, 1, kWave);  // every lane shuffles
-  after = lane + 1 < NS ? after : 0x7fffffff;
-#pragma unroll
-  for (int off = 1; off < NS; off <<= 1) {
-    const int y = __shfl_down(after, off, kWave);
-    if (lane + off < NS) after = min(after, y);
-  }
-  const int slot_l = sk_l == gi.seg[0] ? 0 : (sk_l == gi.seg[1] ? 1 : -1);
-  const bool local_l = slot_l < 0 || (slot_l == 0 ? (gi.lo[0] == grp && gi.hi[0] == grp)
-                                                  : (gi.lo[1] == grp && gi.hi[1] == grp));
-  const bool valid_l = lane < NS && sk_l >= 0;
-  const uint32_t validm = (uint32_t)__ballot(valid_l);
-  const uint32_t endm = (uint32_t)__ballot(valid_l && after != sk_l);
-  const uint32_t localm = (uint32_t)__ballot(valid_l && local_l);
-  const uint32_t kind1m = (uint32_t)__ballot(valid_l && !local_l && slot_l == 1);
-  const uint32_t glob0m = (uint32_t)__ballot(valid_l && !local_l && slot_l == 0);
-  const uint32_t glob1m = kind1m;
+  // (the slot table); each thread then folds the slots of its output element
+  // in order with a running max, as the pieces themselves did.
+  const uint32_t validm = tab.validm, endm = tab.endm, localm = tab.localm;
+  const uint32_t kind1m = tab.kind1m, glob0m = tab.glob0m, glob1m = tab.kind1m;
   int segs[NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) segs[k] = __shfl(sk_l, k, kWave);
+  for (int k = 0; k < NS; ++k) segs[k] = __builtin_amdgcn_readlane(tab.sk, k);
   // segments this workgroup leaves as partials (first, last)
-  const int g0s = __shfl(sk_l, glob0m ? __builtin_ctz(glob0m) : 0, kWave);
-  const int g1s = __shfl(sk_l, glob1m ? __builtin_ctz(glob1m) : 0, kWave);
+  const int g0s = __builtin_amdgcn_readlane(tab.sk, glob0m ? __builtin_ctz(glob0m) : 0);
+  const int g1s = __builtin_amdgcn_readlane(tab.sk, glob1m ? __builtin_ctz(glob1m) : 0);
   const int glob[2] = {glob0m ? g0s : -1, glob1m ? g1s : -1};
   constexpr int kP2 = (HG * D + kGroupThreads - 1) / kGroupThreads;  // passes over the outputs
 #pragma unroll
@@ -768,7 +812,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // Cross-workgroup merge: publish the partials, count arrivals, and let the
   // last workgroup of each segment combine every workgroup's partial in order.
   // Lanes 0 and 1 arrive for the first and the last segment at the same time.
-  store_plan();
+  store_plan(true);
   wait_stores();
   __syncthreads();
   if (tid < 2) {

@@ -63,6 +63,10 @@ struct alignas(16) GroupInfo {
   int32_t lo[2];       // first workgroup whose range touches seg[k]
   int32_t hi[2];       // last workgroup whose range touches seg[k]
   int32_t slot_lo[2];  // partial slot (0 = first segment, 1 = last) seg[k] has in workgroup lo[k]
+  // Segment of each wave's partial first (slot 2w) and last (slot 2w + 1)
+  // piece, -1 when that piece is a whole segment or absent: the table the
+  // in-workgroup merge works from, known from the plan before any K/V is read.
+  int32_t slot_seg[2 * kWavesPerGroup];
 };
 
 // Byte offsets of the workspace sections; every section is 256-byte aligned.

@@ -36,7 +36,11 @@ __device__ void build_plan(const MetaArgs& a, const Locator& loc, I T, int W) {
        x += gridDim.x * THREADS) {
     if (x < nw) {
       const int i = x / kWavesPerGroup;
-      a.waves[x] = plan_wave_range<I>(loc, pm, W, i, x - i * kWavesPerGroup);
+      const int w = x - i * kWavesPerGroup;
+      const WaveRange r = plan_wave_range<I>(loc, pm, W, i, w);
+      a.waves[x] = r;
+      plan_wave_slots<I>(loc, pm, i, w, a.units, r, &a.ginfo[i].slot_seg[2 * w],
+                         &a.ginfo[i].slot_seg[2 * w + 1]);
     } else {
       const int i = (x - nw) >> 1, k = (x - nw) & 1;
       plan_group_half<I>(loc, pm, W, a.units, i, k, &a.ginfo[i]);

@@ -169,6 +169,30 @@ __device__ WaveRange plan_wave_range(const Loc& loc, const PlanMath<I>& pm, int 
   return r;
 }
 
+// The merge slots of wave w of workgroup i, whose range is r: its first piece
+// (the part of segment (r.b, r.u) from page r.p on) is partial unless it starts
+// at the segment's first page and covers the whole segment; its last piece,
+// when the range reaches past the first segment, starts at its segment's
+// first page and is partial when it stops before the segment's last page.
+// Every piece between is a whole segment.
+template <typename I, typename Loc>
+__device__ void plan_wave_slots(const Loc& loc, const PlanMath<I>& pm, int i, int w, int U,
+                                const WaveRange& r, int32_t* first, int32_t* last) {
+  int s0 = -1, s1 = -1;
+  if (r.count > 0) {
+    const int first_len = min(r.count, r.pages - r.p);
+    if (!(r.p == 0 && first_len == r.pages)) s0 = r.b * U + r.u;
+    if (r.count > first_len) {
+      const I g0 = pm.start(i), len = pm.start(i + 1) - g0;
+      const I t1 = g0 + PlanMath<I>::part(len, w + 1);  // end of the wave's range
+      const WaveRange e = loc.at(t1 - 1, 0);
+      if (e.p + 1 < e.pages) s1 = e.b * U + e.u;
+    }
+  }
+  *first = s0;
+  *last = s1;
+}
+
 // Half k of the merge record of workgroup i: its first (k = 0) or last (k = 1)
 // segment (b * U + u), and the workgroups that segment's tiles span.  A
 // segment is the first segment of a workgroup exactly when that workgroup's

@@ -20,6 +20,11 @@ def lib():
     return pkv.load_library()
 
 
+# Bytes of a workgroup's merge record: its first and last segment with the
+# workgroups each spans (8 words), then the segment of each wave's two slots.
+REC = 32 + 8 * pkv.WAVES_PER_GROUP
+
+
 def test_header_declares_expected_entry_points():
     names = pkv.declared_functions()
     assert set(names) == {
@@ -67,7 +72,7 @@ def test_workspace_bytes(lib):
     n = pkv.pkv_workspace_bytes(d)
     groups, hg, segs = 256, 4, 16 * 8
     expect = 256  # header
-    for sz in (32 * groups * pkv.WAVES_PER_GROUP, 32 * groups, 4 * segs, 4 * 2 * groups * hg,
+    for sz in (32 * groups * pkv.WAVES_PER_GROUP, REC * groups, 4 * segs, 4 * 2 * groups * hg,
                4 * 2 * groups * hg * 128):
         expect += (sz + 255) // 256 * 256
     assert n == expect
@@ -207,8 +212,8 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_header_wave_count_matches_library(lib):
-    # the workspace holds one 32-byte range per wave of every workgroup
+    # the workspace holds one 32-byte range per wave and one merge record per workgroup
     one = pkv.pkv_workspace_bytes(_desc(num_workgroups=1024))
     two = pkv.pkv_workspace_bytes(_desc(num_workgroups=2048))
-    per_group = 32 * pkv.WAVES_PER_GROUP + 32 + 4 * 2 * 4 * (1 + 128)
+    per_group = 32 * pkv.WAVES_PER_GROUP + REC + 4 * 2 * 4 * (1 + 128)
     assert two - one == 1024 * per_group

@@ -56,7 +56,7 @@ def _plan_bytes(ws, groups):
     hdr = b[:256].view(np.int32)
     waves = 32 * groups * pkv.WAVES_PER_GROUP
     waves_end = 256 + (waves + 255) // 256 * 256
-    ginfo_end = waves_end + 32 * groups
+    ginfo_end = waves_end + (32 + 8 * pkv.WAVES_PER_GROUP) * groups
     return np.concatenate([hdr[[0, 1, 2, 3, 5]].view(np.uint8), b[256:256 + waves],
                            b[waves_end:ginfo_end]])
 
