@@ -184,6 +184,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   int ngroups, nempty;
   WaveRange rng;
   GroupInfo gi0;
+  int slot_seg_l = -1;  // two-call path: segment of merge slot `lane` (lanes below kSlots)
   long long ptiles = 0;  // planning launch: tiles of the plan
   int perr_bits = 0;     // and its error bits
   if constexpr (PLAN) {
@@ -278,6 +279,10 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     const bool plan_ok = a.hdr[kHdrBatch] == a.batch && a.hdr[kHdrUnits] == a.units;
     rng = a.waves[grp * kWavesPerGroup + w];
     gi0 = a.ginfo[grp];
+    // The slot segments, one per lane, for the merge at the end: one vector
+    // load that nothing waits for before then (held in scalar registers
+    // through the stream they crowd the stream's own registers).
+    slot_seg_l = a.ginfo[grp].slot_seg[lane & (kSlots - 1)];
     if (!plan_ok) {  // uniform over the grid
       if (grp == 0 && tid == 0) atomicOr(&a.hdr[kHdrError], (int)kErrPlanMismatch);
       return;
@@ -707,10 +712,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   if constexpr (!PLAN) {
     // The slot segments come with the plan: the table is built here, while
     // the workgroup's other waves may still stream.
-    int sk = -1;
-#pragma unroll
-    for (int k = 0; k < NS; ++k) sk = lane == k ? gi0.slot_seg[k] : sk;
-    tab = make_slot_table(sk, lane, grp, gi0);
+    tab = make_slot_table(lane < NS ? slot_seg_l : -1, lane, grp, gi0);
   }
   __syncthreads();  // also publishes s_gi, s_seg and s_ptr
   const GroupInfo gi = s_gi;
