@@ -93,7 +93,7 @@ struct Combine4 {
   float m = kFloorMax, den = 0.f;
   f4 num = {0.f, 0.f, 0.f, 0.f};
   __device__ __forceinline__ void add(float mk, float lk, f4 vk) {
-    const float mn = fmaxf(m, mk);
+    const float mn = vmax2(m, mk);
     const float ca = fast_exp2(m - mn);
     const float cb = fast_exp2(mk - mn);
     den = den * ca + lk * cb;
@@ -782,7 +782,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       if (!((validm >> k) & 1u)) continue;
-      const float mn = fmaxf(M, mv[k]);
+      const float mn = vmax2(M, mv[k]);
       const float ca = fast_exp2(M - mn);
       const float cb = fast_exp2(mv[k] - mn);
       L = L * ca + lv[k] * cb;
@@ -912,7 +912,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         float mr = kFloorMax;
 #pragma unroll
         for (int i = 0; i < kPer; ++i)
-          if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) mr = fmaxf(mr, ls[k][og][i]);
+          if (lo[k] + (rd * kPer + i) * kQuarters + q <= hi[k]) mr = vmax2(mr, ls[k][og][i]);
         float den = 0.f;
         f4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

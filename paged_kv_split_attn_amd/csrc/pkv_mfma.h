@@ -53,12 +53,29 @@ __device__ __forceinline__ LanePair pair32(float x) {
                                                   false);
   return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
-// Max / sum over the four lanes l % 16 + 16 k (the four lane groups).
+// Maxima of score values without the compiler's NaN quieting (fmaxf makes it
+// canonicalise every input first, which doubles the instruction count of a
+// max tree).  A NaN score can only come from NaN q or K data: masked keys are
+// set to -inf before any max, so garbage past the sequence end never gets here,
+// and the merges combine maxima that are finite or -inf.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// Max over the four lanes l % 16 + 16 k (the four lane groups).
 __device__ __forceinline__ float max_over_groups(float x) {
   const LanePair a = pair16(x);
-  const LanePair b = pair32(fmaxf(a.lo, a.hi));
-  return fmaxf(b.lo, b.hi);
+  const LanePair b = pair32(vmax2(a.lo, a.hi));
+  return vmax2(b.lo, b.hi);
 }
+
+// Sum over the four lanes l % 16 + 16 k (the four lane groups).
 __device__ __forceinline__ float sum_over_groups(float x) {
   const LanePair a = pair16(x);
   const LanePair b = pair32(a.lo + a.hi);
@@ -133,7 +150,7 @@ struct MfmaWave {
     for (int i = 0; i < 4; ++i)
       if (((keep >> (8 * i)) & 0xffu) == 0) s[i] = kMinusInf;
     // Step max of row r over its 16 tokens (4 per lane, 4 lanes).
-    const float pm = max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    const float pm = max_over_groups(vmax3(s[0], s[1], vmax2(s[2], s[3])));
     if (__builtin_amdgcn_ballot_w64(pm > m + kRescaleSlack) != 0) {
       const float mn = fmaxf(m, pm);
       const float alpha = fast_exp2(m - mn);

@@ -25,27 +25,6 @@ __device__ __forceinline__ uint32_t keys_upto(int d) {
   return four(d) | (four(d - 16) << 4);
 }
 
-// Maxima of score values without the compiler's NaN quieting (fmaxf makes it
-// canonicalise every input first, which doubles the instruction count of a
-// max tree).  A NaN score can only come from NaN q or K data: masked keys are
-// set to -inf before any max, so garbage past the sequence end never gets here.
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float vmax2(float a, float b) {
-  float r;
-  __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-// Max over the four lane groups (the lanes l % 16 + 16 k), as max_over_groups.
-__device__ __forceinline__ float vmax_over_groups(float x) {
-  const LanePair a = pair16(x);
-  const LanePair b = pair32(vmax2(a.lo, a.hi));
-  return vmax2(b.lo, b.hi);
-}
-
 // One wave's online softmax over NT tiles of 16 score rows, 32 keys per step;
 // the tiles share every K and V operand the wave reads.  Scores of the
 // step's two 16-key halves come from v_mfma_f32_16x16x32_bf16 as in the decode
@@ -149,7 +128,7 @@ struct Wave32 {
     bf16x8_t pb[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const float pm = vmax_over_groups(vmax3(vmax3(s[t][0], s[t][1], s[t][2]),
+      const float pm = max_over_groups(vmax3(vmax3(s[t][0], s[t][1], s[t][2]),
                                               vmax3(s[t][3], s[t][4], s[t][5]),
                                               vmax2(s[t][6], s[t][7])));
       if (__builtin_amdgcn_ballot_w64(pm > m[t] + kRescaleSlack) != 0) {
