@@ -86,6 +86,85 @@ def test_metadata_bit_exact(case, grid, forced):
     assert np.array_equal(np.array(info["waves"]), plan["waves"])
 
 
+def _merge_records_brute_force(batch, desc, plan):
+    """Every workgroup's merge record, worked out tile by tile from the plan.
+
+    Words: first / last segment of the workgroup's tiles (b * U + u), the
+    first and last workgroup each of them touches, whether that segment is
+    the first (0) or last (1) partial slot of the workgroup where it starts,
+    then per wave the segment of its first and of its last piece when that
+    piece does not cover its whole segment (-1 otherwise or when absent).
+    """
+    _, U = oracle.head_groups(batch.Hq, batch.Hkv)
+    ip = np.asarray(plan["kv_indptr"], dtype=np.int64)
+    T, Wn = int(plan["tiles"]), int(plan["groups"])
+    nw = pkv.WAVES_PER_GROUP
+    starts = ip * U
+    t = np.arange(T, dtype=np.int64)
+    b = np.searchsorted(starts, t, side="right") - 1
+    n = ip[b + 1] - ip[b]
+    seg = b * U + (t - starts[b]) // n  # segment of every tile
+    pages = n                            # tiles of that segment
+    g = [i * T // Wn for i in range(Wn + 1)] if Wn else [0]
+    owner = np.zeros(T, dtype=np.int64)
+    for i in range(Wn):
+        owner[g[i]:g[i + 1]] = i
+    first_tile = {}
+    for x in range(T - 1, -1, -1):
+        first_tile[int(seg[x])] = x
+    recs = np.zeros((desc.groups(), 8 + 2 * nw), dtype=np.int64)
+    for i in range(desc.groups()):
+        rec = [-1, -1, 0, 0, -1, -1, 0, 0] + [-1] * (2 * nw)
+        if i < Wn and g[i + 1] > g[i]:
+            for k, x in enumerate((g[i], g[i + 1] - 1)):
+                s_ = int(seg[x])
+                t0 = first_tile[s_]
+                t1 = t0 + int(pages[x]) - 1
+                rec[k], rec[2 + k], rec[4 + k] = s_, int(owner[t0]), int(owner[t1])
+                rec[6 + k] = 0 if g[int(owner[t0])] >= t0 else 1
+            for w in range(nw):
+                a0 = g[i] + w * (g[i + 1] - g[i]) // nw
+                a1 = g[i] + (w + 1) * (g[i + 1] - g[i]) // nw
+                if a1 <= a0:
+                    continue
+                pieces = []  # (segment, tiles) runs of the wave's range
+                for x in range(a0, a1):
+                    if pieces and pieces[-1][0] == int(seg[x]):
+                        pieces[-1][1] += 1
+                    else:
+                        pieces.append([int(seg[x]), 1])
+                sp = int(pages[a0])
+                if pieces[0][1] < sp:
+                    rec[8 + 2 * w] = pieces[0][0]
+                if len(pieces) > 1 and pieces[-1][1] < int(pages[a1 - 1]):
+                    rec[8 + 2 * w + 1] = pieces[-1][0]
+        recs[i] = rec
+    return recs
+
+
+@pytest.mark.parametrize("case", ["c1", "c3", "c5", "rand0", "g8", "g12", "g4_p64"])
+@pytest.mark.parametrize("grid,forced", [(0, 0), (0, 3), (1000, 0)])
+def test_merge_records_match_brute_force(case, grid, forced):
+    say(f"merge records case={case} grid={grid} forced={forced}")
+    if case in PLAN_SHAPES:
+        batch = _shape_lengths_batch(case)
+    elif case.startswith("c"):
+        batch = cfg(int(case[1]))
+    else:
+        batch = _random_lengths_batch(10, 37, True)
+    desc = make_desc(batch, num_workgroups=grid)
+    run = GpuRun(batch, desc)
+    run.metadata(forced)
+    torch.cuda.synchronize()
+    groups = desc.groups()
+    waves_end = 256 + (32 * groups * pkv.WAVES_PER_GROUP + 255) // 256 * 256
+    words = 8 + 2 * pkv.WAVES_PER_GROUP
+    got = run.ws[waves_end:waves_end + 4 * words * groups].view(torch.int32).view(groups, words)
+    want = _merge_records_brute_force(batch, desc, oracle_plan(batch, desc, forced))
+    bad = np.argwhere(got.cpu().numpy() != want)
+    assert bad.size == 0, f"{len(bad)} words differ, first at (workgroup, word) {tuple(bad[0])}"
+
+
 # -------------------------------------------------------------------- append
 
 @pytest.mark.parametrize("which", ["small", "c5"])
