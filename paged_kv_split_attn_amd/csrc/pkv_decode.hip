@@ -86,6 +86,7 @@ enum Kind : int { kPlain = 0, kAppend = 1, kMasked = 2, kTokens = 3 };
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
 
 // Online-softmax combine of (m, l, values) in the log2 domain, four channels
 // that share m and l.
@@ -159,8 +160,10 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   // Pieces that leave a wave unfinished: slot 0 = the wave's first piece,
   // slot 1 = its last piece (every other piece is a whole segment).
   __shared__ __align__(16) float s_acc[kWavesPerGroup][2][HG][D];
-  __shared__ float s_m[kWavesPerGroup][2][HG];
-  __shared__ float s_l[kWavesPerGroup][2][HG];
+  // Max and sum of slot k = 2 w + (0 | 1) of head h at [h][k]: a head's 16
+  // slots are four 16-byte reads.
+  __shared__ __align__(16) float s_m[HG][kSlots];
+  __shared__ __align__(16) float s_l[HG][kSlots];
   __shared__ int s_seg[PLAN ? kWavesPerGroup : 1][2];  // planning launch: the slot segments
   __shared__ __align__(16) float s_out[kWavesPerGroup][HG][D];  // per-wave transpose of finished rows
   __shared__ int s_merge[2];  // of those, the ones this workgroup merges
@@ -683,8 +686,8 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
             s_acc[w][slot][i][16 * vb + r16] = st.o[vb][i & 3];
         }
         if (lane == i) {
-          s_m[w][slot][i] = st.m;
-          s_l[w][slot][i] = lt;
+          s_m[i][2 * w + slot] = st.m;
+          s_l[i][2 * w + slot] = lt;
         }
       }
       if constexpr (PLAN) {
@@ -761,24 +764,28 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const int g0s = __builtin_amdgcn_readlane(tab.sk, glob0m ? __builtin_ctz(glob0m) : 0);
   const int g1s = __builtin_amdgcn_readlane(tab.sk, glob1m ? __builtin_ctz(glob1m) : 0);
   const int glob[2] = {glob0m ? g0s : -1, glob1m ? g1s : -1};
-  constexpr int kP2 = (HG * D + kGroupThreads - 1) / kGroupThreads;  // passes over the outputs
-#pragma unroll
-  for (int r2 = 0; r2 < kP2; ++r2) {
-  const int e2 = tid + r2 * kGroupThreads;
-  if (e2 < HG * D) {
-    const int h = e2 / D;
-    const int c = e2 - h * D;
+  // Thread t < HG * D / 2 folds channels c, c + 1 of head h (e = 2 t).
+  static_assert(HG * D / 2 <= kGroupThreads, "one pass over the outputs");
+  if (tid < HG * D / 2) {
+    const int e = 2 * tid;
+    const int h = e / D;
+    const int c = e - h * D;
     const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
-    // Every slot's max, sum and value are loaded up front (independent LDS
+    // Every slot's max, sum and values are loaded up front (independent LDS
     // reads); slots without a segment are skipped.
-    float mv[NS], lv[NS], xv[NS];
+    float mv[NS], lv[NS];
+    float2 xv[NS];
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      mv[k] = s_m[k >> 1][k & 1][h];
-      lv[k] = s_l[k >> 1][k & 1][h];
-      xv[k] = s_acc[k >> 1][k & 1][h][c];
+    for (int k4 = 0; k4 < NS; k4 += 4) {
+      const float4 m4 = *reinterpret_cast<const float4*>(&s_m[h][k4]);
+      const float4 l4 = *reinterpret_cast<const float4*>(&s_l[h][k4]);
+      mv[k4] = m4.x, mv[k4 + 1] = m4.y, mv[k4 + 2] = m4.z, mv[k4 + 3] = m4.w;
+      lv[k4] = l4.x, lv[k4 + 1] = l4.y, lv[k4 + 2] = l4.z, lv[k4 + 3] = l4.w;
     }
-    float M = kFloorMax, L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+      xv[k] = *reinterpret_cast<const float2*>(&s_acc[k >> 1][k & 1][h][c]);
+    float M = kFloorMax, L = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       if (!((validm >> k) & 1u)) continue;
@@ -786,29 +793,32 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       const float ca = fast_exp2(M - mn);
       const float cb = fast_exp2(mv[k] - mn);
       L = L * ca + lv[k] * cb;
-      acc = acc * ca + xv[k] * cb;
+      a0 = a0 * ca + xv[k].x * cb;
+      a1 = a1 * ca + xv[k].y * cb;
       M = mn;
       if (!((endm >> k) & 1u)) continue;
       const bool live = L > 0.f;
-      const float val = live ? acc * __builtin_amdgcn_rcpf(L) : 0.f;
+      const float inv = live ? __builtin_amdgcn_rcpf(L) : 0.f;
       const int sk = segs[k];
       if ((localm >> k) & 1u) {
         const int eb = sk / U;
         const int row0 = eb * Hq + (sk - eb * U) * HG;
-        a.out[(size_t)(row0 + h) * D + c] = (uint16_t)bf16_rne(val);
+        *reinterpret_cast<uint32_t*>(a.out + (size_t)(row0 + h) * D + c) =
+            pack_bf16x2(a0 * inv, a1 * inv);
       } else {
         const int row = (2 * grp + (int)((kind1m >> k) & 1u)) * HG + h;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), opart_rs, (row * D + c) * 4,
-                                              0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            u2v{__float_as_uint(a0 * inv), __float_as_uint(a1 * inv)},
+            opart_rs, (row * D + c) * 4, 0, kCoherent);
         if (c == 0)
           __builtin_amdgcn_raw_buffer_store_b32(
               __float_as_uint(live ? M + fast_log2(L) : kMinusInf), lse_rs, row * 4, 0, kCoherent);
       }
       M = kFloorMax;
       L = 0.f;
-      acc = 0.f;
+      a0 = 0.f;
+      a1 = 0.f;
     }
-  }
   }
 
   // Cross-workgroup merge: publish the partials, count arrivals, and let the
