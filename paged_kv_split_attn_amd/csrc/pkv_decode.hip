@@ -764,17 +764,21 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   const int g0s = __builtin_amdgcn_readlane(tab.sk, glob0m ? __builtin_ctz(glob0m) : 0);
   const int g1s = __builtin_amdgcn_readlane(tab.sk, glob1m ? __builtin_ctz(glob1m) : 0);
   const int glob[2] = {glob0m ? g0s : -1, glob1m ? g1s : -1};
-  // Thread t < HG * D / 2 folds channels c, c + 1 of head h (e = 2 t).
-  static_assert(HG * D / 2 <= kGroupThreads, "one pass over the outputs");
-  if (tid < HG * D / 2) {
-    const int e = 2 * tid;
+  // Thread t < HG * D / kCh folds channels c .. c + kCh - 1 of head h: four
+  // channels for eight-head groups, else two (256 threads either way at
+  // D = 128; measured: two for four heads, four for eight).
+  constexpr int kCh = HG * D >= 1024 ? 4 : 2;
+  static_assert(HG * D / kCh <= kGroupThreads, "one pass over the outputs");
+  using ChVec = float __attribute__((ext_vector_type(kCh)));
+  if (tid < HG * D / kCh) {
+    const int e = kCh * tid;
     const int h = e / D;
     const int c = e - h * D;
     const __amdgpu_buffer_rsrc_t lse_rs = lse_rsrc(), opart_rs = opart_rsrc();
     // Every slot's max, sum and values are loaded up front (independent LDS
     // reads); slots without a segment are skipped.
     float mv[NS], lv[NS];
-    float2 xv[NS];
+    ChVec xv[NS];
 #pragma unroll
     for (int k4 = 0; k4 < NS; k4 += 4) {
       const float4 m4 = *reinterpret_cast<const float4*>(&s_m[h][k4]);
@@ -784,8 +788,9 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < NS; ++k)
-      xv[k] = *reinterpret_cast<const float2*>(&s_acc[k >> 1][k & 1][h][c]);
-    float M = kFloorMax, L = 0.f, a0 = 0.f, a1 = 0.f;
+      xv[k] = *reinterpret_cast<const ChVec*>(&s_acc[k >> 1][k & 1][h][c]);
+    float M = kFloorMax, L = 0.f;
+    ChVec acc = {};
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       if (!((validm >> k) & 1u)) continue;
@@ -793,8 +798,8 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       const float ca = fast_exp2(M - mn);
       const float cb = fast_exp2(mv[k] - mn);
       L = L * ca + lv[k] * cb;
-      a0 = a0 * ca + xv[k].x * cb;
-      a1 = a1 * ca + xv[k].y * cb;
+#pragma unroll
+      for (int j = 0; j < kCh; ++j) acc[j] = acc[j] * ca + xv[k][j] * cb;
       M = mn;
       if (!((endm >> k) & 1u)) continue;
       const bool live = L > 0.f;
@@ -803,21 +808,31 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       if ((localm >> k) & 1u) {
         const int eb = sk / U;
         const int row0 = eb * Hq + (sk - eb * U) * HG;
-        *reinterpret_cast<uint32_t*>(a.out + (size_t)(row0 + h) * D + c) =
-            pack_bf16x2(a0 * inv, a1 * inv);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.out + (size_t)(row0 + h) * D + c);
+        if constexpr (kCh == 4)
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                                      pack_bf16x2(acc[2] * inv, acc[3] * inv));
+        else
+          *dst = pack_bf16x2(acc[0] * inv, acc[1] * inv);
       } else {
         const int row = (2 * grp + (int)((kind1m >> k) & 1u)) * HG + h;
-        __builtin_amdgcn_raw_buffer_store_b64(
-            u2v{__float_as_uint(a0 * inv), __float_as_uint(a1 * inv)},
-            opart_rs, (row * D + c) * 4, 0, kCoherent);
+        const int off = (row * D + c) * 4;
+        if constexpr (kCh == 4)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u4v{__float_as_uint(acc[0] * inv), __float_as_uint(acc[1] * inv),
+                  __float_as_uint(acc[2] * inv), __float_as_uint(acc[3] * inv)},
+              opart_rs, off, 0, kCoherent);
+        else
+          __builtin_amdgcn_raw_buffer_store_b64(
+              u2v{__float_as_uint(acc[0] * inv), __float_as_uint(acc[1] * inv)}, opart_rs, off, 0,
+              kCoherent);
         if (c == 0)
           __builtin_amdgcn_raw_buffer_store_b32(
               __float_as_uint(live ? M + fast_log2(L) : kMinusInf), lse_rs, row * 4, 0, kCoherent);
       }
       M = kFloorMax;
       L = 0.f;
-      a0 = 0.f;
-      a1 = 0.f;
+      acc = ChVec{};
     }
   }
 
