@@ -128,8 +128,9 @@ typedef struct pkv_pool {
  *  num_q_heads          Hq; num_kv_heads must divide it, and the group size
  *                       G = Hq / Hkv must be at most 4 or a multiple of 4
  *                       (else PKV_ERR_UNSUPPORTED); the decode reads each K/V
- *                       tile once per head group of min(G, 4) heads, or of 8
- *                       heads when G is a multiple of 8
+ *                       tile once per head group of min(G, 4) heads, or of 12
+ *                       heads when G is a multiple of 12, else of 8 when G is
+ *                       a multiple of 8
  *  num_kv_heads         Hkv
  *  head_dim             D, 64 or 128
  *  page_size            P, a power of two >= 16
@@ -171,7 +172,8 @@ size_t pkv_workspace_bytes(const pkv_desc* desc);
  * step, the token appended this step included) it writes
  *   kv_indptr   device int32 [batch + 1], page prefix sums as defined above,
  * and the work plan into the workspace.  Plan, with U = num_q_heads / H query
- * head groups per request (H = G for G <= 4, 8 for a multiple of 8, else 4) and
+ * head groups per request (H = G for G <= 4, 12 for a multiple of 12, 8 for a
+ * multiple of 8, else 4) and
  * T = kv_indptr[batch] * U
  * tiles:
  *   groups   W = min(num_workgroups, max(1, ceil(T / min_tiles_per_group))),

@@ -78,11 +78,15 @@ struct WsLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Query heads one decode head group covers: the whole GQA group up to four
-// heads, eight for a multiple of eight (one 16-row matrix-core tile holds up to
-// sixteen), else four; the rest of a larger group goes to sibling head groups
-// that read the same K/V tiles again.
-inline int heads_per_group(int G) { return G <= 4 ? G : (G % 8 == 0 ? 8 : 4); }
+// Query heads one decode head group covers: the largest size the decode is
+// built for (1, 2, 3, 4, 8, 12) that divides G -- the whole GQA group up to
+// four heads, twelve for a multiple of twelve, eight for a multiple of eight,
+// else four.  One 16-row matrix-core tile holds up to sixteen; sixteen-head
+// groups would not fit the merge's LDS.  The rest of a larger group goes to
+// sibling head groups that read the same K/V tiles again.
+inline int heads_per_group(int G) {
+  return G <= 4 ? G : (G % 12 == 0 ? 12 : (G % 8 == 0 ? 8 : 4));
+}
 // Query heads of one prefill row tile (16 rows = 16 / HG tokens x HG heads).
 inline int prefill_heads_per_group(int G) { return G <= 4 ? G : 4; }
 

@@ -25,6 +25,7 @@ CASES = {  # name: (Hq, Hkv, D, P, lengths)
     "g8_p64": (32, 4, 128, 64, [100, 64, 65, 1, 300, 128]),
     "g1_p32": (8, 8, 128, 32, [31, 32, 33, 2, 257]),
     "g12_p16": (48, 4, 128, 16, [1, 16, 17, 250, 47]),
+    "g20_p16": (40, 2, 128, 16, [1, 16, 17, 250, 47]),
     "g16_p32": (64, 4, 64, 32, [33, 1, 96, 500, 31]),
     "g2_p16": (8, 4, 64, 16, [5000, 3, 77]),
 }

@@ -323,17 +323,17 @@ def pin_head_groups(mod):
     only say that the query heads of one KV head read its K/V together).
 
     Three independent statements of it: the table of head-group sizes for
-    G = 1 .. 16 that the library header documents (the whole group up to four
-    heads, eight when G is a multiple of eight, else four); the same sizes
-    found by search, as the largest head-group size the kernels are built for
-    (1, 2, 3, 4, 8) that divides G; and the structure every grouping must have
-    (a group lies inside one KV head, and the groups cover the query heads
-    exactly once)."""
-    table = {1: 1, 2: 2, 3: 3, 4: 4, 8: 8, 12: 4, 16: 8}
+    G = 1 .. 24 that the library header documents (the whole group up to four
+    heads, twelve when G is a multiple of twelve, eight when it is a multiple
+    of eight, else four); the same sizes found by search, as the largest
+    head-group size the kernels are built for (1, 2, 3, 4, 8, 12) that divides
+    G; and the structure every grouping must have (a group lies inside one KV
+    head, and the groups cover the query heads exactly once)."""
+    table = {1: 1, 2: 2, 3: 3, 4: 4, 8: 8, 12: 12, 16: 8, 20: 4, 24: 12}
     for G, hg in table.items():
         for Hkv in (1, 2, 8):
             assert mod.head_groups(G * Hkv, Hkv) == (hg, G * Hkv // hg), (G, Hkv)
-    built = (1, 2, 3, 4, 8)
+    built = (1, 2, 3, 4, 8, 12)
     for G in [g for g in range(1, 65) if g <= 4 or g % 4 == 0]:
         for Hkv in (1, 3, 8):
             Hq = G * Hkv
@@ -730,6 +730,12 @@ def _mutants():
     m["head_groups_four_at_g8"] = {
         "head_groups": lambda Hq, Hkv: ((Hq // Hkv if Hq // Hkv <= 4 else 4),
                                         Hq // (Hq // Hkv if Hq // Hkv <= 4 else 4))}
+    # the grouping before groups of twelve existed: four heads at G = 12
+    m["head_groups_four_at_g12"] = {
+        "head_groups": lambda Hq, Hkv: ((Hq // Hkv if Hq // Hkv <= 4 else
+                                         (8 if (Hq // Hkv) % 8 == 0 else 4)),
+                                        Hq // (Hq // Hkv if Hq // Hkv <= 4 else
+                                               (8 if (Hq // Hkv) % 8 == 0 else 4)))}
     # groups of eight for any G above four (splits a KV head's heads at G = 12)
     m["head_groups_eight_above_four"] = {
         "head_groups": lambda Hq, Hkv: ((Hq // Hkv if Hq // Hkv <= 4 else 8),
