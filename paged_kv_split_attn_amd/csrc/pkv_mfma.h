@@ -84,6 +84,7 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 
 // MFMA operand vectors.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 

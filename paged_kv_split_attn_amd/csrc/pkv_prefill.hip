@@ -34,42 +34,57 @@ __device__ __forceinline__ uint32_t keys_upto(int d) {
 // reduction index runs over the eight keys lane group g holds (4g .. 4g+3 of
 // half 0, then of half 1): the weights never move between lanes, and the
 // double-rate instruction does twice the work of the 16-key one in the same
-// time.  P enters rounded to bf16 (the weights are at most 1; the row sum
-// keeps their fp32 values, and the rounding adds about 3e-5 to the mean
-// error of the fp32-accumulated output, against a 1e-3 bar; splitting P into
-// bf16 high and low parts cost a third more matrix-core time for that).
+// time.  P enters rounded to bf16 (the weights are at most 2^8 times the
+// row's running maximum weight; splitting P into bf16 high and low parts cost
+// a third more matrix-core time), and the row sums are those of the rounded
+// weights (numerator and denominator use the same weights), accumulated in
+// fp32 by four v_dot2c_f32_bf16 against a pair of ones per step.
 // Output: lane (g, r) register i of block vb of tile t holds O[row 4g+i of
 // t][channel 16 vb + r].
+//
+// The running max m is kept in the scaled log2 domain; the step compares the
+// raw scores with thr = (m + kRescaleSlack) / scale, so that the common step
+// (no rescale) needs only each lane's own maximum: the row maximum over the
+// four lane groups is formed only when some lane is over its threshold, and
+// the scale goes into the exponent's fma.  This needs scale > 0: the caller
+// folds a negative scale's sign into q and raises its magnitude to at least
+// FLT_MIN (a zero scale then gives equal weights, as exactly as before, and
+// a masked key's -inf times the scale stays -inf).
 template <int D, int NT>
 struct Wave32 {
   static constexpr int KB = D / 32;  // q.K MFMAs per half and tile
   static constexpr int VB = D / 16;  // p.V channel blocks
   floatx4_t o[NT][VB];
-  bf16x8_t qb[NT][KB];  // q^T operands (zero for unused rows)
-  float m[NT], l[NT];   // row r of tile t: running max (log2 domain), partial sum
+  bf16x8_t qb[NT][KB];  // q^T operands
+  float m[NT];          // row r of tile t: running max (scaled, log2 domain)
+  float thr[NT];        // row r of tile t: (m + kRescaleSlack) / scale
+  float l[NT];          // row r of tile t: this lane's part of its weight sum
 
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) o[t][vb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      m[t] = kFloorMax;
       l[t] = 0.f;
+      m[t] = kFloorMax;
+      thr[t] = kMinusInf;  // the first step with any live key sets m
     }
   }
 
   // k[h][kk]: K of token r of half h, channels 8 (4kk + g) .. +8.
   // load_v(vv) fills vv[vb] with channel 16 vb + r, keys 4g .. 4g+3 of half 0
-  // then of half 1; it is called after the score MFMAs, which need only K.  keep[t]: bit 4h + j set when key
-  // 16h + 4g + j counts for this lane's row of tile t.  vlive: keys from this
-  // one on hold no data (their V is zeroed); 32 when all do.  masked (uniform)
-  // false: every key of the step counts for every row of the wave, and keep
-  // and vlive are not read (most steps of a causal block lie below its
-  // diagonal, and the per-key selects are a fifth of a step's vector work).
+  // then of half 1; it is called after the score MFMAs, which need only K.
+  // keep[t]: bit 4h + j set when key 16h + 4g + j counts for this lane's row
+  // of tile t.  vlive: keys from this one on hold no data; pages_ok (uniform):
+  // bits 4h .. 4h+3 set when half h has a page; the V of keys outside both is
+  // zeroed.  masked (uniform) false: every key of the step counts for every
+  // row of the wave, and keep, vlive and pages_ok are not read (most steps of
+  // a causal block lie below its diagonal, and the per-key selects are a
+  // fifth of a step's vector work).
   template <class LoadV>
   __device__ __forceinline__ void step(const uint4 (&k)[2][KB], LoadV&& load_v,
-                                       const uint32_t (&keep)[NT], int vlive, bool masked, int g,
-                                       float scale_log2, const float (&bias)[NT]) {
+                                       const uint32_t (&keep)[NT], int vlive, uint32_t pages_ok,
+                                       bool masked, int g, float scale, float inv_scale) {
     floatx4_t sc[NT][2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) sc[t][0] = sc[t][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -91,13 +106,13 @@ struct Wave32 {
               __builtin_bit_cast(bf16x8_t, k[h][kk]), qb[t][kk], sc[t][h], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
-    float s[NT][8];
+    float s[NT][8];  // raw scores q . k
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[t][i] = fmaf(sc[t][0][i], scale_log2, bias[t]);
-        s[t][4 + i] = fmaf(sc[t][1][i], scale_log2, bias[t]);
+        s[t][i] = sc[t][0][i];
+        s[t][4 + i] = sc[t][1][i];
       }
     }
     if (masked) {
@@ -109,10 +124,11 @@ struct Wave32 {
     }
     uint4 vv[VB];
     load_v(vv);
-    if (masked && vlive < 32) {
-      // Keys past the sequence end may hold anything, NaN included: a zero
-      // weight times their V must give exactly zero.
-      const uint32_t lv = keys_upto(vlive - 1 - 4 * g);
+    if (masked && (vlive < 32 || pages_ok != 0xffu)) {
+      // Keys past the sequence end, and keys of a piece without a page, may
+      // hold anything, NaN included: a zero weight times their V must give
+      // exactly zero.
+      const uint32_t lv = keys_upto(vlive - 1 - 4 * g) & pages_ok;
       uint32_t msk[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -128,14 +144,16 @@ struct Wave32 {
     bf16x8_t pb[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const float pm = max_over_groups(vmax3(vmax3(s[t][0], s[t][1], s[t][2]),
-                                              vmax3(s[t][3], s[t][4], s[t][5]),
-                                              vmax2(s[t][6], s[t][7])));
-      if (__builtin_amdgcn_ballot_w64(pm > m[t] + kRescaleSlack) != 0) {
+      const float lm = vmax3(vmax3(s[t][0], s[t][1], s[t][2]), vmax3(s[t][3], s[t][4], s[t][5]),
+                             vmax2(s[t][6], s[t][7]));
+      if (__builtin_amdgcn_ballot_w64(lm > thr[t]) != 0) {
+        // Some row's maximum is over its threshold: form every row's maximum.
+        const float pm = max_over_groups(lm) * scale;
         const float mn = fmaxf(m[t], pm);
         const float alpha = fast_exp2(m[t] - mn);
-        l[t] *= alpha;
         m[t] = mn;
+        thr[t] = (mn + kRescaleSlack) * inv_scale;
+        l[t] *= alpha;
         // Register i of lane group g holds row 4g + i, whose factor lane 4g + i has.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -144,12 +162,14 @@ struct Wave32 {
           for (int vb = 0; vb < VB; ++vb) o[t][vb][i] *= ai;
         }
       }
-      float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[t][i] - m[t]);
-      l[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[t][i] = (__bf16)p[i];
+      for (int i = 0; i < 8; ++i) pb[t][i] = (__bf16)fast_exp2(fmaf(s[t][i], scale, -m[t]));
+      const uint4 pw = __builtin_bit_cast(uint4, pb[t]);
+      const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+      l[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.x), one2, l[t], false);
+      l[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.y), one2, l[t], false);
+      l[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.z), one2, l[t], false);
+      l[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.w), one2, l[t], false);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
@@ -247,16 +267,21 @@ prefill_kernel(PrefillArgs a) {
   const int g4 = lane >> 4;
   const int r16 = lane & 15;
   // Row r16 of tile t = (token tok0 + t QT + r16 / HG, head r16 % HG).
+  // Rows without a query token read the request's first row of q (so that
+  // every lane loads, with no masked branch around the loads): their weights
+  // are computed and never stored, and rows do not mix.
   int rt[NT], lim[NT];
   bool rvalid[NT];
-  float bias[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     rt[t] = tok0 + t * QT + r16 / HG;
     rvalid[t] = r16 < ROWS && rt[t] < n;
     lim[t] = a.causal ? L - n + rt[t] : L - 1;  // last key the row sees
-    bias[t] = rvalid[t] ? 0.f : kMinusInf;
   }
+  // The step wants a positive scale: a negative one's sign goes into q (an
+  // exact bf16 sign flip, below), and its magnitude is at least FLT_MIN.
+  const float scale = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+  const float inv_scale = 1.0f / scale;
   // Keys this wave reads, and keys the workgroup reads (its last wave's limit).
   auto block_end = [&](int t0) {
     const int last = min(t0 + NT * QT, n) - 1;
@@ -279,13 +304,25 @@ prefill_kernel(PrefillArgs a) {
           a.q + ((size_t)(q0 + (rvalid[t] ? rt[t] : 0)) * Hq + hq0 + r16 % HG) * D + g4 * 8);
 #pragma unroll
       for (int kk = 0; kk < Wave32<D, NT>::KB; ++kk) {
-        const uint4 w4 = rvalid[t] ? qp[4 * kk] : make_uint4(0, 0, 0, 0);
-        st.qb[t][kk] = __builtin_bit_cast(bf16x8_t, w4);
+        st.qb[t][kk] = __builtin_bit_cast(bf16x8_t, qp[4 * kk]);
       }
     }
     // Wait for q here: left to the first matrix-core step, the wait would sit
     // inside the KV loop and drain the next chunk's loads with it every step.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (a.scale_log2 < 0.f) {  // uniform; after the wait, so the q loads go out together
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int kk = 0; kk < Wave32<D, NT>::KB; ++kk) {
+          uint4 w4 = __builtin_bit_cast(uint4, st.qb[t][kk]);
+          w4.x ^= 0x80008000u;
+          w4.y ^= 0x80008000u;
+          w4.z ^= 0x80008000u;
+          w4.w ^= 0x80008000u;
+          st.qb[t][kk] = __builtin_bit_cast(bf16x8_t, w4);
+        }
+    }
   }
 
   const int P = a.page_size;
@@ -317,30 +354,47 @@ prefill_kernel(PrefillArgs a) {
   // pieces.  Piece y of 16 keys' K is (channel block y / 16, key y % 16);
   // piece y of their V is (channel y / 2, keys 8 (y % 2) .. +7).  A wave's 64
   // pieces lie in one 16-key piece and one operand, so page lookup and K/V
-  // choice are wave-uniform.
+  // choice are wave-uniform.  A piece whose page does not exist is not
+  // loaded: its registers keep older data, which the step masks (its keys'
+  // weights are zero and their V is zeroed), so no register is cleared per
+  // chunk.
   uint4 stage[kLoads];
-  int pids[kHalves];  // pages of the 16-key pieces of the chunk being fetched
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) stage[i] = make_uint4(0, 0, 0, 0);
+  int pids[kHalves];    // pages of the 16-key pieces of the chunk being fetched
+  uint32_t pages_next;  // bit hf: piece hf of that chunk has a page (uniform)
   auto piece = [&](int i, int& hf, int& y, bool& is_v) {
     const int xw = w * kWave + i * kThreads;  // the wave's first piece
-    hf = xw / (2 * kPieces);
+    if constexpr ((2 * kPieces) % kThreads == 0) {
+      // The workgroup's pieces i cover whole 16-key pieces: hf is known here.
+      hf = i * kThreads / (2 * kPieces);
+    } else {
+      hf = xw / (2 * kPieces);
+    }
     const int yw = xw - hf * 2 * kPieces;
     is_v = yw >= kPieces;
     y = yw - (is_v ? kPieces : 0) + lane;
   };
   auto fetch = [&](int c) {
+    uint32_t ok = 0;
 #pragma unroll
-    for (int hf = 0; hf < kHalves; ++hf)
+    for (int hf = 0; hf < kHalves; ++hf) {
       pids[hf] = c * kHalves + hf < halves ? page_of(c * kHalves + hf) : -1;
+      ok |= pids[hf] >= 0 ? 1u << hf : 0u;
+    }
+    pages_next = __builtin_amdgcn_readfirstlane(ok);
+    // Nothing is in flight here (the last chunk's loads were published), but
+    // the compiler cannot tell: without this wait it puts one between the
+    // chunk's loads (a load may skip a piece, so their registers keep older
+    // values) and the second load leaves only when the first has returned.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       int hf, y;
       bool is_v;
       piece(i, hf, y, is_v);
       const int pid = pids[hf];
-      if (pid < 0) {
-        stage[i] = make_uint4(0, 0, 0, 0);
-        continue;
-      }
+      if (pid < 0) continue;
       const int sub = (c * kHalves + hf) & ((1 << log2_s) - 1);
       const char* tile = (is_v ? vbase : kbase) + (size_t)pid * a.num_kv_heads * tile_b + head_b;
       // Step sub of the tile: V [D][16], K [D/8][16][8].
@@ -374,9 +428,7 @@ prefill_kernel(PrefillArgs a) {
   __syncthreads();
   for (int c = 0; c < chunks; ++c) {
     const int buf = c & 1;
-    int live_pids[kHalves];
-#pragma unroll
-    for (int hf = 0; hf < kHalves; ++hf) live_pids[hf] = pids[hf];
+    const uint32_t pages_live = pages_next;
     if (c + 1 < chunks) fetch(c + 1);  // in flight while this chunk is consumed
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
@@ -396,20 +448,19 @@ prefill_kernel(PrefillArgs a) {
         // Key t0 + 16h + 4 g4 + j counts for a row when it is at most
         // min(lim, kv_end - 1) and its page exists; when that holds for all 32
         // keys and every row of the wave (uniform), no key is masked.
-        const bool pages_all = (live_pids[2 * s] >= 0) & (live_pids[2 * s + 1] >= 0);
-        const bool masked = !(pages_all && t0 + 31 <= lim_min);
+        const uint32_t pages_ok = ((pages_live >> (2 * s)) & 1u ? 0x0fu : 0u) |
+                                  ((pages_live >> (2 * s + 1)) & 1u ? 0xf0u : 0u);
+        const bool masked = !(pages_ok == 0xffu && t0 + 31 <= lim_min);
         const int vlive = min(32, kv_end - t0);
         uint32_t keep[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) keep[t] = 0xffu;
         if (masked) {
-          const uint32_t pages_ok = (live_pids[2 * s] < 0 ? 0u : 0x0fu) |
-                                    (live_pids[2 * s + 1] < 0 ? 0u : 0xf0u);
 #pragma unroll
           for (int t = 0; t < NT; ++t)
             keep[t] = keys_upto(min(lim[t], kv_end - 1) - t0 - 4 * g4) & pages_ok;
         }
-        st.step(kop, load_v, keep, vlive, masked, g4, a.scale_log2, bias);
+        st.step(kop, load_v, keep, vlive, pages_ok, masked, g4, scale, inv_scale);
       }
     }
     // The other buffer held chunk c - 1, which every wave finished before the

@@ -7,6 +7,8 @@ pkv_build_metadata, as in a serving step.  Outputs start as NaN, so a row the
 kernel skips shows up.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -81,6 +83,27 @@ def test_prefill_parity(case, causal):
     batch = W.make_prefill(name=case, seed=sum(map(ord, case)), **CASES[case])
     got = run_prefill(batch, causal)
     compare(got, oracle_prefill(batch, causal), f"prefill {case} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [-1.0 / np.sqrt(128.0), 0.0, 1.0],
+                         ids=["negative", "zero", "large"])
+def test_prefill_scale_sign_and_size(scale):
+    # The kernel compares raw scores against a threshold divided by a positive
+    # scale: a negative scale's sign goes into q, a zero scale gives equal
+    # weights to the visible keys, and a large one (scores with a standard
+    # deviation of about 16 log2 units) makes many steps raise the running max.
+    # V is scaled by 1/4 (exact in bf16): a sharp softmax puts outputs near
+    # single V values, and at |o| ~ 3 the bf16 rounding of the output alone is
+    # 7.8e-3, which with the bf16 weights' rounding exceeds the 1e-2 bar at
+    # scale 1 for any kernel that rounds them (1.4e-2 measured).
+    say(f"prefill sm_scale={scale}")
+    batch = W.make_prefill(name="scale", seed=9, Hq=8, Hkv=2, D=128, P=16, q_lens=[40, 7, 1],
+                           prefix_lens=[30, 100, 0])
+    v_quarter = W.f32_to_bf16_bits(W.bf16_bits_to_f32(batch.v_pool) * np.float32(0.25))
+    batch = dataclasses.replace(batch, sm_scale=scale, v_pool=v_quarter)
+    for causal in (True, False):
+        got = run_prefill(batch, causal)
+        compare(got, oracle_prefill(batch, causal), f"sm_scale={scale} causal={causal}")
 
 
 def test_prefill_single_rows_match_decode_semantics():
