@@ -384,6 +384,10 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
 
   const int g4 = lane >> 4;   // lane group: tokens 4*g4 .. 4*g4+3 of a step
   const int r16 = lane & 15;  // head of the scores / channel of the outputs
+  // Channel of output column r16 of P.V block vb: 16 vb + r16, or for
+  // token-major K/V (whose V is read as contiguous channels per token)
+  // (D / 16) r16 + vb.
+  auto out_ch = [&](int vb) { return TOKENS ? (D / 16) * r16 + vb : 16 * vb + r16; };
   const float bias = r16 < HG ? 0.f : kMinusInf;
   const int P = a.page_size;
   const int log2_s = a.log2_steps;  // steps of 16 tokens per page
@@ -472,24 +476,32 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       }
     }
 
-    // Token-major K/V: blocks of 4 steps, lane i holding the slot of token
-    // 16 (p + jb) + i of the block (its K row for lane r16 = i, its V element
-    // for the lanes whose four tokens include it, both fetched by a lane
-    // shuffle), or -1 past the sequence or for an unusable slot.
-    constexpr int kBlock = TOKENS ? 4 : kWave;
+    // Token-major K/V: blocks of 16 steps, register r of lane i holding the
+    // slot of token 16 (p + jb) + 64 r + i of the block (its K row for lane
+    // r16 of step 4 r + i / 16, its V row for the lanes whose four tokens
+    // include it, both fetched by a lane shuffle), or -1 past the sequence or
+    // for an unusable slot.  (With one register, blocks of 4 steps, the
+    // register ring restarted every 4 steps behind a slot-id load.)
+    constexpr int kTokRegs = 4;
+    constexpr int kBlock = TOKENS ? 4 * kTokRegs : kWave;
     for (int jb = 0; jb < len; jb += kBlock) {
       const int nb = min(kBlock, len - jb);
       int vpage = -1;
+      int vslot[TOKENS ? kTokRegs : 1];
       if constexpr (TOKENS) {
-        const int tk = (p + jb) * 16 + lane;
-        if (lane < nb * 16 && tk < L) {
-          if (tk >= a.table_stride) {
-            err |= kErrBadIndexPos;
-          } else {
-            const int pos = b * a.table_stride + tk;  // below 2^31 (checked on the host)
-            const int slot = a.slot_table ? a.slot_table[pos] : pos;
-            if (slot < 0 || slot >= a.num_slots) err |= kErrBadPageId;
-            else vpage = slot;
+#pragma unroll
+        for (int r = 0; r < kTokRegs; ++r) {
+          vslot[r] = -1;
+          const int tk = (p + jb) * 16 + 64 * r + lane;
+          if (64 * r + lane < nb * 16 && tk < L) {
+            if (tk >= a.table_stride) {
+              err |= kErrBadIndexPos;
+            } else {
+              const int pos = b * a.table_stride + tk;  // below 2^31 (checked on the host)
+              const int slot = a.slot_table ? a.slot_table[pos] : pos;
+              if (slot < 0 || slot >= a.num_slots) err |= kErrBadPageId;
+              else vslot[r] = slot;
+            }
           }
         }
       } else {
@@ -519,32 +531,76 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         const int jc = j < ns ? j : ns - 1;
         const char* khead = kbase + (size_t)g * D * 2;
         const char* vhead = vbase + (size_t)g * D * 2;
+        // The slot register of step jc (uniform choice), and its first lane.
+        const int reg = jc >> 2;
+        int vs = vslot[0];
+#pragma unroll
+        for (int r = 1; r < kTokRegs; ++r) vs = reg == r ? vslot[r] : vs;
+        const int l0 = 16 * (jc & 3);
         // K: lane (g4, r16) reads channels 8 (4kk + g4) .. +8 of token r16.
-        const int sk = __shfl(vpage, 16 * jc + r16, kWave);
+        const int sk = __shfl(vs, l0 + r16, kWave);
         const char* kq = khead + (size_t)(sk < 0 ? 0 : sk) * slot_b + g4 * 16;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) sd.k[kk] = *reinterpret_cast<const uint4*>(kq + kk * 64);
-        // V^T: channel 16 vb + r16 of tokens 4 g4 .. 4 g4 + 3, one element each;
-        // an unusable slot reads slot 0 and contributes zero (keep byte 0, V 0).
+        // V: lane (g4, r16) reads channels VB r16 .. VB r16 + VB - 1 of each of
+        // tokens 4 g4 .. 4 g4 + 3 (one 2 VB-byte load per token; sd.v holds
+        // token i's channels in its entries VB/4 i ..); consume() turns them
+        // into the V^T operand with column r of block vb = channel VB r + vb.
+        // An unusable slot reads slot 0 and gets keep byte 0 (its V is zeroed
+        // in consume()).
+        constexpr int VB = D / 16;
         int sv[4];
         uint32_t keep = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sv[i] = __shfl(vpage, 16 * jc + 4 * g4 + i, kWave);
+          sv[i] = __shfl(vs, l0 + 4 * g4 + i, kWave);
           keep |= (sv[i] >= 0 ? 1u : 0u) << (8 * i);
-        }
-#pragma unroll
-        for (int vb = 0; vb < D / 16; ++vb) {
-          uint32_t e[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint16_t x = *reinterpret_cast<const uint16_t*>(
-                vhead + (size_t)(sv[i] < 0 ? 0 : sv[i]) * slot_b + (16 * vb + r16) * 2);
-            e[i] = sv[i] < 0 ? 0u : (uint32_t)x;
+          const char* vq = vhead + (size_t)(sv[i] < 0 ? 0 : sv[i]) * slot_b + r16 * (2 * VB);
+          if constexpr (VB == 8) {
+            const uint4 x = *reinterpret_cast<const uint4*>(vq);
+            sd.v[2 * i] = make_uint2(x.x, x.y);
+            sd.v[2 * i + 1] = make_uint2(x.z, x.w);
+          } else {
+            sd.v[i] = *reinterpret_cast<const uint2*>(vq);
           }
-          sd.v[vb] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
         }
         sd.keep = keep;
+      };
+      // Token-major V, as loaded, into the V^T operand: block vb takes half
+      // vb % 2 of dword vb / 2 of each token's channels.
+      auto transpose_tokens_v = [&](Step<D>& sd) {
+        constexpr int VB = D / 16;
+        constexpr int PER = VB / 2;  // dwords of one token's channels
+        uint32_t wv[4][PER];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < PER; ++j) {
+            const uint2 u = sd.v[i * PER / 2 + j / 2];
+            wv[i][j] = (j & 1) ? u.y : u.x;
+          }
+        if (__builtin_amdgcn_ballot_w64(sd.keep != 0x01010101u) != 0) {
+          // Some lane has a token without a usable slot (past the sequence
+          // end, or a bad slot id): zero its V so that its zero weight gives
+          // exactly zero.
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = ((sd.keep >> (8 * i)) & 0xffu) != 0;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) wv[i][j] = ok ? wv[i][j] : 0u;
+          }
+        }
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          const int j = vb >> 1;
+          if (vb & 1) {
+            sd.v[vb] = make_uint2((wv[0][j] >> 16) | (wv[1][j] & 0xffff0000u),
+                                  (wv[2][j] >> 16) | (wv[3][j] & 0xffff0000u));
+          } else {
+            sd.v[vb] = make_uint2((wv[0][j] & 0xffffu) | (wv[1][j] << 16),
+                                  (wv[2][j] & 0xffffu) | (wv[3][j] << 16));
+          }
+        }
       };
       auto issue = [&](int j, Step<D>& sd) {
         if constexpr (TOKENS) {
@@ -574,6 +630,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
       auto consume = [&](int j, Step<D>& sd) {
         if constexpr (TOKENS) {
           const int t0 = (p + jb + j) * 16;
+          transpose_tokens_v(sd);
           st.step(sd, min(16, max(0, L - t0)), g4, a.scale_log2, bias, sd.keep);
           return;
         }
@@ -660,7 +717,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         if (g4 == (i >> 2)) {  // head i: register i % 4 of lane group i / 4
 #pragma unroll
           for (int vb = 0; vb < MfmaWave<D, HG>::VB; ++vb)
-            s_out[w][i][16 * vb + r16] = st.o[vb][i & 3] * inv;
+            s_out[w][i][out_ch(vb)] = st.o[vb][i & 3] * inv;
         }
       }
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes land first
@@ -684,7 +741,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         if (g4 == (i >> 2)) {
 #pragma unroll
           for (int vb = 0; vb < MfmaWave<D, HG>::VB; ++vb)
-            s_acc[w][slot][i][16 * vb + r16] = st.o[vb][i & 3];
+            s_acc[w][slot][i][out_ch(vb)] = st.o[vb][i & 3];
         }
         if (lane == i) {
           s_m[i][2 * w + slot] = st.m;
