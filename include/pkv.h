@@ -241,7 +241,8 @@ int pkv_append_kv_ragged(const pkv_pool* pool, const void* k_new, const void* v_
  *  kv_indptr    device int32 [batch + 1] written by pkv_build_metadata this step
  *  kv_indices   device int32 [num_indices] (may be NULL when num_indices is 0)
  *  seq_lens     device int32 [batch], the same array pkv_build_metadata read
- *  sm_scale     softmax scale (usually 1 / sqrt(head_dim))
+ *  sm_scale     softmax scale (usually 1 / sqrt(head_dim)); any value but NaN,
+ *               zero and negative included (zero gives equal weights)
  *  workspace    the workspace pkv_build_metadata wrote this step
  *  out          device bf16 [batch][num_q_heads][head_dim]; a request with
  *               seq_len 0 gets a zero row

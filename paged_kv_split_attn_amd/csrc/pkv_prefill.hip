@@ -34,9 +34,10 @@ __device__ __forceinline__ uint32_t keys_upto(int d) {
 // reduction index runs over the eight keys lane group g holds (4g .. 4g+3 of
 // half 0, then of half 1): the weights never move between lanes, and the
 // double-rate instruction does twice the work of the 16-key one in the same
-// time.  P enters rounded to bf16 (the weights are at most 2^8 times the
-// row's running maximum weight; splitting P into bf16 high and low parts cost
-// a third more matrix-core time), and the row sums are those of the rounded
+// time.  P enters rounded to bf16 (a weight is at most 2^8: a row is rescaled
+// once a score passes its running max by kRescaleSlack in the log2 domain;
+// splitting P into bf16 high and low parts cost a third more matrix-core
+// time), and the row sums are those of the rounded
 // weights (numerator and denominator use the same weights), accumulated in
 // fp32 by four v_dot2c_f32_bf16 against a pair of ones per step.
 // Output: lane (g, r) register i of block vb of tile t holds O[row 4g+i of
@@ -46,10 +47,10 @@ __device__ __forceinline__ uint32_t keys_upto(int d) {
 // raw scores with thr = (m + kRescaleSlack) / scale, so that the common step
 // (no rescale) needs only each lane's own maximum: the row maximum over the
 // four lane groups is formed only when some lane is over its threshold, and
-// the scale goes into the exponent's fma.  This needs scale > 0: the caller
+// the scale goes into the exponent's fma.  This needs scale > 0: the kernel
 // folds a negative scale's sign into q and raises its magnitude to at least
-// FLT_MIN (a zero scale then gives equal weights, as exactly as before, and
-// a masked key's -inf times the scale stays -inf).
+// FLT_MIN (so a zero scale gives equal weights to the visible keys, and a
+// masked key's -inf times the scale stays -inf).
 template <int D, int NT>
 struct Wave32 {
   static constexpr int KB = D / 32;  // q.K MFMAs per half and tile

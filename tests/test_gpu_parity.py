@@ -7,6 +7,8 @@ slot and the workspace starts as all-ones bytes (NaN as fp32), so any stray
 read or unwritten partial shows up as NaN.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -350,6 +352,21 @@ def test_decode_shapes(Hq, Hkv, D, P):
         desc = make_desc(batch, num_workgroups=grid, min_tiles=1)
         got = GpuRun(batch, desc).step(forced)
         compare(got, expect, f"Hq={Hq} Hkv={Hkv} D={D} P={P} forced={forced}")
+
+
+@pytest.mark.parametrize("scale", [-1.0 / np.sqrt(128.0), 0.0], ids=["negative", "zero"])
+def test_decode_scale_sign_and_zero(scale):
+    # Any scale but NaN is accepted: a negative one reverses which keys weigh
+    # most, and zero gives every live token of a request the same weight.
+    say(f"decode sm_scale={scale}")
+    batch = dataclasses.replace(
+        W.make_batch(name="scale", seed=77, B=5, Hq=32, Hkv=8, D=128, P=16,
+                     lengths=np.array([1, 15, 17, 83, 700])), sm_scale=scale)
+    expect = oracle_out(batch)
+    for grid, forced in ((0, 0), (300, 300)):
+        desc = make_desc(batch, num_workgroups=grid, min_tiles=1)
+        got = GpuRun(batch, desc).step(forced)
+        compare(got, expect, f"sm_scale={scale} forced={forced}")
 
 
 def test_seq_len_one_is_exact():
