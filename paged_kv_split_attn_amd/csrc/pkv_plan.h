@@ -57,9 +57,12 @@ struct PlanMath {
   // First tile of workgroup i (i <= W): floor(i T / W) = i q + floor(i r / W),
   // where i r <= 65536 * 65535 fits 32 bits.
   __device__ I start(uint32_t i) const { return (I)i * q + (I)(i * (uint32_t)r / W); }
-  // floor(w len / 8) without forming w len.
+  // floor(w len / kWavesPerGroup) without forming w len.
   __device__ static I part(I len, int w) {
-    return (I)w * (len >> 3) + (I)(((uint32_t)w * (uint32_t)(len & 7)) >> 3);
+    static_assert((kWavesPerGroup & (kWavesPerGroup - 1)) == 0, "a power-of-two wave count");
+    constexpr int kShift = __builtin_ctz(kWavesPerGroup);
+    return (I)w * (len >> kShift) +
+           (I)(((uint32_t)w * (uint32_t)(len & (kWavesPerGroup - 1))) >> kShift);
   }
   // Workgroup that owns tile t: floor(((t + 1) W - 1) / T), the largest i with
   // start(i) <= t.  In 32-bit plans the dividend is below 2^47, so a double
