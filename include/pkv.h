@@ -86,7 +86,7 @@ extern "C" {
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1,          /* null pointer, negative size, inconsistent shapes */
-  PKV_ERR_UNSUPPORTED = 2,          /* head_dim / page_size / group size not compiled in */
+  PKV_ERR_UNSUPPORTED = 2,          /* head_dim / page_size not compiled in */
   PKV_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below pkv_workspace_bytes(desc) */
   PKV_ERR_CAPACITY = 4,             /* batch or forced split count above the descriptor's capacity */
   PKV_ERR_LAUNCH = 5,               /* the HIP runtime rejected a kernel launch */
@@ -126,11 +126,10 @@ typedef struct pkv_pool {
  *
  *  max_batch            requests per call (1 .. 65536)
  *  num_q_heads          Hq; num_kv_heads must divide it, and the group size
- *                       G = Hq / Hkv must be at most 4 or a multiple of 4
- *                       (else PKV_ERR_UNSUPPORTED); the decode reads each K/V
- *                       tile once per head group of min(G, 4) heads, or of 12
- *                       heads when G is a multiple of 12, else of 8 when G is
- *                       a multiple of 8
+ *                       G = Hq / Hkv may be any size; the decode reads each
+ *                       K/V tile once per head group of H heads, H the
+ *                       largest of 1 .. 8 and 12 that divides G (all of G up
+ *                       to 8; a prime G above 8 reads each tile G times)
  *  num_kv_heads         Hkv
  *  head_dim             D, 64 or 128
  *  page_size            P, a power of two >= 16
@@ -172,8 +171,7 @@ size_t pkv_workspace_bytes(const pkv_desc* desc);
  * step, the token appended this step included) it writes
  *   kv_indptr   device int32 [batch + 1], page prefix sums as defined above,
  * and the work plan into the workspace.  Plan, with U = num_q_heads / H query
- * head groups per request (H = G for G <= 4, 12 for a multiple of 12, 8 for a
- * multiple of 8, else 4) and
+ * head groups per request (H the largest of 1 .. 8 and 12 that divides G) and
  * T = kv_indptr[batch] * U
  * tiles:
  *   groups   W = min(num_workgroups, max(1, ceil(T / min_tiles_per_group))),

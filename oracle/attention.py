@@ -291,14 +291,13 @@ def even_page_ranges(n_pages: int, nsplit: int) -> List[Tuple[int, int]]:
 def head_groups(Hq: int, Hkv: int) -> Tuple[int, int]:
     """(HG, U): query heads per head group and head groups per request.
 
-    A head group is query heads of one KV head: all of them up to four, twelve
-    when their number is a multiple of twelve, eight when it is a multiple of
-    eight, else four; a KV head with more query heads than that gets several
-    head groups.  (The grouping is the decode plan's, not the pages': it only
+    A head group is query heads of one KV head: the largest number of them
+    in 1 .. 8 or 12 that divides G (all of them up to eight); a KV head with
+    more query heads than that gets several head groups.  (The grouping is the decode plan's, not the pages': it only
     orders the plan's tiles.)
     """
     G = Hq // Hkv
-    HG = G if G <= 4 else (12 if G % 12 == 0 else (8 if G % 8 == 0 else 4))
+    HG = max(h for h in (1, 2, 3, 4, 5, 6, 7, 8, 12) if G % h == 0)
     return HG, Hq // HG
 
 

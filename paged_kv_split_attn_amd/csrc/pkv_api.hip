@@ -46,7 +46,7 @@ bool supported(int head_dim, int page_size, int G) {
   if (head_dim != 64 && head_dim != 128) return false;
   // A wave consumes 16 tokens of one page per step.
   if (page_size < 16 || (page_size & (page_size - 1)) != 0) return false;
-  if (G < 1 || (G > 4 && G % 4 != 0)) return false;
+  if (G < 1) return false;
   return true;
 }
 

@@ -6,9 +6,8 @@
 // wave.  Each wave keeps two steps of loads in flight; two waves per SIMD hide
 // each other's tail of a step better than one wave with a deeper register ring
 // (which measured slower at every depth).  A head group is HG query heads
-// that share one KV head (HG = G for G <= 4, else 12, 8 or 4, the largest that
-// divides G), so a tile is one page of one KV
-// head, K and V, read once for HG query heads.  Each wave streams its range,
+// that share one KV head (the largest of 12, 8, 7, .., 1 that divides G), so
+// a tile is one page of one KV head, K and V, read once for HG query heads.  Each wave streams its range,
 // keeping an online-softmax state that it closes whenever the range leaves a
 // (request, head group) segment.  A segment wholly inside a wave is written
 // straight to the output; other pieces go to LDS, where the workgroup merges
@@ -1049,6 +1048,9 @@ hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
     case 2: hipLaunchKernelGGL((decode_kernel<D, 2, KIND, PLAN>), grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL((decode_kernel<D, 3, KIND, PLAN>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((decode_kernel<D, 4, KIND, PLAN>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((decode_kernel<D, 5, KIND, PLAN>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((decode_kernel<D, 6, KIND, PLAN>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((decode_kernel<D, 7, KIND, PLAN>), grid, block, 0, s, a); break;
     case 8: hipLaunchKernelGGL((decode_kernel<D, 8, KIND, PLAN>), grid, block, 0, s, a); break;
     case 12: hipLaunchKernelGGL((decode_kernel<D, 12, KIND, PLAN>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;

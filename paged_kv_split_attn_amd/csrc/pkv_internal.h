@@ -79,16 +79,27 @@ struct WsLayout {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Query heads one decode head group covers: the largest size the decode is
-// built for (1, 2, 3, 4, 8, 12) that divides G -- the whole GQA group up to
-// four heads, twelve for a multiple of twelve, eight for a multiple of eight,
-// else four.  One 16-row matrix-core tile holds up to sixteen; sixteen-head
-// groups would not fit the merge's LDS.  The rest of a larger group goes to
-// sibling head groups that read the same K/V tiles again.
+// built for (1 .. 8, 12) that divides G (G >= 1) -- the whole GQA group up
+// to eight heads.  One 16-row matrix-core tile holds up to sixteen;
+// sixteen-head groups would not fit the merge's LDS.  The rest of a larger
+// group goes to sibling head groups that read the same K/V tiles again, so
+// the largest divisor means the fewest passes over each KV head.
 inline int heads_per_group(int G) {
-  return G <= 4 ? G : (G % 12 == 0 ? 12 : (G % 8 == 0 ? 8 : 4));
+  constexpr int kBuilt[] = {12, 8, 7, 6, 5, 4, 3, 2};
+  for (int h : kBuilt)
+    if (G % h == 0) return h;
+  return 1;
 }
-// Query heads of one prefill row tile (16 rows = 16 / HG tokens x HG heads).
-inline int prefill_heads_per_group(int G) { return G <= 4 ? G : 4; }
+// Query heads of one prefill row tile (16 rows hold 16 / HG tokens x HG
+// heads): the whole group up to seven heads, else four when four divide G
+// (every row of the tile used), else the largest size up to seven that does.
+inline int prefill_heads_per_group(int G) {
+  if (G <= 7) return G;
+  if (G % 4 == 0) return 4;
+  for (int h = 7; h > 1; --h)
+    if (G % h == 0) return h;
+  return 1;
+}
 
 // Returns false for an invalid descriptor; `groups` is the resolved grid size.
 bool ws_layout(const pkv_desc& d, int groups, WsLayout* out);

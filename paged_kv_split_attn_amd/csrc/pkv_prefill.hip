@@ -516,6 +516,9 @@ hipError_t launch_p(const PrefillArgs& a, int hg, dim3 grid, hipStream_t s) {
     case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL((prefill_kernel<D, 3>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((prefill_kernel<D, 5>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((prefill_kernel<D, 6>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((prefill_kernel<D, 7>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -105,9 +105,8 @@ def test_host_checks_reject_before_launch(lib):
                 ws_bytes - 1, fake, None) == 3
     # negative forced workgroup count
     assert _raw(lib, "pkv_build_metadata", B(d), fake, 4, -1, fake, fake, ws_bytes, None) == 1
-    # unsupported head_dim / page_size / group size
-    for bad in (dict(head_dim=96), dict(page_size=12), dict(page_size=24),
-                dict(num_q_heads=48, num_kv_heads=8)):
+    # unsupported head_dim / page_size (every group size G is supported)
+    for bad in (dict(head_dim=96), dict(page_size=12), dict(page_size=24)):
         db = _desc(**bad)
         assert _raw(lib, "pkv_build_metadata", B(db.c()), fake, 4, 0, fake, fake, 1 << 30,
                     None) == 2

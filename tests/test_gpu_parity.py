@@ -46,13 +46,13 @@ def _random_lengths_batch(seed, B, with_zeros):
 
 
 # Plans away from four query heads per KV head and pages of 16 tokens:
-# (Hq, Hkv, P) -> head groups of G (G <= 4), of twelve (G = 12), of eight (G a
-# multiple of 8, two groups per KV head at G = 16) or of four (G = 20: five
-# groups per KV head).
+# (Hq, Hkv, P) -> head groups of the largest of 1 .. 8 and 12 that divides G:
+# all of G up to eight (G = 1, 3, 6, 7, 8), twelve (G = 12), eight (G = 16: two
+# groups per KV head), five (G = 20: four groups) or one (G = 11, a prime).
 PLAN_SHAPES = {
     "g8": (64, 8, 16), "g3": (24, 8, 16), "g12": (48, 4, 16), "g1": (8, 8, 16),
-    "g16": (128, 8, 16), "g20": (40, 2, 16), "g4_p32": (32, 8, 32), "g4_p64": (32, 8, 64),
-    "g8_p64": (64, 8, 64),
+    "g16": (128, 8, 16), "g20": (40, 2, 16), "g6": (48, 8, 16), "g7": (28, 4, 16),
+    "g11": (22, 2, 16), "g4_p32": (32, 8, 32), "g4_p64": (32, 8, 64), "g8_p64": (64, 8, 64),
 }
 
 
@@ -200,8 +200,12 @@ FUSED_CASES = {  # name: (Hq, Hkv, D, P, lengths)
     "g1_p32": (8, 8, 128, 32, [31, 32, 33, 2, 257]),
     # one head group of twelve per KV head
     "g12_p16": (48, 4, 128, 16, [1, 16, 17, 250, 47]),
-    # five head groups of four per KV head: only the first writes the token
+    # four head groups of five per KV head: only the first writes the token
     "g20_p16": (40, 2, 128, 16, [1, 16, 17, 250, 47]),
+    # one head group of seven per KV head
+    "g7_p16": (28, 4, 128, 16, [1, 16, 17, 250, 47]),
+    # two head groups of five per KV head
+    "g10_p32": (20, 2, 64, 32, [2, 31, 32, 33, 400]),
     # two head groups of eight per KV head
     "g16_p32": (64, 4, 64, 32, [33, 1, 96, 500, 31]),
 }
@@ -336,7 +340,12 @@ def test_repeated_decodes_reuse_one_plan():
     (24, 8, 64, 16),   # G = 3
     (64, 8, 128, 16),  # G = 8: one head group of eight per KV head
     (48, 4, 128, 16),  # G = 12: one head group of twelve per KV head
-    (40, 2, 128, 16),  # G = 20: five head groups of four per KV head
+    (40, 2, 128, 16),  # G = 20: four head groups of five per KV head
+    (40, 8, 128, 16),  # G = 5: one head group of five
+    (48, 8, 64, 16),   # G = 6: one head group of six
+    (28, 4, 128, 16),  # G = 7: one head group of seven
+    (36, 4, 64, 16),   # G = 9: three head groups of three per KV head
+    (22, 2, 128, 16),  # G = 11: eleven head groups of one per KV head
     (128, 8, 64, 16),  # G = 16: two head groups of eight per KV head
     (96, 8, 128, 32),  # G = 12 with pages of 32
     (32, 4, 64, 32),   # two rounds per page at D = 64

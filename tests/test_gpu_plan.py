@@ -26,6 +26,8 @@ CASES = {  # name: (Hq, Hkv, D, P, lengths)
     "g1_p32": (8, 8, 128, 32, [31, 32, 33, 2, 257]),
     "g12_p16": (48, 4, 128, 16, [1, 16, 17, 250, 47]),
     "g20_p16": (40, 2, 128, 16, [1, 16, 17, 250, 47]),
+    "g6_p16": (48, 8, 64, 16, [1, 16, 17, 250, 47]),
+    "g10_p32": (20, 2, 128, 32, [2, 31, 32, 33, 400]),
     "g16_p32": (64, 4, 64, 32, [33, 1, 96, 500, 31]),
     "g2_p16": (8, 4, 64, 16, [5000, 3, 77]),
 }

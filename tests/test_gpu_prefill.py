@@ -1,7 +1,7 @@
 """Parity of the HIP paged prefill / extend kernel with the fp64 oracle.
 
 Query rows of ragged lengths attend to each request's paged KV (prefix plus the
-new tokens), with and without the causal mask, for G = 1, 2, 3, 4, 8, head dims
+new tokens), with and without the causal mask, for G = 1 .. 8, 10 and 12, head dims
 64 and 128 and pages of 16, 32 and 64 tokens.  The metadata comes from
 pkv_build_metadata, as in a serving step.  Outputs start as NaN, so a row the
 kernel skips shows up.
@@ -27,6 +27,13 @@ CASES = {
     "g3": dict(Hq=24, Hkv=8, D=64, P=16, q_lens=[11, 6], prefix_lens=[4, 20]),
     "g8_p64": dict(Hq=32, Hkv=4, D=128, P=64, q_lens=[50, 3], prefix_lens=[77, 128]),
     "square_512": dict(Hq=32, Hkv=8, D=128, P=16, q_lens=[512, 300], prefix_lens=[0, 0]),
+    # row tiles of 3 tokens x 5 heads, 2 x 6 and 2 x 7 (15, 12 and 14 of 16 rows)
+    "g5": dict(Hq=10, Hkv=2, D=128, P=16, q_lens=[20, 1, 33], prefix_lens=[7, 40, 0]),
+    "g6_d64": dict(Hq=24, Hkv=4, D=64, P=32, q_lens=[9, 50], prefix_lens=[100, 3]),
+    "g7": dict(Hq=14, Hkv=2, D=128, P=16, q_lens=[17, 64], prefix_lens=[0, 31]),
+    # two row-tile head groups of five per KV head; three of four at G = 12
+    "g10": dict(Hq=20, Hkv=2, D=128, P=16, q_lens=[25, 6], prefix_lens=[12, 70]),
+    "g12": dict(Hq=24, Hkv=2, D=64, P=16, q_lens=[11, 40], prefix_lens=[33, 0]),
 }
 
 

@@ -25,6 +25,7 @@ CASES = {
     "table_g1": dict(B=3, Hq=4, Hkv=4, D=128, lengths=[17, 300, 5], table=True),
     "table_g3": dict(B=3, Hq=24, Hkv=8, D=64, lengths=[40, 1, 129], table=True),
     "table_g8": dict(B=2, Hq=32, Hkv=4, D=128, lengths=[250, 31], table=True),
+    "table_g7": dict(B=3, Hq=28, Hkv=4, D=128, lengths=[90, 1, 333], table=True),
     "contig_d128": dict(B=4, Hq=32, Hkv=8, D=128, lengths=[100, 1, 700, 0], table=False,
                         stride=704),
     "contig_d64": dict(B=3, Hq=8, Hkv=2, D=64, lengths=[33, 64, 5], table=False, stride=64),

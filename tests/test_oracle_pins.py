@@ -322,23 +322,27 @@ def pin_head_groups(mod):
     """The decode plan's head grouping (a rule of this library's plan; the pages
     only say that the query heads of one KV head read its K/V together).
 
-    Three independent statements of it: the table of head-group sizes for
-    G = 1 .. 24 that the library header documents (the whole group up to four
-    heads, twelve when G is a multiple of twelve, eight when it is a multiple
-    of eight, else four); the same sizes found by search, as the largest
-    head-group size the kernels are built for (1, 2, 3, 4, 8, 12) that divides
-    G; and the structure every grouping must have (a group lies inside one KV
-    head, and the groups cover the query heads exactly once)."""
-    table = {1: 1, 2: 2, 3: 3, 4: 4, 8: 8, 12: 12, 16: 8, 20: 4, 24: 12}
+    Three statements of it: the table of head-group sizes that the library
+    header documents, written out by hand (the largest of 1 .. 8 and 12 that
+    divides G: all of a KV head's query heads up to eight, then twelve, eight,
+    seven, ..., one); the same sizes found by counting, for every size built,
+    the passes over each KV head it needs (G / HG, fewest wins, only sizes that
+    divide G allowed); and the structure every grouping must have (a group
+    lies inside one KV head, and the groups cover the query heads exactly
+    once)."""
+    table = {1: 1, 2: 2, 3: 3, 4: 4, 5: 5, 6: 6, 7: 7, 8: 8, 9: 3, 10: 5, 11: 1, 12: 12,
+             13: 1, 14: 7, 15: 5, 16: 8, 18: 6, 20: 5, 21: 7, 24: 12, 28: 7, 32: 8, 36: 12,
+             44: 4, 48: 12}
     for G, hg in table.items():
         for Hkv in (1, 2, 8):
             assert mod.head_groups(G * Hkv, Hkv) == (hg, G * Hkv // hg), (G, Hkv)
-    built = (1, 2, 3, 4, 8, 12)
-    for G in [g for g in range(1, 65) if g <= 4 or g % 4 == 0]:
+    built = (1, 2, 3, 4, 5, 6, 7, 8, 12)
+    for G in range(1, 65):
         for Hkv in (1, 3, 8):
             Hq = G * Hkv
             HG, U = mod.head_groups(Hq, Hkv)
-            assert HG == max(h for h in built if G % h == 0), (G, Hkv, HG)
+            passes = {h: G // h for h in built if G % h == 0}
+            assert passes[HG] == min(passes.values()), (G, Hkv, HG)
             assert HG * U == Hq
             heads = []
             for u in range(U):
@@ -736,6 +740,14 @@ def _mutants():
                                          (8 if (Hq // Hkv) % 8 == 0 else 4)),
                                         Hq // (Hq // Hkv if Hq // Hkv <= 4 else
                                                (8 if (Hq // Hkv) % 8 == 0 else 4)))}
+    # the grouping before groups of five to seven existed: four heads at G = 6
+    m["head_groups_four_at_g6"] = {
+        "head_groups": lambda Hq, Hkv: ((Hq // Hkv if Hq // Hkv <= 4 else
+                                         (12 if (Hq // Hkv) % 12 == 0 else
+                                          (8 if (Hq // Hkv) % 8 == 0 else 4))),
+                                        Hq // (Hq // Hkv if Hq // Hkv <= 4 else
+                                               (12 if (Hq // Hkv) % 12 == 0 else
+                                                (8 if (Hq // Hkv) % 8 == 0 else 4))))}
     # groups of eight for any G above four (splits a KV head's heads at G = 12)
     m["head_groups_eight_above_four"] = {
         "head_groups": lambda Hq, Hkv: ((Hq // Hkv if Hq // Hkv <= 4 else 8),
