@@ -128,8 +128,8 @@ typedef struct pkv_pool {
  *  num_q_heads          Hq; num_kv_heads must divide it, and the group size
  *                       G = Hq / Hkv may be any size; the decode reads each
  *                       K/V tile once per head group of H heads, H the
- *                       largest of 1 .. 8 and 12 that divides G (all of G up
- *                       to 8; a prime G above 8 reads each tile G times)
+ *                       largest of 1 .. 8, 12 and 16 that divides G (all of
+ *                       G up to 8; a prime G above 8 reads each tile G times)
  *  num_kv_heads         Hkv
  *  head_dim             D, 64 or 128
  *  page_size            P, a power of two >= 16
@@ -171,7 +171,7 @@ size_t pkv_workspace_bytes(const pkv_desc* desc);
  * step, the token appended this step included) it writes
  *   kv_indptr   device int32 [batch + 1], page prefix sums as defined above,
  * and the work plan into the workspace.  Plan, with U = num_q_heads / H query
- * head groups per request (H the largest of 1 .. 8 and 12 that divides G) and
+ * head groups per request (H the largest of 1 .. 8, 12 and 16 that divides G) and
  * T = kv_indptr[batch] * U
  * tiles:
  *   groups   W = min(num_workgroups, max(1, ceil(T / min_tiles_per_group))),

@@ -292,12 +292,12 @@ def head_groups(Hq: int, Hkv: int) -> Tuple[int, int]:
     """(HG, U): query heads per head group and head groups per request.
 
     A head group is query heads of one KV head: the largest number of them
-    in 1 .. 8 or 12 that divides G (all of them up to eight); a KV head with
-    more query heads than that gets several head groups.  (The grouping is the decode plan's, not the pages': it only
+    in 1 .. 8, 12 or 16 that divides G (all of them up to eight); a KV head
+    with more query heads than that gets several head groups.  (The grouping is the decode plan's, not the pages': it only
     orders the plan's tiles.)
     """
     G = Hq // Hkv
-    HG = max(h for h in (1, 2, 3, 4, 5, 6, 7, 8, 12) if G % h == 0)
+    HG = max(h for h in (1, 2, 3, 4, 5, 6, 7, 8, 12, 16) if G % h == 0)
     return HG, Hq // HG
 
 

@@ -6,7 +6,7 @@
 // wave.  Each wave keeps two steps of loads in flight; two waves per SIMD hide
 // each other's tail of a step better than one wave with a deeper register ring
 // (which measured slower at every depth).  A head group is HG query heads
-// that share one KV head (the largest of 12, 8, 7, .., 1 that divides G), so
+// that share one KV head (the largest of 16, 12, 8, 7, .., 1 that divides G), so
 // a tile is one page of one KV head, K and V, read once for HG query heads.  Each wave streams its range,
 // keeping an online-softmax state that it closes whenever the range leaves a
 // (request, head group) segment.  A segment wholly inside a wave is written
@@ -158,14 +158,18 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
   constexpr int kStages = 2;  // register ring: steps in flight per wave
 
   // Pieces that leave a wave unfinished: slot 0 = the wave's first piece,
-  // slot 1 = its last piece (every other piece is a whole segment).
+  // slot 1 = its last piece (every other piece is a whole segment).  Slot 1
+  // also serves as the wave's transpose of a whole segment's finished rows:
+  // whole segments come before the last piece, and a partial piece after the
+  // first is the last (its range ends inside it), so the rows are written out
+  // before slot 1 takes the last piece.  (Sixteen-head groups fit in LDS only
+  // with the transpose kept there.)
   __shared__ __align__(16) float s_acc[kWavesPerGroup][2][HG][D];
   // Max and sum of slot k = 2 w + (0 | 1) of head h at [h][k]: a head's 16
   // slots are four 16-byte reads.
   __shared__ __align__(16) float s_m[HG][kSlots];
   __shared__ __align__(16) float s_l[HG][kSlots];
   __shared__ int s_seg[PLAN ? kWavesPerGroup : 1][2];  // planning launch: the slot segments
-  __shared__ __align__(16) float s_out[kWavesPerGroup][HG][D];  // per-wave transpose of finished rows
   __shared__ int s_merge[2];  // of those, the ones this workgroup merges
   __shared__ GroupInfo s_gi;  // the workgroup's merge record, for the epilogue
   __shared__ EpiloguePtrs s_ptr;
@@ -716,7 +720,7 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         if (g4 == (i >> 2)) {  // head i: register i % 4 of lane group i / 4
 #pragma unroll
           for (int vb = 0; vb < MfmaWave<D, HG>::VB; ++vb)
-            s_out[w][i][out_ch(vb)] = st.o[vb][i & 3] * inv;
+            s_acc[w][1][i][out_ch(vb)] = st.o[vb][i & 3] * inv;
         }
       }
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's LDS writes land first
@@ -725,14 +729,14 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
         if (e8 + lane < HG * (D / 8)) {
           const int i = (e8 + lane) / (D / 8);
           const int c8 = (e8 + lane - i * (D / 8)) * 8;
-          const float4 x0 = *reinterpret_cast<const float4*>(&s_out[w][i][c8]);
-          const float4 x1 = *reinterpret_cast<const float4*>(&s_out[w][i][c8 + 4]);
+          const float4 x0 = *reinterpret_cast<const float4*>(&s_acc[w][1][i][c8]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&s_acc[w][1][i][c8 + 4]);
           *reinterpret_cast<uint4*>(a.out + ((size_t)b * Hq + hq0 + i) * D + c8) =
               make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
                          pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
         }
       }
-      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before s_out is reused
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before slot 1 is reused
     } else {
       const int slot = piece == 0 ? 0 : 1;
 #pragma unroll
@@ -1053,6 +1057,7 @@ hipError_t launch_d(const DecodeArgs& a, int hg, int groups, hipStream_t s) {
     case 7: hipLaunchKernelGGL((decode_kernel<D, 7, KIND, PLAN>), grid, block, 0, s, a); break;
     case 8: hipLaunchKernelGGL((decode_kernel<D, 8, KIND, PLAN>), grid, block, 0, s, a); break;
     case 12: hipLaunchKernelGGL((decode_kernel<D, 12, KIND, PLAN>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((decode_kernel<D, 16, KIND, PLAN>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

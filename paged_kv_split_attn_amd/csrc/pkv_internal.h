@@ -79,13 +79,13 @@ struct WsLayout {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Query heads one decode head group covers: the largest size the decode is
-// built for (1 .. 8, 12) that divides G (G >= 1) -- the whole GQA group up
-// to eight heads.  One 16-row matrix-core tile holds up to sixteen;
-// sixteen-head groups would not fit the merge's LDS.  The rest of a larger
-// group goes to sibling head groups that read the same K/V tiles again, so
-// the largest divisor means the fewest passes over each KV head.
+// built for (1 .. 8, 12, 16) that divides G (G >= 1) -- the whole GQA group
+// up to eight heads.  One 16-row matrix-core tile holds up to sixteen.  The
+// rest of a larger group goes to sibling head groups that read the same K/V
+// tiles again, so the largest divisor means the fewest passes over each KV
+// head.
 inline int heads_per_group(int G) {
-  constexpr int kBuilt[] = {12, 8, 7, 6, 5, 4, 3, 2};
+  constexpr int kBuilt[] = {16, 12, 8, 7, 6, 5, 4, 3, 2};
   for (int h : kBuilt)
     if (G % h == 0) return h;
   return 1;

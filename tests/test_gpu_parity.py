@@ -47,8 +47,8 @@ def _random_lengths_batch(seed, B, with_zeros):
 
 # Plans away from four query heads per KV head and pages of 16 tokens:
 # (Hq, Hkv, P) -> head groups of the largest of 1 .. 8 and 12 that divides G:
-# all of G up to eight (G = 1, 3, 6, 7, 8), twelve (G = 12), eight (G = 16: two
-# groups per KV head), five (G = 20: four groups) or one (G = 11, a prime).
+# all of G up to eight (G = 1, 3, 6, 7, 8), twelve (G = 12), sixteen (G = 16),
+# five (G = 20: four groups per KV head) or one (G = 11, a prime).
 PLAN_SHAPES = {
     "g8": (64, 8, 16), "g3": (24, 8, 16), "g12": (48, 4, 16), "g1": (8, 8, 16),
     "g16": (128, 8, 16), "g20": (40, 2, 16), "g6": (48, 8, 16), "g7": (28, 4, 16),
@@ -206,8 +206,10 @@ FUSED_CASES = {  # name: (Hq, Hkv, D, P, lengths)
     "g7_p16": (28, 4, 128, 16, [1, 16, 17, 250, 47]),
     # two head groups of five per KV head
     "g10_p32": (20, 2, 64, 32, [2, 31, 32, 33, 400]),
-    # two head groups of eight per KV head
+    # one head group of sixteen per KV head
     "g16_p32": (64, 4, 64, 32, [33, 1, 96, 500, 31]),
+    # two head groups of sixteen per KV head
+    "g32_p16": (64, 2, 128, 16, [1, 16, 17, 250, 47]),
 }
 
 
@@ -346,7 +348,8 @@ def test_repeated_decodes_reuse_one_plan():
     (28, 4, 128, 16),  # G = 7: one head group of seven
     (36, 4, 64, 16),   # G = 9: three head groups of three per KV head
     (22, 2, 128, 16),  # G = 11: eleven head groups of one per KV head
-    (128, 8, 64, 16),  # G = 16: two head groups of eight per KV head
+    (128, 8, 64, 16),  # G = 16: one head group of sixteen
+    (64, 2, 128, 16),  # G = 32: two head groups of sixteen per KV head
     (96, 8, 128, 32),  # G = 12 with pages of 32
     (32, 4, 64, 32),   # two rounds per page at D = 64
     (8, 2, 128, 32),   # four rounds per page at D = 128

@@ -323,20 +323,20 @@ def pin_head_groups(mod):
     only say that the query heads of one KV head read its K/V together).
 
     Three statements of it: the table of head-group sizes that the library
-    header documents, written out by hand (the largest of 1 .. 8 and 12 that
-    divides G: all of a KV head's query heads up to eight, then twelve, eight,
-    seven, ..., one); the same sizes found by counting, for every size built,
+    header documents, written out by hand (the largest of 1 .. 8, 12 and 16
+    that divides G: all of a KV head's query heads up to eight, then sixteen,
+    twelve, eight, seven, ..., one); the same sizes found by counting, for every size built,
     the passes over each KV head it needs (G / HG, fewest wins, only sizes that
     divide G allowed); and the structure every grouping must have (a group
     lies inside one KV head, and the groups cover the query heads exactly
     once)."""
     table = {1: 1, 2: 2, 3: 3, 4: 4, 5: 5, 6: 6, 7: 7, 8: 8, 9: 3, 10: 5, 11: 1, 12: 12,
-             13: 1, 14: 7, 15: 5, 16: 8, 18: 6, 20: 5, 21: 7, 24: 12, 28: 7, 32: 8, 36: 12,
-             44: 4, 48: 12}
+             13: 1, 14: 7, 15: 5, 16: 16, 18: 6, 20: 5, 21: 7, 24: 12, 28: 7, 32: 16,
+             36: 12, 40: 8, 44: 4, 48: 16, 60: 12}
     for G, hg in table.items():
         for Hkv in (1, 2, 8):
             assert mod.head_groups(G * Hkv, Hkv) == (hg, G * Hkv // hg), (G, Hkv)
-    built = (1, 2, 3, 4, 5, 6, 7, 8, 12)
+    built = (1, 2, 3, 4, 5, 6, 7, 8, 12, 16)
     for G in range(1, 65):
         for Hkv in (1, 3, 8):
             Hq = G * Hkv
