@@ -480,11 +480,11 @@ __global__ void __launch_bounds__(kGroupThreads) decode_kernel(DecodeArgs a) {
     }
 
     // Token-major K/V: blocks of 16 steps, register r of lane i holding the
-    // slot of token 16 (p + jb) + 64 r + i of the block (its K row for lane
-    // r16 of step 4 r + i / 16, its V row for the lanes whose four tokens
-    // include it, both fetched by a lane shuffle), or -1 past the sequence or
-    // for an unusable slot.  (With one register, blocks of 4 steps, the
-    // register ring restarted every 4 steps behind a slot-id load.)
+    // slot of token 16 (p + jb) + 64 r + i of the block (the K row of lanes
+    // r16 = i % 16 in step 4 r + i / 16, and the V row of the lanes whose four
+    // tokens include it, both fetched by a lane shuffle), or -1 past the
+    // sequence or for an unusable slot.  The register ring starts again at
+    // every block, behind the block's slot-id loads, so blocks are long.
     constexpr int kTokRegs = 4;
     constexpr int kBlock = TOKENS ? 4 * kTokRegs : kWave;
     for (int jb = 0; jb < len; jb += kBlock) {
